@@ -1,0 +1,251 @@
+"""CPU model of the event-tensor task graph (test infrastructure only).
+
+What the pages fix: event tensors are counters that encode the dependencies between
+tiled tasks (OpenAlex record of "Event Tensor: A Unified Abstraction for Compiling
+Dynamic Megakernel", abstract); a task waits until its counter reaches a target, and
+with MoE routing the target depends on how many producer tasks the routing creates,
+so it is computed on the GPU before anyone waits (chapter "5 · Event Tensor et le
+dynamisme", §5.5 Obstacle 1); with unpredictable task sizes the work is handed out
+online through atomics (§5.5 Obstacle 3); static scheduling suits regular work and
+dynamic scheduling irregular work such as MoE (podcast episode page "Prompt
+Boundary-Aware Scheduling with Event Tensors for Dynamic Kernels", summary).
+
+reading (tiling): per layer, with BT tokens per routing tile, BM rows per expert row
+tile, BN1 ffn columns per gate/up tile, BN2 hidden columns per down tile and the
+down projection split along ffn into chunks of GPC gate/up tiles:
+
+  R(tau)          routing tile tau                      waits  done[l-1][tau] >= 1 (l > 0)
+                                                        signals route[l] += 1
+  S               counts, scan, permutation             waits  route[l] >= n_rt
+                                                        signals scan[l] = 1
+  GU(e, m, n)     gate/up tile                          waits  scan[l] >= 1
+                                                        signals gu[l][e,m][n // GPC] += 1
+  D(e, m, n2, s)  down tile over ffn chunk s            waits  gu[l][e,m][s] >= tiles in chunk s
+                                                        signals comb[l][tau] += rows of (e,m) in tau
+  F(tau)          finalize the output rows of tau       waits  comb[l][tau] >= |tau| * k * n2 * nS
+                                                        signals done[l][tau] += 1
+
+Static mode runs the tasks in one fixed ticket order (per layer: all R, S, all GU,
+all D, all F) and each worker spins on the dependencies of the task it drew.
+Dynamic mode keeps a FIFO ready queue: the R tasks of the first layer are queued at
+the start; the worker whose signal completes a counter (the last arriver) makes the
+dependents ready -- S runs inline after the last R, S queues every GU task, a full
+gu chunk queues its D tasks, a full comb tile queues its F, and F queues the next
+layer's R for the same tokens.
+"""
+
+from dataclasses import dataclass, field
+import random
+
+
+def cdiv(a, b):
+    return -(-a // b)
+
+
+@dataclass(frozen=True)
+class Plan:
+    BT: int  # tokens per routing tile
+    BM: int  # rows per expert row tile
+    BN1: int  # ffn columns per gate/up tile
+    BN2: int  # hidden columns per down tile
+    GPC: int  # gate/up tiles per down chunk (ffn split of the down projection)
+
+
+@dataclass
+class Task:
+    kind: str
+    layer: int
+    key: tuple
+    waits: list = field(default_factory=list)  # [(counter, target)]
+    signals: list = field(default_factory=list)  # [(counter, amount)]
+
+
+def layer_shape(T, H, F, plan):
+    n_rt = cdiv(T, plan.BT)
+    n1 = cdiv(F, plan.BN1)
+    n2 = cdiv(H, plan.BN2)
+    nS = cdiv(n1, plan.GPC)
+    return n_rt, n1, n2, nS
+
+
+def rows_per_routing_tile(T, plan):
+    return [min(plan.BT, T - tau * plan.BT) for tau in range(cdiv(T, plan.BT))]
+
+
+def build_layer(l, T, H, F, k, counts, plan, tokens_of_rows):
+    """Tasks of layer ``l``.  ``tokens_of_rows[e]`` lists the token of every row of
+    expert e in row order (the permutation), used to count rows per routing tile."""
+    n_rt, n1, n2, nS = layer_shape(T, H, F, plan)
+    tile_rows = rows_per_routing_tile(T, plan)
+    R, GU, D, Fin = [], [], [], []
+    for tau in range(n_rt):
+        waits = [(("done", l - 1, tau), 1)] if l > 0 else []
+        R.append(Task("R", l, (tau,), waits, [(("route", l), 1)]))
+    S = Task("S", l, (), [(("route", l), n_rt)], [(("scan", l), 1)])
+    for e, c in enumerate(counts):
+        for m in range(cdiv(int(c), plan.BM)):
+            for n in range(n1):
+                GU.append(Task("GU", l, (e, m, n), [(("scan", l), 1)],
+                               [(("gu", l, e, m, n // plan.GPC), 1)]))
+    for e, c in enumerate(counts):
+        for m in range(cdiv(int(c), plan.BM)):
+            rows = tokens_of_rows[e][m * plan.BM:(m + 1) * plan.BM]
+            per_tau = {}
+            for t in rows:
+                per_tau[t // plan.BT] = per_tau.get(t // plan.BT, 0) + 1
+            sig = [(("comb", l, tau), cnt) for tau, cnt in sorted(per_tau.items())]
+            for s in range(nS):
+                need = min(plan.GPC, n1 - s * plan.GPC)
+                for n2i in range(n2):
+                    D.append(Task("D", l, (e, m, n2i, s), [(("gu", l, e, m, s), need)], sig))
+    for tau in range(n_rt):
+        target = tile_rows[tau] * k * n2 * nS
+        Fin.append(Task("F", l, (tau,), [(("comb", l, tau), target)], [(("done", l, tau), 1)]))
+    return R, S, GU, D, Fin
+
+
+def build_graph(T, H, F, k, layer_counts, layer_tokens_of_rows, plan):
+    """All layers, each as (R, S, GU, D, F) lists."""
+    return [build_layer(l, T, H, F, k, c, plan, tr)
+            for l, (c, tr) in enumerate(zip(layer_counts, layer_tokens_of_rows))]
+
+
+def expected_final_counters(graph):
+    """Every counter's value once all tasks have signalled."""
+    final = {}
+    for R, S, GU, D, Fin in graph:
+        for t in R + [S] + GU + D + Fin:
+            for ctr, amt in t.signals:
+                final[ctr] = final.get(ctr, 0) + amt
+    return final
+
+
+def static_order(graph):
+    order = []
+    for R, S, GU, D, Fin in graph:
+        order += R + [S] + GU + D + Fin
+    return order
+
+
+def _ready(task, counters):
+    return all(counters.get(c, 0) >= tgt for c, tgt in task.waits)
+
+
+def _signal(task, counters):
+    for c, amt in task.signals:
+        counters[c] = counters.get(c, 0) + amt
+
+
+def simulate_static(graph, workers, rng=None):
+    """Workers draw tickets in order and spin on the drawn task's waits.  Returns the
+    execution order; raises RuntimeError on deadlock (no worker can move)."""
+    rng = rng or random.Random(0)
+    order = static_order(graph)
+    counters, executed = {}, []
+    next_ticket = 0
+    holding = [None] * workers  # task drawn by each worker
+    while len(executed) < len(order):
+        # every idle worker draws the next ticket (drawing is an atomic increment)
+        for w in range(workers):
+            if holding[w] is None and next_ticket < len(order):
+                holding[w] = order[next_ticket]
+                next_ticket += 1
+        movable = [w for w in range(workers)
+                   if holding[w] is not None and _ready(holding[w], counters)]
+        if not movable:
+            stuck = [holding[w] for w in range(workers) if holding[w] is not None]
+            raise RuntimeError(f"static schedule deadlocked holding {[(t.kind, t.key) for t in stuck]}")
+        w = rng.choice(movable)
+        t = holding[w]
+        _signal(t, counters)
+        executed.append(t)
+        holding[w] = None
+    return executed, counters
+
+
+def simulate_dynamic(graph, workers, rng=None):
+    """FIFO ready queue filled by last arrivers.  Returns (execution order, counters);
+    raises RuntimeError if work remains but nothing is queued or running."""
+    rng = rng or random.Random(0)
+    counters, executed = {}, []
+    layers = len(graph)
+    queue = list(graph[0][0])  # R tasks of the first layer
+    running = []
+    # lookups of the dependents that a completed counter releases
+    gu_by_layer = [g[2] for g in graph]
+    d_by_chunk = []
+    f_by_tau = []
+    r_by_tau = []
+    for R, S, GU, D, Fin in graph:
+        dd = {}
+        for t in D:
+            e, m, _, s = t.key
+            dd.setdefault((e, m, s), []).append(t)
+        d_by_chunk.append(dd)
+        f_by_tau.append({t.key[0]: t for t in Fin})
+        r_by_tau.append({t.key[0]: t for t in R})
+    total = sum(len(R) + len(GU) + len(D) + len(Fin) + 1 for R, S, GU, D, Fin in graph)
+    while len(executed) < total:
+        while queue and len(running) < workers:
+            running.append(queue.pop(0))
+        if not running:
+            raise RuntimeError("dynamic schedule starved: no task queued or running")
+        t = running.pop(rng.randrange(len(running)))
+        if not _ready(t, counters):
+            raise RuntimeError(f"task {t.kind}{t.key} was queued before it was ready")
+        before = dict(counters)
+        _signal(t, counters)
+        executed.append(t)
+        l = t.layer
+        R, S, GU, D, Fin = graph[l]
+        for ctr, amt in t.signals:
+            old, new = before.get(ctr, 0), counters[ctr]
+            kind = ctr[0]
+            if kind == "route" and new == len(R) and old < new:
+                # the last routing tile runs S inline
+                assert _ready(S, counters)
+                _signal(S, counters)
+                executed.append(S)
+                queue.extend(gu_by_layer[l])
+            elif kind == "gu":
+                _, _, e, m, s = ctr
+                deps = d_by_chunk[l].get((e, m, s), [])
+                if deps and old < deps[0].waits[0][1] <= new:
+                    queue.extend(deps)
+            elif kind == "comb":
+                ft = f_by_tau[l][ctr[2]]
+                if old < ft.waits[0][1] <= new:
+                    queue.append(ft)
+            elif kind == "done" and l + 1 < layers:
+                queue.append(r_by_tau[l + 1][ctr[2]])
+    return executed, counters
+
+
+def check_execution(executed, graph):
+    """Each task ran once and only after its waits were met (replays the order)."""
+    counters = {}
+    seen = set()
+    for t in executed:
+        ident = (t.kind, t.layer, t.key)
+        if ident in seen:
+            raise AssertionError(f"{ident} ran twice")
+        seen.add(ident)
+        if not _ready(t, counters):
+            raise AssertionError(f"{ident} ran before its dependencies")
+        _signal(t, counters)
+    n = sum(len(R) + 1 + len(GU) + len(D) + len(Fin) for R, S, GU, D, Fin in graph)
+    if len(seen) != n:
+        raise AssertionError(f"{len(seen)} of {n} tasks ran")
+    return counters
+
+
+# ------------------------------------------------------------------ split-K graph
+
+
+def splitk_graph(M, N, split_k, BM, BN):
+    """P(tile, s) partial tasks signal ev[tile]; the reduction of a tile waits for
+    ev[tile] >= split_k (podcast episode summary: the split-K summation example)."""
+    tiles = [(i, j) for i in range(cdiv(M, BM)) for j in range(cdiv(N, BN))]
+    P = [Task("P", 0, (tile, s), [], [(("ev", tile), 1)]) for s in range(split_k) for tile in tiles]
+    K = [Task("K", 0, (tile,), [(("ev", tile), split_k)], [(("out", tile), 1)]) for tile in tiles]
+    return P, K
