@@ -1,0 +1,215 @@
+/*
+ * etc_moe.h -- C ABI of the event-tensor MoE layer and split-K GEMM for AMD MI355X
+ * (gfx950).
+ *
+ * Background.  An event tensor is an array of counters in global memory that encodes
+ * the dependencies between tiled tasks of one persistent kernel; a task runs once its
+ * counter reaches a target, and with Mixture-of-Experts routing the targets depend on
+ * the router's output, so the kernel computes them on the GPU before anyone waits
+ * (OpenAlex record of "Event Tensor: A Unified Abstraction for Compiling Dynamic
+ * Megakernel", abstract; tutorial chapter "5 · Event Tensor et le dynamisme", §5.3 and
+ * §5.5 Obstacle 1).  The batch size is a run-time argument: one compiled kernel serves
+ * every token count (podcast episode page "Prompt Boundary-Aware Scheduling with Event
+ * Tensors for Dynamic Kernels", summary: symbolic batch-size template; §5.3 of the
+ * chapter: one compilation instead of one per batch size).
+ *
+ * Conventions for every entry point:
+ *   - Pointers named device are HIP device pointers owned by the caller; the library
+ *     never allocates, frees or keeps them after the call returns.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls are
+ *     asynchronous: they enqueue one kernel and return; only etc_query_device_status
+ *     synchronises the stream.
+ *   - Arguments are validated on the host before any HIP call.  On any error other
+ *     than ETC_ERR_HIP nothing is enqueued and no output is touched.
+ *   - Tensors are dense and row-major; "[a][b]" means b is the contiguous index.
+ *   - A workspace belongs to one stream at a time; calls sharing a workspace must be
+ *     ordered on that stream.  It must be cleared once with etc_workspace_init after
+ *     allocation; the kernel leaves it cleared again when it returns.
+ */
+#ifndef ETC_MOE_H
+#define ETC_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ETC_OK = 0,
+  ETC_ERR_INVALID_ARG = 1, /* a pointer, size or enum is out of range */
+  ETC_ERR_UNSUPPORTED = 2, /* valid shape this build does not handle (see each call) */
+  ETC_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or too small */
+  ETC_ERR_HIP = 4,         /* a HIP runtime call failed (device state unknown) */
+  ETC_ERR_TIMEOUT = 5,     /* device status: a wait exceeded its time limit, the kernel
+                              stopped early and its outputs are not valid */
+  ETC_ERR_NO_DEVICE = 6    /* no usable gfx950 device is current */
+} etc_status;
+
+typedef enum { ETC_DTYPE_F32 = 0, ETC_DTYPE_BF16 = 1 } etc_dtype;
+
+/* Static: every workgroup draws the next ticket of one fixed topological task order
+ * and waits on that task's counters.  Dynamic: a ready queue in global memory; the
+ * producer whose signal completes a counter enqueues the dependents, and workgroups
+ * only ever take ready tasks.  (Episode summary of the podcast page: static suits
+ * regular work, dynamic pays off under irregularity such as MoE routing; chapter §5.5
+ * Obstacle 3: online balancing through atomics.) */
+typedef enum { ETC_SCHED_STATIC = 0, ETC_SCHED_DYNAMIC = 1 } etc_sched_mode;
+
+/* Atomic: the down-projection tiles add gate * y straight into a float32 accumulator
+ * (order of additions varies run to run).  Ordered: they store y and the finalize
+ * task sums the k slots of each token in slot order (bit-reproducible). */
+typedef enum { ETC_COMBINE_ATOMIC = 0, ETC_COMBINE_ORDERED = 1 } etc_combine;
+
+/* debug flags */
+#define ETC_FLAG_KEEP_COUNTERS 0x1u /* do not clear the event counters on exit, so the
+                                       caller can read them (etc_moe_workspace_layout);
+                                       call etc_workspace_init before the next call */
+
+/* Weights of one MoE layer (all device pointers).  dtype is the call's dtype except
+ * gamma and router_bias, which are always float32.  Layouts follow nn.Linear
+ * ([out][in]): w_router [E][H], w_gate [E][F][H], w_up [E][F][H], w_down [E][H][F]. */
+typedef struct {
+  const float* gamma;       /* [H] RMSNorm scale */
+  const void* w_router;     /* [E][H] */
+  const float* router_bias; /* [E] or NULL (added to the logits) */
+  const void* w_gate;       /* [E][F][H] */
+  const void* w_up;         /* [E][F][H] */
+  const void* w_down;       /* [E][H][F] */
+} etc_moe_weights;
+
+/* Optional routing outputs (device pointers, any may be NULL).  When given, the kernel
+ * uses them as its working storage for that array, so they hold the layer's routing
+ * after the call. */
+typedef struct {
+  int32_t* topk_idx;      /* [L][T][k] experts in slot order (largest logit first) */
+  float* topk_w;          /* [L][T][k] gate weights (softmax over the k selected) */
+  int32_t* expert_counts; /* [L][E] tokens routed to each expert */
+  int32_t* sorted_assign; /* [L][T*k] t*k+j grouped by expert, tokens ascending */
+} etc_moe_routing;
+
+/*
+ * etc_moe_layer -- num_layers chained MoE layers in one persistent kernel.
+ *
+ * Per layer and token t: xn = RMSNorm(x_t) (float32 math, gamma, eps); logits =
+ * xn W_r^T (+ bias) in float32; the top_k experts by logit (ties to the lower index);
+ * gates = softmax over the selected logits; per-expert counts, their exclusive scan and
+ * the permutation grouping (token, slot) pairs by expert with tokens ascending; for
+ * each expert the rows X = dtype(xn) of its tokens go through h = dtype(silu(X W_g^T) *
+ * (X W_u^T)) and y = h W_d^T with float32 accumulation; out_t = dtype(sum_j gate_tj *
+ * y_tj).  The output of layer l is the input of layer l+1.  (The pages name the MoE
+ * routing with data-dependent event counters computed from router outputs -- episode
+ * summary of "Prompt Boundary-Aware Scheduling with Event Tensors for Dynamic Kernels"
+ * -- but no formula; the readings taken for each stage are those stated here.)
+ *
+ *   tokens       T, 0 <= T <= max_tokens (T == 0 is a no-op returning ETC_OK)
+ *   hidden       H, a multiple of 128
+ *   experts      E, 1..256
+ *   top_k        k, 1..min(E, 16)
+ *   ffn          F, a multiple of 64
+ *   num_layers   L, 1..4
+ *   dtype        storage type of x, out, layer_out and all weights but gamma/bias
+ *   eps          RMSNorm epsilon (> 0 or 0)
+ *   weights      host array of L etc_moe_weights
+ *   x            device [T][H] layer-0 input
+ *   out          device [T][H] output of the last layer
+ *   layer_out    device [L-1][T][H] outputs of layers 0..L-2, or NULL (then they live
+ *                in the workspace)
+ *   routing      optional outputs, or NULL
+ *   workspace    device, 256-byte aligned, >= etc_moe_workspace_size(max_tokens, ...)
+ *   max_tokens   capacity the workspace was sized for
+ *   mode, combine  see the enums
+ *   flags        ETC_FLAG_* bits (0 for normal use)
+ *   workers      persistent workgroups to launch; 0 = one per resident slot of the
+ *                device (CUs x occupancy), larger values are clamped to that
+ *   stream       hipStream_t
+ * Errors: ETC_ERR_INVALID_ARG (null pointer, size or enum out of range, unaligned
+ * pointer -- every tensor pointer must be 16-byte aligned), ETC_ERR_UNSUPPORTED
+ * (H % 128, F % 64, E > 256, k > 16, L > 4), ETC_ERR_WORKSPACE, ETC_ERR_HIP,
+ * ETC_ERR_NO_DEVICE.  Device-side timeouts are reported by etc_query_device_status.
+ */
+etc_status etc_moe_layer(int32_t tokens, int32_t hidden, int32_t experts, int32_t top_k,
+                         int32_t ffn, int32_t num_layers, etc_dtype dtype, float eps,
+                         const etc_moe_weights* weights, const void* x, void* out,
+                         void* layer_out, const etc_moe_routing* routing, void* workspace,
+                         size_t workspace_bytes, int32_t max_tokens, etc_sched_mode mode,
+                         etc_combine combine, uint32_t flags, int32_t workers, void* stream);
+
+/* Bytes of workspace etc_moe_layer needs for up to max_tokens tokens (0 on invalid
+ * arguments).  The ordered combine needs an extra float32 [max_tokens*k][H] buffer. */
+size_t etc_moe_workspace_size(int32_t max_tokens, int32_t hidden, int32_t experts,
+                              int32_t top_k, int32_t ffn, int32_t num_layers,
+                              etc_dtype dtype, etc_combine combine);
+
+/* Where the event counters of layer `layer` live inside a workspace, as byte offsets
+ * from its start, for inspection after a call with ETC_FLAG_KEEP_COUNTERS.  Writes
+ * ETC_LAYOUT_WORDS int64 values to out_offsets (host memory):
+ *   [0] ev_route (1 int32)   [1] ev_scan (1 int32)   [2] ev_gu ([max_rt][n1] int32)
+ *   [3] ev_comb ([n_rt] int32)   [4] ev_done ([n_rt] int32)   [5] plan words (int32)
+ *   [6] max_rt   [7] n1   [8] n_rt(max_tokens)   [9] rows per routing tile
+ *   [10] rows per expert tile   [11] ffn columns per gate/up tile
+ *   [12] hidden columns per down tile.
+ * The plan words are: [0] row tiles RT, [1] gate/up tasks, [2] down tasks,
+ * [3] finalize tasks, [4] ffn chunks of the down projection nS, [5] gate/up tiles per
+ * chunk, [6] first static ticket of the next layer. */
+#define ETC_LAYOUT_WORDS 13
+etc_status etc_moe_workspace_layout(int32_t max_tokens, int32_t hidden, int32_t experts,
+                                    int32_t top_k, int32_t ffn, int32_t num_layers,
+                                    etc_dtype dtype, etc_combine combine, int32_t layer,
+                                    int64_t* out_offsets);
+
+/*
+ * etc_splitk_gemm -- C = A B with the K range cut into split_k slices.
+ *
+ * Each (output tile, slice) partial task writes a float32 partial tile and signals the
+ * tile's event counter; the tile's reduction runs once that counter reaches split_k
+ * and adds the partials in slice order 0..split_k-1 (episode summary of "Prompt
+ * Boundary-Aware Scheduling with Event Tensors for Dynamic Kernels": the split-K
+ * summation example of fine-grained dependencies).  Static mode puts the reductions
+ * after all partials in ticket order; dynamic mode lets the partial task whose signal
+ * completes the counter run the reduction.
+ *
+ *   M, N, K    sizes; M >= 1, N a multiple of 128, K a multiple of 64 * split_k
+ *   split_k    1..64
+ *   A          device bfloat16 [M][K]
+ *   B          device bfloat16 [K][N]
+ *   C          device float32 [M][N]
+ *   workspace  device, 256-byte aligned, >= etc_splitk_workspace_size(M, N, split_k)
+ *   workers    as for etc_moe_layer
+ * Errors: ETC_ERR_INVALID_ARG, ETC_ERR_UNSUPPORTED (shape constraints above),
+ * ETC_ERR_WORKSPACE, ETC_ERR_HIP, ETC_ERR_NO_DEVICE.
+ */
+etc_status etc_splitk_gemm(int32_t M, int32_t N, int32_t K, int32_t split_k, const void* A,
+                           const void* B, float* C, void* workspace, size_t workspace_bytes,
+                           etc_sched_mode mode, uint32_t flags, int32_t workers,
+                           void* stream);
+
+size_t etc_splitk_workspace_size(int32_t M, int32_t N, int32_t split_k);
+
+/* Clear a freshly allocated workspace (enqueues a memset of its control words on
+ * `stream`).  Needed once after allocation, and after a call that failed with a
+ * device timeout or used ETC_FLAG_KEEP_COUNTERS. */
+etc_status etc_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/* Synchronises `stream`, then returns the device status left in the workspace by the
+ * last call: ETC_OK or ETC_ERR_TIMEOUT.  ETC_ERR_HIP if the copy fails. */
+etc_status etc_query_device_status(const void* workspace, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* etc_status_string(etc_status status);
+
+/* Persistent workgroups a call would launch on the current device with workers = 0,
+ * for the MoE kernel (kind 0, given dtype) or the split-K kernel (kind 1); 0 if no
+ * device.  Lets callers size tests; does not launch anything. */
+int32_t etc_default_workers(int32_t kind, etc_dtype dtype);
+
+/* ABI version of this header: (major << 16) | minor. */
+#define ETC_ABI_VERSION 0x00010000
+int32_t etc_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ETC_MOE_H */

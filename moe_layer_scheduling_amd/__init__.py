@@ -15,7 +15,7 @@ from . import synth  # noqa: F401  (pure-Python input generator, no GPU needed)
 
 _BINDING_NAMES = {
     "moe_layer", "splitk_gemm", "MoEWorkspace", "SplitKWorkspace", "load_library",
-    "EtcError", "EtcLibraryError", "library_path", "plan_for",
+    "EtcError", "EtcLibraryError", "library_path", "default_workers", "Workspace",
 }
 
 

@@ -1,0 +1,155 @@
+// Device-side building blocks shared by the persistent kernels: storage types,
+// bfloat16 conversion, the event-counter primitives (signal / wait with a watchdog)
+// and wave-level reductions.  gfx950 (CDNA4), wave64, one 256-thread workgroup per
+// persistent worker.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define ETC_DEV __device__ __forceinline__
+
+namespace etc {
+
+constexpr int NT = 256;  // threads per persistent workgroup (4 waves)
+constexpr int WAVE = 64;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct bf16 {
+  uint16_t bits;
+};
+
+// ------------------------------------------------------------------ conversions
+
+ETC_DEV float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Round to nearest even; NaN stays NaN (quiet).
+ETC_DEV uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+template <typename TE>
+struct Elem;
+template <>
+struct Elem<float> {
+  static constexpr int BYTES = 4;
+  ETC_DEV static float load(const float* p, long i) { return p[i]; }
+  ETC_DEV static void store(float* p, long i, float v) { p[i] = v; }
+};
+template <>
+struct Elem<bf16> {
+  static constexpr int BYTES = 2;
+  ETC_DEV static float load(const bf16* p, long i) { return bf16_bits_to_f32(p[i].bits); }
+  ETC_DEV static void store(bf16* p, long i, float v) { p[i].bits = (uint16_t)f32_to_bf16_bits(v); }
+};
+
+// 16 bytes of a row, expanded to floats (8 bf16 or 4 f32 values)
+ETC_DEV void expand16(const uint4& v, float* out8, const bf16*) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    out8[2 * i] = __uint_as_float(w[i] << 16);
+    out8[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+ETC_DEV void expand16(const uint4& v, float* out4, const float*) {
+  out4[0] = __uint_as_float(v.x);
+  out4[1] = __uint_as_float(v.y);
+  out4[2] = __uint_as_float(v.z);
+  out4[3] = __uint_as_float(v.w);
+}
+
+// ------------------------------------------------------------------ event counters
+//
+// An event counter is an int32 in global memory.  A producer first makes its own
+// results visible to the whole device, then adds to the counter with release
+// semantics at agent scope; a consumer reads the counter with acquire semantics at
+// agent scope until it reaches its target.  On gfx950 the agent-scope release writes
+// back this XCD's L2 and the acquire invalidates the reader's caches, so data written
+// on one XCD is seen on another.  Only one lane of a workgroup touches a counter; the
+// rest of the workgroup is ordered by barriers around it.
+
+ETC_DEV int ev_load(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+ETC_DEV int ev_load_relaxed(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+ETC_DEV int ev_add(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+ETC_DEV void ev_store(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+ETC_DEV void ev_store_relaxed(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+ETC_DEV long long q_load(const long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+ETC_DEV void q_store_relaxed(long long* p, long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+ETC_DEV void fence_release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+ETC_DEV void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+// Every thread waits until all of its own memory operations have completed, then the
+// workgroup meets at a barrier: after this, one thread's agent-scope release covers
+// the stores of the whole workgroup.
+ETC_DEV void wg_publish() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+ETC_DEV uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }  // 100 MHz
+
+// Control words shared by all workgroups of one call (in the workspace).
+enum SchedWord {
+  W_TICKET = 0,   // static: next ticket
+  W_QHEAD = 1,    // dynamic: next queue slot to take
+  W_QTAIL = 2,    // dynamic: queue slots handed out to producers
+  W_QTOTAL = 3,   // dynamic: tasks that will ever be queued (grows as layers plan)
+  W_PLANNED = 4,  // dynamic: layers whose task counts are final
+  W_EXIT = 5,     // workgroups that have left the task loop
+  W_ABORT = 6,    // set when a wait times out: every workgroup leaves
+  W_STATUS = 7,   // 0 ok, else an etc_status; survives the end-of-call reset
+  W_AUX = 8,      // debug: where the abort came from
+  W_NWORDS = 16
+};
+
+// Spin (one lane) until *ctr >= target.  Returns false if the call was aborted, by
+// this wait timing out or by another workgroup.
+ETC_DEV bool spin_until_geq(const int* ctr, int target, int* sched, uint64_t deadline,
+                            int where) {
+  int it = 0;
+  while (true) {
+    if (ev_load(ctr) >= target) return true;
+    if ((++it & 15) == 0) {
+      if (ev_load_relaxed(sched + W_ABORT)) return false;
+      if (now_ticks() > deadline) {
+        ev_store_relaxed(sched + W_STATUS, 5 /* ETC_ERR_TIMEOUT */);
+        ev_store_relaxed(sched + W_AUX, where);
+        ev_store(sched + W_ABORT, 1);
+        return false;
+      }
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// ------------------------------------------------------------------ wave helpers
+
+ETC_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, WAVE);
+  return v;
+}
+
+__host__ __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace etc

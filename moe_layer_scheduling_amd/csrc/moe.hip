@@ -1,0 +1,1046 @@
+// The event-tensor MoE layer: one persistent kernel per call.
+//
+// What the pages fix.  The podcast episode page "Prompt Boundary-Aware Scheduling with
+// Event Tensors for Dynamic Kernels" (summary) describes MoE routing handled through
+// event counters whose values and task triggers are computed from the router's output,
+// a symbolic batch size that avoids recompiling, and static versus dynamic scheduling.
+// The OpenAlex record of "Event Tensor: A Unified Abstraction for Compiling Dynamic
+// Megakernel" (abstract) has the event tensor encode dependencies between tiled tasks of
+// one persistent kernel.  The chapter "5 · Event Tensor et le dynamisme" adds that the
+// counter targets depend on how many producer tasks the routing creates and are computed
+// on the GPU before anyone waits (§5.5 Obstacle 1), and that unpredictable task sizes
+// call for online scheduling through atomics (§5.5 Obstacle 3).
+//
+// Tasks of layer l (BT = 16 tokens per routing tile, BM = 128 rows per expert row tile,
+// BN1 = 64 ffn columns per gate/up tile, BN2 = 128 hidden columns per down tile):
+//   R(tau)         RMSNorm, router logits, top-k, softmax for 16 tokens; ranks of their
+//                  (token, slot) pairs inside the tile and the tile's expert histogram
+//                  -> ev_route[l] += 1.  For l > 0 it waits ev_done[l-1][tau] >= 1.
+//   S              waits ev_route[l] >= n_rt: counts, exclusive scan, row tiles per
+//                  expert, permutation; sizes the down split (nS chunks of GPC gate/up
+//                  tiles) from the actual number of row tiles; -> ev_scan[l] = 1.
+//   GU(e, m, n)    gate/up tile of expert e rows m*128.. and ffn columns n*64..;
+//                  h = silu(G) * U -> ev_gu[l][rt(e,m)][n / GPC] += 1.
+//   D(e, m, n2, s) down tile over ffn chunk s; waits ev_gu[l][rt][s] >= tiles in chunk s;
+//                  adds gate * y into the float32 accumulator (or stores y) ->
+//                  ev_comb[l][tau] += its rows in tau, per routing tile tau it touches.
+//   F(tau)         waits ev_comb[l][tau] >= rows(tau) * k * n2 * nS; writes the layer
+//                  output rows -> ev_done[l][tau] = 1.
+// Static mode: workgroups draw tickets of the order [R.. S GU.. D.. F..] per layer and
+// spin on each task's counter.  Dynamic mode: a queue of ready tasks; the R tasks of the
+// first layer are implicit in slots 0..n_rt-1, the last R runs S inline, S enqueues the
+// GU tasks, and whichever signal completes a counter enqueues the tasks it releases.
+// The token count T is a kernel argument; nothing in the code depends on its value.
+#include <float.h>
+#include <string.h>
+
+#include "common.hpp"
+#include "host.hpp"
+#include "ktile.hpp"
+
+namespace etc {
+namespace moe {
+
+constexpr int MAXL = 4, MAXE = 256, MAXK = 16;
+constexpr int BT = 16, BM = 128, BN1 = 64, BN2 = 128;
+constexpr int RCH = 512, XS_STRIDE = RCH + 4;  // routing: hidden chunk staged in LDS
+constexpr int MAX_WORKERS = 2048;
+constexpr int MAX_TOKENS = 262143;  // task fields are 14 bits
+
+enum Kind { K_NONE = 0, K_R = 1, K_S = 2, K_GU = 3, K_D = 4, K_F = 5 };
+enum PlanWord { PL_RT = 0, PL_NGU, PL_ND, PL_NF, PL_NS, PL_GPC, PL_NEXTBASE, PL_WORDS = 8 };
+
+struct Task {
+  int kind, layer, a, b, c, d;
+};
+
+ETC_DEV long long enc(const Task& t) {
+  unsigned long long v = (unsigned long long)t.kind | ((unsigned long long)t.layer << 4) |
+                         ((unsigned long long)t.a << 8) | ((unsigned long long)t.b << 22) |
+                         ((unsigned long long)t.c << 36) | ((unsigned long long)t.d << 50);
+  return (long long)v;
+}
+ETC_DEV Task dec(long long sv) {
+  unsigned long long v = (unsigned long long)sv;
+  Task t;
+  t.kind = v & 15;
+  t.layer = (v >> 4) & 15;
+  t.a = (v >> 8) & 0x3fff;
+  t.b = (v >> 22) & 0x3fff;
+  t.c = (v >> 36) & 0x3fff;
+  t.d = (v >> 50) & 0x3fff;
+  return t;
+}
+
+struct LayerArgs {
+  const float* gamma;
+  const void* w_router;
+  const float* bias;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const void* in;
+  void* out;
+  int* topk_idx;       // [T][k]
+  float* topk_w;       // [T][k]
+  int* lrank;          // [T][k] rank of the pair among its tile's pairs for the same expert
+  int* hist;           // [n_rt][E]
+  int* tile_off;       // [n_rt][E] first sorted row of tile tau's pairs for expert e
+  int* counts;         // [E]
+  int* offsets;        // [E+1]
+  int* rt_base;        // [E+1] first row tile of each expert
+  int* sorted_assign;  // [T*k]
+  int* pos;            // [T][k]
+  int* plan;           // [PL_WORDS]
+  int* ev_route;       // 1
+  int* ev_scan;        // 1
+  int* ev_gu;          // [max_rt][n1]
+  int* ev_comb;        // [n_rt]
+  int* ev_done;        // [n_rt]
+};
+
+struct Args {
+  int T, H, E, K, F, L;
+  float eps;
+  int mode, combine;
+  unsigned flags;
+  int n_rt, n1, n2, workers, max_rt, n_rt_cap, queue_len;
+  uint64_t timeout_ticks;
+  void* xq;        // [T][H] normalised input in storage precision
+  void* hbuf;      // [T*k][F] SwiGLU output, rows in sorted order
+  float* out_acc;  // [T][H] atomic-combine accumulator
+  float* ybuf;     // [T*k][H] ordered-combine rows
+  long long* queue;
+  int* sched;
+  LayerArgs layer[MAXL];
+};
+
+struct RouteSmem {
+  float xs[BT][XS_STRIDE];
+  float lg[BT][MAXE];
+  float rs[BT];
+  int sel[BT][MAXK];
+};
+struct ScanSmem {
+  int off[MAXE + 1];
+  int rtb[MAXE + 1];
+  int tmp[8];
+};
+struct TileSmem {
+  char gemm[KTile<float>::LDS_BYTES];
+  int row_tok[BM];
+  float row_gate[BM];
+};
+union SmemU {
+  RouteSmem r;
+  ScanSmem s;
+  TileSmem t;
+};
+struct Smem {
+  SmemU u;
+  Task task;
+  int flag;
+  int ibuf[4];
+};
+
+template <typename TE>
+ETC_DEV uint4 pack16(const float* v);
+template <>
+ETC_DEV uint4 pack16<bf16>(const float* v) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = f32_to_bf16_bits(v[2 * i]) | (f32_to_bf16_bits(v[2 * i + 1]) << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+template <>
+ETC_DEV uint4 pack16<float>(const float* v) {
+  return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+}
+
+ETC_DEV int tile_rows(const Args& p, int tau) { return min(BT, p.T - tau * BT); }
+
+// Largest e in [0, E) with rt_base[e] * mult <= idx: the expert owning task idx.
+ETC_DEV int owner_expert(const int* rt_base, int E, int idx, int mult) {
+  int lo = 0, hi = E;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (rt_base[mid] * mult <= idx) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+// ------------------------------------------------------------------ R: routing tile
+
+template <typename TE>
+ETC_DEV void route_task(const Args& p, const LayerArgs& L, int tau, Smem& sm) {
+  constexpr int EPC = 16 / (int)sizeof(TE);
+  constexpr int QMAX = MAXE * BT / NT;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int H = p.H, E = p.E, K = p.K;
+  const int t0 = tau * BT, nt = tile_rows(p, tau);
+  const TE* x = static_cast<const TE*>(L.in);
+  const TE* wr = static_cast<const TE*>(L.w_router);
+  TE* xq = static_cast<TE*>(p.xq);
+  RouteSmem& R = sm.u.r;
+  const TE* tag = nullptr;
+
+  // 1. reciprocal RMS per token (wave w: tokens w, w+4, ...)
+  for (int tt = w; tt < BT; tt += 4) {
+    float ss = 0.f;
+    if (tt < nt) {
+      const TE* row = x + (size_t)(t0 + tt) * H;
+      for (int h = lane * EPC; h < H; h += WAVE * EPC) {
+        float v[EPC];
+        expand16(*reinterpret_cast<const uint4*>(row + h), v, tag);
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) ss += v[i] * v[i];
+      }
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) R.rs[tt] = (tt < nt) ? 1.0f / sqrtf(ss / (float)H + p.eps) : 0.f;
+  }
+  __syncthreads();
+
+  // 2. normalised rows chunk by chunk: the storage copy goes to xq for the experts, the
+  //    float32 values feed the router (output o = (token o % 16, expert o / 16))
+  const int nout = BT * E;
+  float logit[QMAX];
+#pragma unroll
+  for (int q = 0; q < QMAX; ++q) logit[q] = 0.f;
+  for (int h0 = 0; h0 < H; h0 += RCH) {
+    const int hw = min(RCH, H - h0);
+    const int cpr = hw / EPC;  // chunks per row
+    for (int c = tid; c < BT * cpr; c += NT) {
+      const int tt = c / cpr, hc = (c % cpr) * EPC;
+      float v[EPC];
+      if (tt < nt) {
+        expand16(*reinterpret_cast<const uint4*>(x + (size_t)(t0 + tt) * H + h0 + hc), v, tag);
+        const float r = R.rs[tt];
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) v[i] = v[i] * r * L.gamma[h0 + hc + i];
+        *reinterpret_cast<uint4*>(xq + (size_t)(t0 + tt) * H + h0 + hc) = pack16<TE>(v);
+      } else {
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) v[i] = 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) R.xs[tt][hc + i] = v[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < QMAX; ++q) {
+      const int o = tid + NT * q;
+      if (o < nout) {
+        const int tt = o % BT, e = o / BT;
+        const TE* wrow = wr + (size_t)e * H + h0;
+        float part = 0.f;
+        for (int hh = 0; hh < hw; hh += EPC) {
+          float wv[EPC];
+          expand16(*reinterpret_cast<const uint4*>(wrow + hh), wv, tag);
+#pragma unroll
+          for (int i = 0; i < EPC; ++i) part += R.xs[tt][hh + i] * wv[i];
+        }
+        logit[q] += part;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int q = 0; q < QMAX; ++q) {
+    const int o = tid + NT * q;
+    if (o < nout) {
+      const int tt = o % BT, e = o / BT;
+      R.lg[tt][e] = logit[q] + (L.bias ? L.bias[e] : 0.f);
+    }
+  }
+  __syncthreads();
+
+  // 3. top-k by (logit desc, expert asc) with k rounds of a wave argmax; softmax over
+  //    the selected logits
+  for (int tt = w; tt < nt; tt += 4) {
+    float v[4];
+    int id[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + 64 * i;
+      v[i] = (e < E) ? R.lg[tt][e] : -FLT_MAX;
+      id[i] = (e < E) ? e : 0x7fffffff;
+    }
+    float selv[MAXK];
+    int sele[MAXK];
+#pragma unroll
+    for (int j = 0; j < MAXK; ++j) {
+      selv[j] = 0.f;
+      sele[j] = 0;
+      if (j < K) {
+        float bv = -FLT_MAX;
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (v[i] > bv || (v[i] == bv && id[i] < be)) { bv = v[i]; be = id[i]; }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+          const float ov = __shfl_xor(bv, off, WAVE);
+          const int oe = __shfl_xor(be, off, WAVE);
+          if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (id[i] == be) { v[i] = -FLT_MAX; id[i] = 0x7fffffff; }
+        selv[j] = bv;
+        sele[j] = be;
+      }
+    }
+    float z[MAXK], zsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < MAXK; ++j) {
+      z[j] = (j < K) ? expf(selv[j] - selv[0]) : 0.f;
+      zsum += z[j];
+    }
+    if (lane == 0) {
+      const int t = t0 + tt;
+#pragma unroll
+      for (int j = 0; j < MAXK; ++j)
+        if (j < K) {
+          L.topk_idx[t * K + j] = sele[j];
+          L.topk_w[t * K + j] = z[j] / zsum;
+          R.sel[tt][j] = sele[j];
+        }
+    }
+  }
+  __syncthreads();
+
+  // 4. rank of each pair among the tile's pairs of the same expert (tokens ascending;
+  //    a token never holds one expert twice) and the tile's expert histogram
+  for (int a = tid; a < nt * K; a += NT) {
+    const int tt = a / K, j = a % K, e = R.sel[tt][j];
+    int rank = 0;
+    for (int u = 0; u < tt; ++u)
+      for (int jj = 0; jj < K; ++jj) rank += (R.sel[u][jj] == e);
+    L.lrank[(t0 + tt) * K + j] = rank;
+  }
+  for (int e = tid; e < E; e += NT) {
+    int c = 0;
+    for (int u = 0; u < nt; ++u)
+      for (int jj = 0; jj < K; ++jj) c += (R.sel[u][jj] == e);
+    L.hist[tau * E + e] = c;
+  }
+
+  // 5. clear this tile's accumulator rows for the atomic combine
+  if (p.combine == ETC_COMBINE_ATOMIC) {
+    float4* acc = reinterpret_cast<float4*>(p.out_acc + (size_t)t0 * H);
+    for (int i = tid; i < nt * H / 4; i += NT) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+
+// ------------------------------------------------------------------ S: scan and permutation
+
+ETC_DEV int block_exclusive_scan(int v, int* tmp, int& total) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, WAVE);
+    if (lane >= off) x += y;
+  }
+  if (lane == 63) tmp[w] = x;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < w; ++i) before += tmp[i];
+  total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+  __syncthreads();
+  return before + x - v;
+}
+
+ETC_DEV void scan_task(const Args& p, const LayerArgs& L, int layer, Smem& sm) {
+  const int tid = threadIdx.x;
+  const int E = p.E, K = p.K, n_rt = p.n_rt;
+  ScanSmem& S = sm.u.s;
+
+  // counts per expert (thread e), then exclusive scans of counts and of row tiles
+  int cnt = 0;
+  if (tid < E) {
+    for (int tau = 0; tau < n_rt; tau += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = (tau + u < n_rt) ? L.hist[(tau + u) * E + tid] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) cnt += v[u];
+    }
+  }
+  int total_rows = 0, RT = 0;
+  const int off = block_exclusive_scan(cnt, S.tmp, total_rows);
+  const int rtb = block_exclusive_scan(cdiv(cnt, BM), S.tmp, RT);
+  if (tid < E) {
+    S.off[tid] = off;
+    S.rtb[tid] = rtb;
+    L.counts[tid] = cnt;
+    L.offsets[tid] = off;
+    L.rt_base[tid] = rtb;
+  }
+  if (tid == 0) {
+    S.off[E] = total_rows;
+    S.rtb[E] = RT;
+    L.offsets[E] = total_rows;
+    L.rt_base[E] = RT;
+  }
+  // first sorted row of every (routing tile, expert) block
+  if (tid < E) {
+    int run = off;
+    for (int tau = 0; tau < n_rt; tau += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = (tau + u < n_rt) ? L.hist[(tau + u) * E + tid] : 0;
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (tau + u < n_rt) {
+          L.tile_off[(tau + u) * E + tid] = run;
+          run += v[u];
+        }
+    }
+  }
+  // the down split: enough down tasks to feed every worker twice, when the combine
+  // is atomic (partial sums over ffn chunks add into the same accumulator)
+  if (tid == 0) {
+    int nS = 1;
+    if (p.combine == ETC_COMBINE_ATOMIC && RT > 0) {
+      const int want = 2 * p.workers;
+      nS = (RT * p.n2 >= want) ? 1 : min(p.n1, cdiv(want, RT * p.n2));
+    }
+    const int gpc = cdiv(p.n1, nS);
+    nS = cdiv(p.n1, gpc);
+    const int ngu = RT * p.n1, nd = RT * p.n2 * nS, nf = n_rt;
+    const int base = (layer == 0) ? 0 : p.layer[layer - 1].plan[PL_NEXTBASE];
+    L.plan[PL_RT] = RT;
+    L.plan[PL_NGU] = ngu;
+    L.plan[PL_ND] = nd;
+    L.plan[PL_NF] = nf;
+    L.plan[PL_NS] = nS;
+    L.plan[PL_GPC] = gpc;
+    L.plan[PL_NEXTBASE] = base + n_rt + 1 + ngu + nd + nf;
+  }
+  wg_publish();
+  fence_acquire_agent();  // tile_off written above by other lanes of this workgroup
+
+  // scatter: pair a = t*k + j goes to row tile_off[tau][e] + rank
+  for (int a = tid; a < p.T * K; a += NT) {
+    const int t = a / K, e = L.topk_idx[a];
+    const int r = L.tile_off[(t / BT) * E + e] + L.lrank[a];
+    L.sorted_assign[r] = a;
+    L.pos[a] = r;
+  }
+}
+
+// ------------------------------------------------------------------ GU / D / F
+
+template <typename TE>
+ETC_DEV void gateup_task(const Args& p, const LayerArgs& L, int e, int m, int n, Smem& sm) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  const int H = p.H, F = p.F, K = p.K;
+  TileSmem& Ts = sm.u.t;
+  const int r0 = L.offsets[e] + m * BM;
+  const int valid = min(BM, L.counts[e] - m * BM);
+  for (int i = tid; i < BM; i += NT) Ts.row_tok[i] = (i < valid) ? L.sorted_assign[r0 + i] / K : -1;
+  __syncthreads();
+
+  const TE* xq = static_cast<const TE*>(p.xq);
+  const TE* wg = static_cast<const TE*>(L.w_gate);
+  const TE* wu = static_cast<const TE*>(L.w_up);
+  const char* rowp[8];
+  const int row0 = tid >> 3;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int tok = Ts.row_tok[row0 + 32 * i];
+    rowp[i] = (tok >= 0) ? reinterpret_cast<const char*>(xq + (size_t)tok * H) : nullptr;
+    // B row b: 16-row blocks alternate gate / up over the same 16 ffn columns
+    const int b = row0 + 32 * i, blk = b >> 4;
+    const int f = n * BN1 + (blk >> 1) * 16 + (b & 15);
+    const TE* src = (blk & 1) ? wu : wg;
+    rowp[4 + i] = reinterpret_cast<const char*>(src + ((size_t)e * F + f) * H);
+  }
+  f32x4 acc[4][4];
+  KTile<TE>::run(Ts.gemm, rowp, H, acc);
+
+  TE* hb = static_cast<TE*>(p.hbuf);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
+        if (row < valid) {
+          const int f = n * BN1 + (2 * wn + jj) * 16 + (lane & 15);
+          const float g = acc[i][2 * jj][r], u = acc[i][2 * jj + 1][r];
+          Elem<TE>::store(hb, (size_t)(r0 + row) * F + f, g / (1.0f + expf(-g)) * u);
+        }
+      }
+}
+
+template <typename TE>
+ETC_DEV void down_task(const Args& p, const LayerArgs& L, int e, int m, int n2i, int s, int gpc,
+                       Smem& sm) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  const int H = p.H, F = p.F, K = p.K;
+  TileSmem& Ts = sm.u.t;
+  const int r0 = L.offsets[e] + m * BM;
+  const int valid = min(BM, L.counts[e] - m * BM);
+  for (int i = tid; i < BM; i += NT) {
+    if (i < valid) {
+      const int a = L.sorted_assign[r0 + i];
+      Ts.row_tok[i] = a / K;
+      Ts.row_gate[i] = L.topk_w[a];
+    } else {
+      Ts.row_tok[i] = -1;
+      Ts.row_gate[i] = 0.f;
+    }
+  }
+  __syncthreads();
+
+  const int kb = s * gpc * BN1;
+  const int klen = min(F, kb + gpc * BN1) - kb;
+  const TE* hb = static_cast<const TE*>(p.hbuf);
+  const TE* wd = static_cast<const TE*>(L.w_down);
+  const char* rowp[8];
+  const int row0 = tid >> 3;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = row0 + 32 * i;
+    rowp[i] = (r < valid) ? reinterpret_cast<const char*>(hb + (size_t)(r0 + r) * F + kb) : nullptr;
+    rowp[4 + i] = reinterpret_cast<const char*>(wd + ((size_t)e * H + n2i * BN2 + r) * F + kb);
+  }
+  f32x4 acc[4][4];
+  KTile<TE>::run(Ts.gemm, rowp, klen, acc);
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
+        if (row < valid) {
+          const int col = n2i * BN2 + wn * 64 + j * 16 + (lane & 15);
+          if (p.combine == ETC_COMBINE_ATOMIC)
+            atomicAdd(p.out_acc + (size_t)Ts.row_tok[row] * H + col, Ts.row_gate[row] * acc[i][j][r]);
+          else
+            p.ybuf[(size_t)(r0 + row) * H + col] = acc[i][j][r];
+        }
+      }
+}
+
+template <typename TE>
+ETC_DEV void finalize_task(const Args& p, const LayerArgs& L, int tau) {
+  constexpr int EPC = 16 / (int)sizeof(TE);
+  const int tid = threadIdx.x, H = p.H, K = p.K;
+  const int t0 = tau * BT, nt = tile_rows(p, tau);
+  TE* out = static_cast<TE*>(L.out);
+  for (int c = tid; c < nt * H / EPC; c += NT) {
+    const int t = t0 + (c * EPC) / H, h = (c * EPC) % H;
+    float v[EPC];
+    if (p.combine == ETC_COMBINE_ATOMIC) {
+#pragma unroll
+      for (int i = 0; i < EPC; i += 4) {
+        const float4 a = *reinterpret_cast<const float4*>(p.out_acc + (size_t)t * H + h + i);
+        v[i] = a.x; v[i + 1] = a.y; v[i + 2] = a.z; v[i + 3] = a.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) v[i] = 0.f;
+      for (int j = 0; j < K; ++j) {  // slot order
+        const float g = L.topk_w[t * K + j];
+        const float* y = p.ybuf + (size_t)L.pos[t * K + j] * H + h;
+#pragma unroll
+        for (int i = 0; i < EPC; i += 4) {
+          const float4 a = *reinterpret_cast<const float4*>(y + i);
+          v[i] += g * a.x; v[i + 1] += g * a.y; v[i + 2] += g * a.z; v[i + 3] += g * a.w;
+        }
+      }
+    }
+    *reinterpret_cast<uint4*>(out + (size_t)t * H + h) = pack16<TE>(v);
+  }
+}
+
+// ------------------------------------------------------------------ scheduling
+
+// Static: the ticket's task; waits for S of a layer before decoding past it.
+ETC_DEV bool claim_static(const Args& p, Task& t, uint64_t deadline) {
+  const int ticket = atomicAdd(p.sched + W_TICKET, 1);
+  int base = 0;
+  for (int l = 0; l < p.L; ++l) {
+    const LayerArgs& L = p.layer[l];
+    t.layer = l;
+    if (ticket < base + p.n_rt) { t.kind = K_R; t.a = ticket - base; return true; }
+    if (ticket == base + p.n_rt) { t.kind = K_S; return true; }
+    if (!spin_until_geq(L.ev_scan, 1, p.sched, deadline, 10 + l)) return false;
+    int off = ticket - base - p.n_rt - 1;
+    const int ngu = L.plan[PL_NGU], nd = L.plan[PL_ND], nf = L.plan[PL_NF], nS = L.plan[PL_NS];
+    if (off < ngu) {
+      const int e = owner_expert(L.rt_base, p.E, off, p.n1);
+      const int me = L.rt_base[e + 1] - L.rt_base[e];
+      const int loc = off - L.rt_base[e] * p.n1;
+      t.kind = K_GU; t.a = e; t.b = loc % me; t.c = loc / me;
+      return true;
+    }
+    off -= ngu;
+    if (off < nd) {
+      const int e = owner_expert(L.rt_base, p.E, off, p.n2 * nS);
+      const int me = L.rt_base[e + 1] - L.rt_base[e];
+      const int loc = off - L.rt_base[e] * p.n2 * nS;
+      t.kind = K_D; t.a = e; t.b = loc % me; t.c = (loc / me) % p.n2; t.d = loc / (me * p.n2);
+      return true;
+    }
+    off -= nd;
+    if (off < nf) { t.kind = K_F; t.a = off; return true; }
+    base = L.plan[PL_NEXTBASE];
+  }
+  t.kind = K_NONE;
+  return true;
+}
+
+// Dynamic: the next queue slot; slots below n_rt are the first layer's R tasks.
+ETC_DEV bool claim_dynamic(const Args& p, Task& t, uint64_t deadline) {
+  const int slot = atomicAdd(p.sched + W_QHEAD, 1);
+  if (slot < p.n_rt) {
+    t.kind = K_R; t.layer = 0; t.a = slot;
+    return true;
+  }
+  // every slot below the final queue total is filled exactly once; a workgroup that
+  // drew a slot past the end of the array only waits for the total to be known
+  const bool in_array = slot < p.queue_len;
+  int it = 0;
+  while (true) {
+    const long long v = in_array ? q_load(p.queue + slot) : 0;
+    if (v != 0) {
+      q_store_relaxed(p.queue + slot, 0);  // the slot is clean for the next call
+      t = dec(v);
+      return true;
+    }
+    if (ev_load(p.sched + W_PLANNED) == p.L && slot >= ev_load_relaxed(p.sched + W_QTOTAL)) {
+      t.kind = K_NONE;
+      return true;
+    }
+    if ((++it & 15) == 0) {
+      if (ev_load_relaxed(p.sched + W_ABORT)) return false;
+      if (now_ticks() > deadline) {
+        ev_store_relaxed(p.sched + W_STATUS, ETC_ERR_TIMEOUT);
+        ev_store_relaxed(p.sched + W_AUX, 2);
+        ev_store(p.sched + W_ABORT, 1);
+        return false;
+      }
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// Static mode: wait until the task's inputs are complete (thread 0).
+ETC_DEV bool wait_deps(const Args& p, const Task& t, uint64_t deadline) {
+  const LayerArgs& L = p.layer[t.layer];
+  switch (t.kind) {
+    case K_R:
+      if (t.layer == 0) return true;
+      return spin_until_geq(p.layer[t.layer - 1].ev_done + t.a, 1, p.sched, deadline, 20);
+    case K_S:
+      return spin_until_geq(L.ev_route, p.n_rt, p.sched, deadline, 21);
+    case K_D: {
+      const int gpc = L.plan[PL_GPC];
+      const int rt = L.rt_base[t.a] + t.b;
+      const int need = min(gpc, p.n1 - t.d * gpc);
+      return spin_until_geq(L.ev_gu + rt * p.n1 + t.d, need, p.sched, deadline, 22);
+    }
+    case K_F: {
+      const int target = tile_rows(p, t.a) * p.K * p.n2 * L.plan[PL_NS];
+      return spin_until_geq(L.ev_comb + t.a, target, p.sched, deadline, 23);
+    }
+    default:
+      return true;
+  }
+}
+
+// Enqueue n tasks (dynamic mode); every thread of the workgroup calls this.
+template <typename Gen>
+ETC_DEV void push_many(const Args& p, Smem& sm, int n, Gen gen) {
+  if (threadIdx.x == 0) sm.ibuf[0] = p.n_rt + atomicAdd(p.sched + W_QTAIL, n);
+  __syncthreads();
+  const int base = sm.ibuf[0];
+  fence_release_agent();
+  for (int i = threadIdx.x; i < n; i += NT) q_store_relaxed(p.queue + base + i, enc(gen(i)));
+  __syncthreads();
+}
+
+ETC_DEV void push_one(const Args& p, const Task& t) {
+  const int slot = p.n_rt + atomicAdd(p.sched + W_QTAIL, 1);
+  fence_release_agent();
+  q_store_relaxed(p.queue + slot, enc(t));
+}
+
+// After S: static mode publishes ev_scan; dynamic mode enqueues every gate/up task and
+// adds the layer's task count to the queue total.
+ETC_DEV void after_scan(const Args& p, int layer, Smem& sm) {
+  const LayerArgs& L = p.layer[layer];
+  wg_publish();
+  if (threadIdx.x == 0) ev_store(L.ev_scan, 1);  // both modes: the event tensor is complete
+  if (p.mode == ETC_SCHED_STATIC) return;
+  const int RT = sm.u.s.rtb[p.E];
+  const int n1 = p.n1;
+  push_many(p, sm, RT * n1, [&](int i) {
+    const int e = owner_expert(sm.u.s.rtb, p.E, i, n1);
+    const int me = sm.u.s.rtb[e + 1] - sm.u.s.rtb[e];
+    const int loc = i - sm.u.s.rtb[e] * n1;
+    Task t;
+    t.kind = K_GU; t.layer = layer; t.a = e; t.b = loc % me; t.c = loc / me; t.d = 0;
+    return t;
+  });
+  if (threadIdx.x == 0) {
+    // the plan words are in global memory, written by this thread before wg_publish
+    const int added = L.plan[PL_NGU] + L.plan[PL_ND] + L.plan[PL_NF] +
+                      (layer + 1 < p.L ? p.n_rt : 0) + (layer == 0 ? p.n_rt : 0);
+    atomicAdd(p.sched + W_QTOTAL, added);
+    ev_add(p.sched + W_PLANNED, 1);
+  }
+}
+
+template <typename TE>
+__global__ __launch_bounds__(NT) void moe_kernel(Args p) {
+  __shared__ Smem sm;
+  const int tid = threadIdx.x;
+  const uint64_t deadline = now_ticks() + p.timeout_ticks;
+
+  while (true) {
+    if (tid == 0) {
+      Task t;
+      t.kind = K_NONE; t.layer = 0; t.a = t.b = t.c = t.d = 0;
+      const bool ok = (p.mode == ETC_SCHED_STATIC) ? claim_static(p, t, deadline)
+                                                    : claim_dynamic(p, t, deadline);
+      if (!ok) t.kind = K_NONE;
+      if (ok && t.kind != K_NONE && p.mode == ETC_SCHED_STATIC && !wait_deps(p, t, deadline))
+        t.kind = K_NONE;
+      sm.task = t;
+    }
+    __syncthreads();
+    const Task t = sm.task;
+    __syncthreads();
+    if (t.kind == K_NONE) break;
+    const LayerArgs& L = p.layer[t.layer];
+
+    if (t.kind == K_R) {
+      route_task<TE>(p, L, t.a, sm);
+      wg_publish();
+      if (tid == 0) {
+        const int old = ev_add(L.ev_route, 1);
+        sm.flag = (p.mode == ETC_SCHED_DYNAMIC && old + 1 == p.n_rt) ? 1 : 0;
+      }
+      __syncthreads();
+      if (sm.flag) {  // last routing tile of the layer: S runs here (dynamic mode)
+        scan_task(p, L, t.layer, sm);
+        after_scan(p, t.layer, sm);
+      }
+    } else if (t.kind == K_S) {
+      scan_task(p, L, t.layer, sm);
+      after_scan(p, t.layer, sm);
+    } else if (t.kind == K_GU) {
+      gateup_task<TE>(p, L, t.a, t.b, t.c, sm);
+      wg_publish();
+      const int gpc = L.plan[PL_GPC];
+      const int s = t.c / gpc;
+      if (tid == 0) {
+        const int rt = L.rt_base[t.a] + t.b;
+        const int need = min(gpc, p.n1 - s * gpc);
+        const int old = ev_add(L.ev_gu + rt * p.n1 + s, 1);
+        sm.flag = (p.mode == ETC_SCHED_DYNAMIC && old + 1 == need) ? 1 : 0;
+      }
+      __syncthreads();
+      if (sm.flag) {
+        const int layer = t.layer, e = t.a, m = t.b;
+        push_many(p, sm, p.n2, [&](int i) {
+          Task d;
+          d.kind = K_D; d.layer = layer; d.a = e; d.b = m; d.c = i; d.d = s;
+          return d;
+        });
+      }
+    } else if (t.kind == K_D) {
+      down_task<TE>(p, L, t.a, t.b, t.c, t.d, L.plan[PL_GPC], sm);
+      wg_publish();
+      // one signal per run of rows in the same routing tile (rows are token-sorted)
+      const int valid = min(BM, L.counts[t.a] - t.b * BM);
+      if (tid < valid) {
+        const int tau = sm.u.t.row_tok[tid] / BT;
+        if (tid == 0 || sm.u.t.row_tok[tid - 1] / BT != tau) {
+          int len = 1;
+          while (tid + len < valid && sm.u.t.row_tok[tid + len] / BT == tau) ++len;
+          const int old = ev_add(L.ev_comb + tau, len);
+          const int target = tile_rows(p, tau) * p.K * p.n2 * L.plan[PL_NS];
+          if (p.mode == ETC_SCHED_DYNAMIC && old + len == target) {
+            Task f;
+            f.kind = K_F; f.layer = t.layer; f.a = tau; f.b = f.c = f.d = 0;
+            push_one(p, f);
+          }
+        }
+      }
+      __syncthreads();
+    } else if (t.kind == K_F) {
+      finalize_task<TE>(p, L, t.a);
+      wg_publish();
+      if (tid == 0) {
+        ev_store(L.ev_done + t.a, 1);
+        if (p.mode == ETC_SCHED_DYNAMIC && t.layer + 1 < p.L) {
+          Task r;
+          r.kind = K_R; r.layer = t.layer + 1; r.a = t.a; r.b = r.c = r.d = 0;
+          push_one(p, r);
+        }
+      }
+      __syncthreads();
+    }
+  }
+
+  // the last workgroup out clears the event counters and control words
+  wg_publish();
+  if (tid == 0) sm.flag = (atomicAdd(p.sched + W_EXIT, 1) == (int)gridDim.x - 1) ? 1 : 0;
+  __syncthreads();
+  if (sm.flag && !(p.flags & ETC_FLAG_KEEP_COUNTERS)) {
+    for (int l = 0; l < p.L; ++l) {
+      const LayerArgs& L = p.layer[l];
+      if (tid == 0) { ev_store_relaxed(L.ev_route, 0); ev_store_relaxed(L.ev_scan, 0); }
+      for (int i = tid; i < p.max_rt * p.n1; i += NT) ev_store_relaxed(L.ev_gu + i, 0);
+      for (int i = tid; i < p.n_rt_cap; i += NT) {
+        ev_store_relaxed(L.ev_comb + i, 0);
+        ev_store_relaxed(L.ev_done + i, 0);
+      }
+    }
+    if (tid < W_NWORDS && tid != W_STATUS && tid != W_AUX) ev_store_relaxed(p.sched + tid, 0);
+  }
+}
+
+// ------------------------------------------------------------------ host side
+
+struct Layout {
+  size_t sched, queue, xq, hbuf, out_acc, ybuf, act, total;
+  struct {
+    size_t topk_idx, topk_w, lrank, hist, tile_off, counts, offsets, rt_base, sorted_assign, pos,
+        plan, ev_route, ev_scan, ev_gu, ev_comb, ev_done;
+  } l[MAXL];
+  int n_rt, max_rt, n1, n2, queue_len;
+};
+
+inline Layout layout(int Tm, int H, int E, int K, int F, int nl, int es, bool ordered) {
+  Layout Y;
+  Y.n_rt = cdiv(Tm, BT);
+  Y.max_rt = (Tm * K) / BM + (E < Tm * K ? E : Tm * K);
+  Y.n1 = F / BN1;
+  Y.n2 = H / BN2;
+  host::Carve c;
+  Y.sched = c.take(W_NWORDS * sizeof(int));
+  for (int l = 0; l < nl; ++l) {  // counters first: the control region
+    Y.l[l].ev_route = c.take(sizeof(int));
+    Y.l[l].ev_scan = c.take(sizeof(int));
+    Y.l[l].ev_gu = c.take((size_t)Y.max_rt * Y.n1 * sizeof(int));
+    Y.l[l].ev_comb = c.take((size_t)Y.n_rt * sizeof(int));
+    Y.l[l].ev_done = c.take((size_t)Y.n_rt * sizeof(int));
+    Y.l[l].plan = c.take(PL_WORDS * sizeof(int));
+  }
+  const long per_layer = (long)Y.n_rt * 3 + (long)Y.max_rt * Y.n1 + 2L * MAX_WORKERS +
+                         (long)Y.max_rt * Y.n2 + 64;
+  // + room for the one extra slot each worker draws before it sees the end
+  Y.queue_len = (int)(Y.n_rt + per_layer * nl + MAX_WORKERS);
+  Y.queue = c.take((size_t)Y.queue_len * sizeof(long long));
+  for (int l = 0; l < nl; ++l) {
+    const size_t pairs = (size_t)Tm * K;
+    Y.l[l].topk_idx = c.take(pairs * 4);
+    Y.l[l].topk_w = c.take(pairs * 4);
+    Y.l[l].lrank = c.take(pairs * 4);
+    Y.l[l].hist = c.take((size_t)Y.n_rt * E * 4);
+    Y.l[l].tile_off = c.take((size_t)Y.n_rt * E * 4);
+    Y.l[l].counts = c.take((size_t)E * 4);
+    Y.l[l].offsets = c.take((size_t)(E + 1) * 4);
+    Y.l[l].rt_base = c.take((size_t)(E + 1) * 4);
+    Y.l[l].sorted_assign = c.take(pairs * 4);
+    Y.l[l].pos = c.take(pairs * 4);
+  }
+  Y.xq = c.take((size_t)Tm * H * es);
+  Y.hbuf = c.take((size_t)Tm * K * F * es);
+  Y.out_acc = c.take((size_t)Tm * H * 4);
+  Y.ybuf = ordered ? c.take((size_t)Tm * K * H * 4) : 0;
+  Y.act = c.take((size_t)(nl > 1 ? nl - 1 : 0) * Tm * H * es);
+  Y.total = c.off;
+  return Y;
+}
+
+}  // namespace moe
+}  // namespace etc
+
+using namespace etc;
+
+static int moe_occupancy(int dev, etc_dtype dt) {
+  static int occ[host::MAX_DEVICES][2] = {{0}};
+  if (occ[dev][dt] == 0) {
+    int v = 0;
+    hipError_t e = (dt == ETC_DTYPE_BF16)
+                       ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, moe::moe_kernel<bf16>, NT, 0)
+                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, moe::moe_kernel<float>, NT, 0);
+    if (e != hipSuccess || v < 1) v = 1;
+    occ[dev][dt] = v;
+  }
+  return occ[dev][dt];
+}
+
+static etc_status moe_shape_check(int32_t Tm, int32_t H, int32_t E, int32_t K, int32_t F, int32_t nl,
+                                  etc_dtype dt) {
+  if (Tm < 0 || H < 1 || E < 1 || K < 1 || F < 1 || nl < 1) return ETC_ERR_INVALID_ARG;
+  if (dt != ETC_DTYPE_F32 && dt != ETC_DTYPE_BF16) return ETC_ERR_INVALID_ARG;
+  if (K > E) return ETC_ERR_INVALID_ARG;
+  if (H % moe::BN2 || F % moe::BN1 || E > moe::MAXE || K > moe::MAXK || nl > moe::MAXL ||
+      Tm > moe::MAX_TOKENS)
+    return ETC_ERR_UNSUPPORTED;
+  return ETC_OK;
+}
+
+ETC_API size_t etc_moe_workspace_size(int32_t max_tokens, int32_t hidden, int32_t experts, int32_t top_k,
+                                      int32_t ffn, int32_t num_layers, etc_dtype dtype, etc_combine combine) {
+  if (moe_shape_check(max_tokens, hidden, experts, top_k, ffn, num_layers, dtype) != ETC_OK) return 0;
+  if (combine != ETC_COMBINE_ATOMIC && combine != ETC_COMBINE_ORDERED) return 0;
+  const int es = dtype == ETC_DTYPE_BF16 ? 2 : 4;
+  return moe::layout(max_tokens < 1 ? 1 : max_tokens, hidden, experts, top_k, ffn, num_layers, es,
+                     combine == ETC_COMBINE_ORDERED)
+      .total;
+}
+
+ETC_API etc_status etc_moe_workspace_layout(int32_t max_tokens, int32_t hidden, int32_t experts,
+                                            int32_t top_k, int32_t ffn, int32_t num_layers, etc_dtype dtype,
+                                            etc_combine combine, int32_t layer, int64_t* out) {
+  const etc_status st = moe_shape_check(max_tokens, hidden, experts, top_k, ffn, num_layers, dtype);
+  if (st != ETC_OK) return st;
+  if (!out || layer < 0 || layer >= num_layers) return ETC_ERR_INVALID_ARG;
+  const int es = dtype == ETC_DTYPE_BF16 ? 2 : 4;
+  const moe::Layout Y = moe::layout(max_tokens < 1 ? 1 : max_tokens, hidden, experts, top_k, ffn, num_layers,
+                                    es, combine == ETC_COMBINE_ORDERED);
+  out[0] = (int64_t)Y.l[layer].ev_route;
+  out[1] = (int64_t)Y.l[layer].ev_scan;
+  out[2] = (int64_t)Y.l[layer].ev_gu;
+  out[3] = (int64_t)Y.l[layer].ev_comb;
+  out[4] = (int64_t)Y.l[layer].ev_done;
+  out[5] = (int64_t)Y.l[layer].plan;
+  out[6] = Y.max_rt;
+  out[7] = Y.n1;
+  out[8] = Y.n_rt;
+  out[9] = moe::BT;
+  out[10] = moe::BM;
+  out[11] = moe::BN1;
+  out[12] = moe::BN2;
+  return ETC_OK;
+}
+
+ETC_API int32_t etc_default_workers(int32_t kind, etc_dtype dtype);
+
+ETC_API etc_status etc_moe_layer(int32_t T, int32_t H, int32_t E, int32_t K, int32_t F, int32_t nl,
+                                 etc_dtype dtype, float eps, const etc_moe_weights* weights, const void* x,
+                                 void* out, void* layer_out, const etc_moe_routing* routing, void* workspace,
+                                 size_t workspace_bytes, int32_t max_tokens, etc_sched_mode mode,
+                                 etc_combine combine, uint32_t flags, int32_t workers, void* stream) {
+  etc_status st = moe_shape_check(max_tokens, H, E, K, F, nl, dtype);
+  if (st != ETC_OK) return st;
+  if (T < 0 || T > max_tokens || !(eps >= 0.f)) return ETC_ERR_INVALID_ARG;
+  if (mode != ETC_SCHED_STATIC && mode != ETC_SCHED_DYNAMIC) return ETC_ERR_INVALID_ARG;
+  if (combine != ETC_COMBINE_ATOMIC && combine != ETC_COMBINE_ORDERED) return ETC_ERR_INVALID_ARG;
+  if (!weights || !x || !out) return ETC_ERR_INVALID_ARG;
+  if (!host::aligned16(x) || !host::aligned16(out) || (layer_out && !host::aligned16(layer_out)))
+    return ETC_ERR_INVALID_ARG;
+  for (int l = 0; l < nl; ++l) {
+    const etc_moe_weights& w = weights[l];
+    if (!w.gamma || !w.w_router || !w.w_gate || !w.w_up || !w.w_down) return ETC_ERR_INVALID_ARG;
+    if (!host::aligned16(w.w_router) || !host::aligned16(w.w_gate) || !host::aligned16(w.w_up) ||
+        !host::aligned16(w.w_down))
+      return ETC_ERR_INVALID_ARG;
+  }
+  if (routing) {
+    const void* ps[4] = {routing->topk_idx, routing->topk_w, routing->expert_counts, routing->sorted_assign};
+    for (const void* q : ps)
+      if (q && (reinterpret_cast<uintptr_t>(q) & 3u)) return ETC_ERR_INVALID_ARG;
+  }
+  const int es = dtype == ETC_DTYPE_BF16 ? 2 : 4;
+  const moe::Layout Y = moe::layout(max_tokens < 1 ? 1 : max_tokens, H, E, K, F, nl, es,
+                                    combine == ETC_COMBINE_ORDERED);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || workspace_bytes < Y.total)
+    return ETC_ERR_WORKSPACE;
+  const int dev = host::current_gfx950_device();
+  if (dev < 0) return ETC_ERR_NO_DEVICE;
+  if (T == 0) return ETC_OK;
+
+  char* ws = static_cast<char*>(workspace);
+  moe::Args p;
+  memset(&p, 0, sizeof(p));
+  p.T = T; p.H = H; p.E = E; p.K = K; p.F = F; p.L = nl;
+  p.eps = eps;
+  p.mode = mode;
+  p.combine = combine;
+  p.flags = flags;
+  p.n_rt = cdiv(T, moe::BT);
+  p.n1 = Y.n1;
+  p.n2 = Y.n2;
+  p.max_rt = Y.max_rt;
+  p.queue_len = Y.queue_len;
+  p.n_rt_cap = Y.n_rt;
+  p.timeout_ticks = 500000000ull;  // 5 s of the 100 MHz real-time clock
+  int grid = host::grid_size(workers, host::device_cus(dev), moe_occupancy(dev, dtype));
+  if (grid > moe::MAX_WORKERS) grid = moe::MAX_WORKERS;
+  p.workers = grid;
+  p.xq = ws + Y.xq;
+  p.hbuf = ws + Y.hbuf;
+  p.out_acc = reinterpret_cast<float*>(ws + Y.out_acc);
+  p.ybuf = combine == ETC_COMBINE_ORDERED ? reinterpret_cast<float*>(ws + Y.ybuf) : nullptr;
+  p.queue = reinterpret_cast<long long*>(ws + Y.queue);
+  p.sched = reinterpret_cast<int*>(ws + Y.sched);
+  const size_t act_bytes = (size_t)T * H * es;
+  for (int l = 0; l < nl; ++l) {
+    moe::LayerArgs& L = p.layer[l];
+    const etc_moe_weights& w = weights[l];
+    L.gamma = w.gamma;
+    L.w_router = w.w_router;
+    L.bias = w.router_bias;
+    L.w_gate = w.w_gate;
+    L.w_up = w.w_up;
+    L.w_down = w.w_down;
+    L.in = (l == 0) ? x : p.layer[l - 1].out;
+    if (l == nl - 1) L.out = out;
+    else if (layer_out) L.out = static_cast<char*>(layer_out) + (size_t)l * act_bytes;
+    else L.out = ws + Y.act + (size_t)l * max_tokens * H * es;
+    const size_t pairs = (size_t)T * K;
+    L.topk_idx = (routing && routing->topk_idx) ? routing->topk_idx + l * pairs
+                                                : reinterpret_cast<int*>(ws + Y.l[l].topk_idx);
+    L.topk_w = (routing && routing->topk_w) ? routing->topk_w + l * pairs
+                                            : reinterpret_cast<float*>(ws + Y.l[l].topk_w);
+    L.counts = (routing && routing->expert_counts) ? routing->expert_counts + (size_t)l * E
+                                                   : reinterpret_cast<int*>(ws + Y.l[l].counts);
+    L.sorted_assign = (routing && routing->sorted_assign) ? routing->sorted_assign + l * pairs
+                                                          : reinterpret_cast<int*>(ws + Y.l[l].sorted_assign);
+    L.lrank = reinterpret_cast<int*>(ws + Y.l[l].lrank);
+    L.hist = reinterpret_cast<int*>(ws + Y.l[l].hist);
+    L.tile_off = reinterpret_cast<int*>(ws + Y.l[l].tile_off);
+    L.offsets = reinterpret_cast<int*>(ws + Y.l[l].offsets);
+    L.rt_base = reinterpret_cast<int*>(ws + Y.l[l].rt_base);
+    L.pos = reinterpret_cast<int*>(ws + Y.l[l].pos);
+    L.plan = reinterpret_cast<int*>(ws + Y.l[l].plan);
+    L.ev_route = reinterpret_cast<int*>(ws + Y.l[l].ev_route);
+    L.ev_scan = reinterpret_cast<int*>(ws + Y.l[l].ev_scan);
+    L.ev_gu = reinterpret_cast<int*>(ws + Y.l[l].ev_gu);
+    L.ev_comb = reinterpret_cast<int*>(ws + Y.l[l].ev_comb);
+    L.ev_done = reinterpret_cast<int*>(ws + Y.l[l].ev_done);
+  }
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (dtype == ETC_DTYPE_BF16)
+    hipLaunchKernelGGL(moe::moe_kernel<bf16>, dim3(grid), dim3(NT), 0, s, p);
+  else
+    hipLaunchKernelGGL(moe::moe_kernel<float>, dim3(grid), dim3(NT), 0, s, p);
+  return hipGetLastError() == hipSuccess ? ETC_OK : ETC_ERR_HIP;
+}
+
+int splitk_default_workers(int dev);
+
+ETC_API int32_t etc_default_workers(int32_t kind, etc_dtype dtype) {
+  const int dev = host::current_gfx950_device();
+  if (dev < 0) return 0;
+  if (kind == 1) return splitk_default_workers(dev);
+  if (dtype != ETC_DTYPE_F32 && dtype != ETC_DTYPE_BF16) return 0;
+  int g = host::device_cus(dev) * moe_occupancy(dev, dtype);
+  return g > moe::MAX_WORKERS ? moe::MAX_WORKERS : g;
+}

@@ -1,0 +1,304 @@
+// Split-K GEMM driven by event counters, as one persistent kernel.
+//
+// The podcast episode page "Prompt Boundary-Aware Scheduling with Event Tensors for
+// Dynamic Kernels" (summary) illustrates waiting on true data dependencies with a
+// split-K summation: C = A B with the K range cut into S slices; each (tile, slice)
+// task produces a partial tile, and the tile's sum starts as soon as its S partials
+// exist instead of after a kernel boundary.  Here the event tensor is ev[tile], one
+// int32 per output tile with target S.
+//
+// Tasks, for T_out = ceil(M/64) * N/128 output tiles of 64 x 128:
+//   P(tile, s)  float32 partial of slice s (K/S columns of A): 4 waves, each 64 rows x
+//               32 columns of bf16 MFMA 16x16x32, A and B staged through LDS; stores
+//               the partial, then ev[tile] += 1 (release).
+//   R(tile)     waits ev[tile] >= S (acquire), C = P_0 + P_1 + ... + P_{S-1}.
+// Static mode: tickets 0 .. S*T_out-1 are the partials (slice-major, so the first
+// wave of tickets spreads over every tile), then T_out reduction tickets.  Dynamic
+// mode: only partial tasks are handed out; the partial whose add returns S-1 runs the
+// reduction itself (last arriver).
+//
+// B is [K][N] (N-contiguous) while the MFMA wants 8 consecutive k per lane, so the B
+// stage keeps LDS rows of N (one per k) padded to 132 elements and each lane gathers
+// its 8 k values with 2-byte reads; the 4 k-groups of a quarter-wave then start 16
+// banks apart and do not conflict.
+#include "common.hpp"
+#include "host.hpp"
+#include "mfma.hpp"
+
+namespace etc {
+namespace splitk {
+
+constexpr int TM = 64, TN = 128, BK = 64;
+constexpr int BSTRIDE = TN + 4;                      // elements per LDS row of B
+constexpr int A_STAGE = TM * 128;                    // bytes (64 rows x 64 bf16)
+constexpr int B_STAGE = BK * BSTRIDE * 2;            // bytes (64 k-rows x 132 bf16)
+constexpr int STAGE = A_STAGE + B_STAGE;
+constexpr int A_LOADS = TM * 8 / NT;                 // 16-byte chunks per thread: 2
+constexpr int B_LOADS = BK * (TN / 8) / NT;          // 4
+
+struct Args {
+  int M, N, K, S;
+  int tiles_m, tiles_n, tiles;
+  int mode;
+  uint32_t flags;
+  const bf16* A;
+  const bf16* B;
+  float* C;
+  float* part;   // [tiles][S][TM][TN]
+  int* sched;    // control words
+  int* ev;       // [tiles]
+  uint64_t timeout_ticks;
+};
+
+struct Smem {
+  char stage[2][STAGE];
+  int task;  // broadcast slot
+  int flag;
+};
+
+ETC_DEV void partial_task(const Args& p, Smem& sm, int tile, int s) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tm = tile / p.tiles_n, tn = tile % p.tiles_n;
+  const int m0 = tm * TM, n0 = tn * TN;
+  const int ks = p.K / p.S, kbeg = s * ks;
+  const int nk = ks / BK;
+
+  // this thread's load assignments
+  const bf16* arow[A_LOADS];
+  int achunk[A_LOADS], arowi[A_LOADS];
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) {
+    int q = tid + NT * i;
+    arowi[i] = q >> 3;
+    achunk[i] = q & 7;
+    int m = m0 + arowi[i];
+    arow[i] = (m < p.M) ? p.A + (long)m * p.K + kbeg + achunk[i] * 8 : nullptr;
+  }
+  int bk[B_LOADS], bc[B_LOADS];
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i) {
+    int q = tid + NT * i;
+    bk[i] = q >> 4;
+    bc[i] = q & 15;
+  }
+
+  uint4 ra[A_LOADS], rb[B_LOADS];
+  auto gload = [&](int kt) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i)
+      ra[i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + k0) : zero4();
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i)
+      rb[i] = *reinterpret_cast<const uint4*>(p.B + (long)(kbeg + k0 + bk[i]) * p.N + n0 + bc[i] * 8);
+  };
+  auto sstore = [&](int buf) {
+    char* base = sm.stage[buf];
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) lds_put_chunk(base, arowi[i], achunk[i], ra[i]);
+    char* bb = base + A_STAGE;
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) {
+      uint2* d = reinterpret_cast<uint2*>(bb + (bk[i] * BSTRIDE + bc[i] * 8) * 2);
+      d[0] = make_uint2(rb[i].x, rb[i].y);
+      d[1] = make_uint2(rb[i].z, rb[i].w);
+    }
+  };
+
+  f32x4 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    if (kt + 1 < nk) gload(kt + 1);
+    const char* base = sm.stage[kt & 1];
+    const uint16_t* bsm = reinterpret_cast<const uint16_t*>(base + A_STAGE);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      uint4 a[4], b[2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = lds_chunk(base, i * 16 + (lane & 15), kk * 4 + (lane >> 4));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int n = w * 32 + j * 16 + (lane & 15);
+        const int k = kk * 32 + (lane >> 4) * 8;
+        uint32_t h[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) h[q] = bsm[(k + q) * BSTRIDE + n];
+        b[j] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                          h[6] | (h[7] << 16));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) mma16(acc[i][j], a[i], b[j], (const bf16*)nullptr);
+    }
+    if (kt + 1 < nk) sstore((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  float* dst = p.part + ((long)tile * p.S + s) * (TM * TN);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = i * 16 + (lane >> 4) * 4 + r;
+        const int col = w * 32 + j * 16 + (lane & 15);
+        dst[row * TN + col] = acc[i][j][r];
+      }
+}
+
+// C tile = partials summed in slice order.
+ETC_DEV void reduce_task(const Args& p, int tile) {
+  const int tid = threadIdx.x;
+  const int tm = tile / p.tiles_n, tn = tile % p.tiles_n;
+  const float* src = p.part + (long)tile * p.S * (TM * TN);
+  for (int e4 = tid; e4 < TM * TN / 4; e4 += NT) {
+    const int row = (e4 * 4) / TN, col = (e4 * 4) % TN;
+    const int m = tm * TM + row;
+    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 0; s < p.S; ++s) {
+      const float4 v = *reinterpret_cast<const float4*>(src + (long)s * TM * TN + e4 * 4);
+      sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+    }
+    if (m < p.M) *reinterpret_cast<float4*>(p.C + (long)m * p.N + tn * TN + col) = sum;
+  }
+}
+
+__global__ __launch_bounds__(NT) void splitk_kernel(Args p) {
+  __shared__ Smem sm;
+  const int tid = threadIdx.x;
+  const uint64_t deadline = now_ticks() + p.timeout_ticks;
+  const int nparts = p.tiles * p.S;
+  const int total = (p.mode == ETC_SCHED_STATIC) ? nparts + p.tiles : nparts;
+
+  while (true) {
+    if (tid == 0) {
+      int t = (p.mode == ETC_SCHED_STATIC) ? atomicAdd(p.sched + W_TICKET, 1)
+                                           : atomicAdd(p.sched + W_QHEAD, 1);
+      if (ev_load_relaxed(p.sched + W_ABORT)) t = total;
+      sm.task = t;
+    }
+    __syncthreads();
+    const int t = sm.task;
+    __syncthreads();
+    if (t >= total) break;
+
+    if (t < nparts) {
+      const int tile = t % p.tiles, s = t / p.tiles;
+      partial_task(p, sm, tile, s);
+      wg_publish();
+      if (tid == 0) {
+        const int old = ev_add(p.ev + tile, 1);
+        sm.flag = (p.mode == ETC_SCHED_DYNAMIC && old == p.S - 1) ? 1 : 0;
+      }
+      __syncthreads();
+      if (sm.flag) reduce_task(p, tile);  // last arriver; its acq_rel add saw every partial
+      __syncthreads();
+    } else {
+      const int tile = t - nparts;
+      if (tid == 0) sm.flag = spin_until_geq(p.ev + tile, p.S, p.sched, deadline, 1) ? 1 : 0;
+      __syncthreads();
+      if (sm.flag) reduce_task(p, tile);
+      __syncthreads();
+    }
+  }
+
+  // the last workgroup out clears the counters for the next call
+  wg_publish();
+  if (tid == 0) sm.flag = (atomicAdd(p.sched + W_EXIT, 1) == (int)gridDim.x - 1) ? 1 : 0;
+  __syncthreads();
+  if (sm.flag && !(p.flags & ETC_FLAG_KEEP_COUNTERS)) {
+    for (int i = tid; i < p.tiles; i += NT) ev_store_relaxed(p.ev + i, 0);
+    if (tid < W_NWORDS && tid != W_STATUS && tid != W_AUX) ev_store_relaxed(p.sched + tid, 0);
+  }
+}
+
+struct Layout {
+  size_t sched, ev, part, total;
+  int tiles;
+};
+
+inline Layout layout(int M, int N, int S) {
+  Layout L;
+  L.tiles = cdiv(M, TM) * (N / TN);
+  host::Carve c;
+  L.sched = c.take(W_NWORDS * sizeof(int));
+  L.ev = c.take((size_t)L.tiles * sizeof(int));
+  L.part = c.take((size_t)L.tiles * S * TM * TN * sizeof(float));
+  L.total = c.off;
+  return L;
+}
+
+}  // namespace splitk
+}  // namespace etc
+
+using namespace etc;
+
+int splitk_default_workers(int dev);
+
+static int splitk_occupancy(int dev) {
+  static int occ[host::MAX_DEVICES] = {0};
+  if (occ[dev] == 0) {
+    int v = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, splitk::splitk_kernel, NT, 0) != hipSuccess || v < 1)
+      v = 1;
+    occ[dev] = v;
+  }
+  return occ[dev];
+}
+
+int splitk_default_workers(int dev) { return host::device_cus(dev) * splitk_occupancy(dev); }
+
+static bool splitk_shape_ok(int32_t M, int32_t N, int32_t K, int32_t S) {
+  return M >= 1 && N >= 1 && K >= 1 && S >= 1 && S <= 64 && N % splitk::TN == 0 &&
+         K % (splitk::BK * S) == 0;
+}
+
+ETC_API size_t etc_splitk_workspace_size(int32_t M, int32_t N, int32_t split_k) {
+  if (M < 1 || N < 1 || N % splitk::TN || split_k < 1 || split_k > 64) return 0;
+  return splitk::layout(M, N, split_k).total;
+}
+
+ETC_API etc_status etc_splitk_gemm(int32_t M, int32_t N, int32_t K, int32_t split_k,
+                                   const void* A, const void* B, float* C, void* workspace,
+                                   size_t workspace_bytes, etc_sched_mode mode, uint32_t flags,
+                                   int32_t workers, void* stream) {
+  if (M < 1 || N < 1 || K < 1 || split_k < 1) return ETC_ERR_INVALID_ARG;
+  if (!A || !B || !C) return ETC_ERR_INVALID_ARG;
+  if (mode != ETC_SCHED_STATIC && mode != ETC_SCHED_DYNAMIC) return ETC_ERR_INVALID_ARG;
+  if (!host::aligned16(A) || !host::aligned16(B) || !host::aligned16(C)) return ETC_ERR_INVALID_ARG;
+  if (!splitk_shape_ok(M, N, K, split_k)) return ETC_ERR_UNSUPPORTED;
+  const splitk::Layout L = splitk::layout(M, N, split_k);
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) || workspace_bytes < L.total)
+    return ETC_ERR_WORKSPACE;
+  const int dev = host::current_gfx950_device();
+  if (dev < 0) return ETC_ERR_NO_DEVICE;
+
+  splitk::Args p;
+  p.M = M; p.N = N; p.K = K; p.S = split_k;
+  p.tiles_m = cdiv(M, splitk::TM);
+  p.tiles_n = N / splitk::TN;
+  p.tiles = L.tiles;
+  p.mode = mode;
+  p.flags = flags;
+  p.A = static_cast<const bf16*>(A);
+  p.B = static_cast<const bf16*>(B);
+  p.C = C;
+  char* ws = static_cast<char*>(workspace);
+  p.sched = reinterpret_cast<int*>(ws + L.sched);
+  p.ev = reinterpret_cast<int*>(ws + L.ev);
+  p.part = reinterpret_cast<float*>(ws + L.part);
+  p.timeout_ticks = 500000000ull;  // 5 s at the 100 MHz real-time clock
+
+  const int grid = host::grid_size(workers, host::device_cus(dev), splitk_occupancy(dev));
+  hipLaunchKernelGGL(splitk::splitk_kernel, dim3(grid), dim3(NT), 0, static_cast<hipStream_t>(stream), p);
+  return hipGetLastError() == hipSuccess ? ETC_OK : ETC_ERR_HIP;
+}

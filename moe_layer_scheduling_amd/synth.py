@@ -129,10 +129,11 @@ def make_splitk(M=None, N=None, K=None, sigma=None, seed=None):
 
 
 def as_numpy(t):
-    """Exact float values of a CPU tensor as a float64 array (for the oracle)."""
+    """Exact values of a tensor as a float32 array (bfloat16 and float32 values are all
+    exact in float32; the oracle widens to float64 where it computes)."""
     if t is None:
         return None
-    return t.detach().to("cpu", torch.float32).numpy().astype(np.float64)
+    return t.detach().to("cpu", torch.float32).numpy()
 
 
 def layers_as_numpy(layers):
