@@ -1,0 +1,258 @@
+"""Throughput of the persistent event-tensor MoE kernel on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
+                    [--mode dynamic|static] [--combine atomic|ordered]
+                    [--secondary | --no-secondary] [--no-cpu-baseline]
+
+A step is one call of the library on one batch of synthetic input already resident in
+HBM: for the headline "prefill" workload, T=4096 tokens through two chained MoE layers
+(H=4096, E=64, k=6, F=1408, bfloat16), i.e. every stage of the path -- RMSNorm,
+router, top-k and softmax, counts, scan and permutation, gate/up and down expert tiles
+released by the event counters, and the weighted combine -- in one kernel launch.
+Steps are timed with HIP events recorded on the stream the kernel is launched on.
+
+Prints one JSON line.  value = tokens per second of the step (T / step time).
+roofline: the prefill kernel is MFMA-bound: achieved = algorithmic bfloat16 expert flops
+(T*k*6*H*F per layer, no padded rows) / average launch time, against 2.5 PFLOP/s;
+decode and fine-grained lines are HBM-bound: algorithmic bytes = expert weights the
+run's routing touches + router weights + x and out, against 8 TB/s.
+cpu_baseline: the CPU oracle on a bounded sample of the same workload.
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from moe_layer_scheduling_amd import binding, synth  # noqa: E402
+
+METRIC = "MoE layer tokens/sec + % of roofline (HBM GB/s decode, MFMA TFLOP/s prefill)"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def time_steps(fn, steps, warmup):
+    """Run fn warmup times, then time exactly `steps` calls with one event pair per
+    call on the current stream.  Returns (ms per step from the outer events, mean
+    launch ms from the per-call events, list of per-call ms)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    outer0, outer1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    outer0.record(stream)
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    outer1.record(stream)
+    torch.cuda.synchronize()
+    per = [a.elapsed_time(b) for a, b in ev]
+    return outer0.elapsed_time(outer1) / steps, float(np.mean(per)), per
+
+
+def moe_inputs(cfg, T, call=0):
+    layers = synth.make_layers(cfg)
+    x = synth.make_x(cfg, T, call=call)
+    ld = [{k: v.cuda() for k, v in l.items()} for l in layers]
+    return layers, x, ld
+
+
+def routed_counts(xd, ld, cfg, ws, mode, combine):
+    _, info = binding.moe_layer(xd, ld, cfg.top_k, eps=cfg.eps, mode=mode, combine=combine,
+                                workspace=ws, return_routing=True)
+    torch.cuda.synchronize()
+    return info["expert_counts"].cpu().numpy()
+
+
+def expert_bytes(cfg):
+    es = 2 if cfg.dtype == "bf16" else 4
+    return 3 * cfg.hidden * cfg.ffn * es
+
+
+def bench_moe(cfg, T, steps, warmup, mode, combine, with_cpu=False):
+    log(f"[bench] {cfg.name}: drawing inputs T={T}")
+    layers, x, ld = moe_inputs(cfg, T)
+    xd = x.cuda()
+    dt = synth.torch_dtype(cfg.dtype)
+    ws = binding.MoEWorkspace(T, cfg.hidden, cfg.experts, cfg.top_k, cfg.ffn, cfg.layers, dt,
+                              combine)
+    counts = routed_counts(xd, ld, cfg, ws, mode, combine)
+    out = torch.empty(0)
+
+    def step():
+        nonlocal out
+        out = binding.moe_layer(xd, ld, cfg.top_k, eps=cfg.eps, mode=mode, combine=combine,
+                                workspace=ws)
+
+    log(f"[bench] {cfg.name}: timing {steps} steps")
+    ms, launch_ms, per = time_steps(step, steps, warmup)
+    st = ws.status()
+    if st != 0:
+        raise RuntimeError(f"device status {st}")
+    es = 2 if cfg.dtype == "bf16" else 4
+    touched = int(sum((c > 0).sum() for c in counts))  # expert-layers with work
+    flops_bf16 = cfg.layers * T * cfg.top_k * 6 * cfg.hidden * cfg.ffn
+    flops_router = cfg.layers * 2 * T * cfg.hidden * cfg.experts
+    bytes_alg = (touched * expert_bytes(cfg) + cfg.layers * cfg.experts * cfg.hidden * es +
+                 2 * T * cfg.hidden * es * cfg.layers)
+    res = {
+        "tokens": T, "ms_per_step": ms, "launch_ms": launch_ms,
+        "launch_ms_p10": float(np.percentile(per, 10)), "launch_ms_p90": float(np.percentile(per, 90)),
+        "tokens_per_s": T / (ms / 1e3),
+        "tflops_bf16": flops_bf16 / (launch_ms / 1e3) / 1e12,
+        "gbs_alg": bytes_alg / (launch_ms / 1e3) / 1e9,
+        "flops_bf16": flops_bf16, "flops_router_fp32": flops_router, "bytes_alg": bytes_alg,
+        "experts_touched": touched,
+    }
+    res["mfma_frac"] = res["tflops_bf16"] / PEAK_BF16_TFLOPS
+    res["hbm_frac"] = res["gbs_alg"] / PEAK_HBM_GBS
+    if with_cpu:
+        res["cpu"] = cpu_baseline(cfg, layers, x)
+    del ws, ld, xd
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(cfg, layers, x, budget_s=20.0):
+    """The oracle as it stands, on a bounded sample: the first n tokens through every
+    layer (per-token outputs do not depend on the other tokens), n doubled until the
+    run takes a few seconds, then extrapolated to tokens/s."""
+    from oracle import moe as om
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        threads = os.cpu_count()
+    lnp = synth.layers_as_numpy(layers)
+    xn = synth.as_numpy(x)
+    n, spent = 4, 0.0
+    while True:
+        t0 = time.perf_counter()
+        om.moe_forward(xn[:n], lnp, cfg.top_k, cfg.eps, cfg.dtype)
+        spent = time.perf_counter() - t0
+        if spent > budget_s / 3 or n >= x.shape[0]:
+            break
+        n = min(2 * n, x.shape[0])
+    return {"value": n / spent, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} of {x.shape[0]} tokens through all {cfg.layers} layer(s) "
+                      f"of the {cfg.name} workload, numpy float64, {spent:.1f} s"}
+
+
+def bench_splitk(steps, warmup, mode="static", copies=4):
+    cfg = synth.SPLITK
+    A, B = synth.make_splitk()
+    Ad = A.cuda()
+    Bs = [B.cuda()]
+    for _ in range(copies - 1):  # rotate B so each call reads it from HBM, not the MALL
+        Bs.append(Bs[0].clone())
+    ws = binding.SplitKWorkspace(cfg["M"], cfg["N"], cfg["split_k"])
+    it = [0]
+
+    def step():
+        binding.splitk_gemm(Ad, Bs[it[0] % copies], cfg["split_k"], mode=mode, workspace=ws)
+        it[0] += 1
+
+    ms, launch_ms, per = time_steps(step, steps, warmup)
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    nbytes = M * K * 2 + K * N * 2 + M * N * 4
+    return {"ms_per_step": ms, "launch_ms": launch_ms, "gbs_alg": nbytes / (launch_ms / 1e3) / 1e9,
+            "hbm_frac": nbytes / (launch_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+            "tflops_bf16": 2 * M * N * K / (launch_ms / 1e3) / 1e12, "bytes_alg": nbytes,
+            "mode": mode}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill", choices=sorted(synth.CONFIGS))
+    ap.add_argument("--tokens", type=int, default=0, help="override T (decode: 1/4/16/64)")
+    ap.add_argument("--mode", default="static", choices=["static", "dynamic"])
+    ap.add_argument("--combine", default="atomic", choices=["atomic", "ordered"])
+    ap.add_argument("--secondary", dest="secondary", action="store_true", default=True)
+    ap.add_argument("--no-secondary", dest="secondary", action="store_false")
+    ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false", default=True)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    binding.load_library()
+
+    cfg = synth.CONFIGS[args.workload]
+    T = args.tokens or cfg.tokens[-1]
+    head = bench_moe(cfg, T, args.steps, args.warmup, args.mode, args.combine, with_cpu=args.cpu)
+    mfma_bound = args.workload in ("prefill", "tiny")
+    if mfma_bound:
+        roof = {"bound": "mfma", "achieved": head["tflops_bf16"], "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": head["mfma_frac"], "traffic": None}
+    else:
+        roof = {"bound": "hbm", "achieved": head["gbs_alg"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": head["hbm_frac"], "traffic": None}
+    roof["kernel"] = "etc::moe::moe_kernel<bf16>" if cfg.dtype == "bf16" else "etc::moe::moe_kernel<float>"
+    roof["per_launch"] = {"flops_bf16": head["flops_bf16"], "flops_router_fp32": head["flops_router_fp32"],
+                          "bytes_alg": head["bytes_alg"], "launch_ms": head["launch_ms"]}
+
+    secondary = {}
+    if args.secondary:
+        dec = synth.CONFIGS["decode"]
+        for t in (1, 64):
+            r = bench_moe(dec, t, max(5, args.steps // 2), 2, args.mode, args.combine)
+            secondary[f"decode_T{t}"] = {k: r[k] for k in ("tokens_per_s", "launch_ms", "gbs_alg",
+                                                          "hbm_frac", "experts_touched")}
+        fg = bench_moe(synth.CONFIGS["finegrained"], 256, max(5, args.steps // 2), 2, args.mode,
+                       args.combine)
+        secondary["finegrained_T256"] = {k: fg[k] for k in ("tokens_per_s", "launch_ms", "gbs_alg",
+                                                           "hbm_frac", "experts_touched")}
+        for m in ("static", "dynamic"):  # split-K's dynamic mode is a last-arriver reduction
+            sk = bench_splitk(max(5, args.steps // 2), 2, m)
+            secondary[f"splitk_{m}"] = {k: sk[k] for k in ("launch_ms", "gbs_alg", "hbm_frac")}
+
+    line = {
+        "metric": METRIC,
+        "value": head["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: T={T} H={cfg.hidden} E={cfg.experts} k={cfg.top_k} "
+                               f"F={cfg.ffn}, {cfg.layers} chained layer(s)",
+                   "tokens_per_step": T, "layers": cfg.layers, "mode": args.mode,
+                   "combine": args.combine, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": head.get("cpu"),
+        "secondary": secondary,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

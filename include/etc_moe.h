@@ -126,8 +126,11 @@ typedef struct {
  *   stream       hipStream_t
  * Errors: ETC_ERR_INVALID_ARG (null pointer, size or enum out of range, unaligned
  * pointer -- every tensor pointer must be 16-byte aligned), ETC_ERR_UNSUPPORTED
- * (H % 128, F % 64, E > 256, k > 16, L > 4), ETC_ERR_WORKSPACE, ETC_ERR_HIP,
- * ETC_ERR_NO_DEVICE.  Device-side timeouts are reported by etc_query_device_status.
+ * (H % 128, F % 64, E > 256, k > 16, L > 4; and mode ETC_SCHED_DYNAMIC unless the
+ * process environment has ETC_ENABLE_DYNAMIC_SCHED=1 -- the dynamic scheduler is
+ * disabled by default while a non-terminating run of it on MI355X is investigated),
+ * ETC_ERR_WORKSPACE, ETC_ERR_HIP, ETC_ERR_NO_DEVICE.  Device-side timeouts are
+ * reported by etc_query_device_status.
  */
 etc_status etc_moe_layer(int32_t tokens, int32_t hidden, int32_t experts, int32_t top_k,
                          int32_t ffn, int32_t num_layers, etc_dtype dtype, float eps,

@@ -53,49 +53,52 @@ def library_path():
     return LIB_PATH
 
 
+def open_library(path):
+    """Open and type a build of the C ABI at `path` (no caching)."""
+    if not os.path.exists(path):
+        raise EtcLibraryError(
+            f"{path} is missing: build it with `python -m moe_layer_scheduling_amd.build`")
+    try:
+        lib = ctypes.CDLL(path)
+    except OSError as exc:
+        raise EtcLibraryError(f"cannot load {path}: {exc}") from exc
+    c_i32, c_u32, c_sz, c_p = ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t, ctypes.c_void_p
+    lib.etc_abi_version.restype = c_i32
+    lib.etc_status_string.restype = ctypes.c_char_p
+    lib.etc_status_string.argtypes = [ctypes.c_int]
+    lib.etc_moe_layer.restype = ctypes.c_int
+    lib.etc_moe_layer.argtypes = [c_i32] * 6 + [ctypes.c_int, ctypes.c_float,
+                                                ctypes.POINTER(MoeWeights), c_p, c_p, c_p,
+                                                ctypes.POINTER(MoeRouting), c_p, c_sz, c_i32,
+                                                ctypes.c_int, ctypes.c_int, c_u32, c_i32, c_p]
+    lib.etc_moe_workspace_size.restype = c_sz
+    lib.etc_moe_workspace_size.argtypes = [c_i32] * 6 + [ctypes.c_int, ctypes.c_int]
+    lib.etc_moe_workspace_layout.restype = ctypes.c_int
+    lib.etc_moe_workspace_layout.argtypes = [c_i32] * 6 + [ctypes.c_int, ctypes.c_int, c_i32,
+                                                           ctypes.POINTER(ctypes.c_int64)]
+    lib.etc_splitk_gemm.restype = ctypes.c_int
+    lib.etc_splitk_gemm.argtypes = [c_i32] * 4 + [c_p, c_p, c_p, c_p, c_sz, ctypes.c_int, c_u32,
+                                                  c_i32, c_p]
+    lib.etc_splitk_workspace_size.restype = c_sz
+    lib.etc_splitk_workspace_size.argtypes = [c_i32] * 3
+    lib.etc_workspace_init.restype = ctypes.c_int
+    lib.etc_workspace_init.argtypes = [c_p, c_sz, c_p]
+    lib.etc_query_device_status.restype = ctypes.c_int
+    lib.etc_query_device_status.argtypes = [c_p, c_p]
+    lib.etc_default_workers.restype = c_i32
+    lib.etc_default_workers.argtypes = [c_i32, ctypes.c_int]
+    if lib.etc_abi_version() != ABI_VERSION:
+        raise EtcLibraryError(f"{path} has ABI {lib.etc_abi_version():#x}, expected {ABI_VERSION:#x}")
+    return lib
+
+
 def load_library(path=None):
-    """Load (once) and type the shared library; raise EtcLibraryError if absent."""
+    """Load (once) the in-tree library; raise EtcLibraryError if it is absent."""
     global _lib
     with _lock:
-        if _lib is not None:
-            return _lib
-        path = path or LIB_PATH
-        if not os.path.exists(path):
-            raise EtcLibraryError(
-                f"{path} is missing: build it with `python -m moe_layer_scheduling_amd.build`")
-        try:
-            lib = ctypes.CDLL(path)
-        except OSError as exc:
-            raise EtcLibraryError(f"cannot load {path}: {exc}") from exc
-        c_i32, c_u32, c_sz, c_p = ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t, ctypes.c_void_p
-        lib.etc_abi_version.restype = c_i32
-        lib.etc_status_string.restype = ctypes.c_char_p
-        lib.etc_status_string.argtypes = [ctypes.c_int]
-        lib.etc_moe_layer.restype = ctypes.c_int
-        lib.etc_moe_layer.argtypes = [c_i32] * 6 + [ctypes.c_int, ctypes.c_float,
-                                                    ctypes.POINTER(MoeWeights), c_p, c_p, c_p,
-                                                    ctypes.POINTER(MoeRouting), c_p, c_sz, c_i32,
-                                                    ctypes.c_int, ctypes.c_int, c_u32, c_i32, c_p]
-        lib.etc_moe_workspace_size.restype = c_sz
-        lib.etc_moe_workspace_size.argtypes = [c_i32] * 6 + [ctypes.c_int, ctypes.c_int]
-        lib.etc_moe_workspace_layout.restype = ctypes.c_int
-        lib.etc_moe_workspace_layout.argtypes = [c_i32] * 6 + [ctypes.c_int, ctypes.c_int, c_i32,
-                                                               ctypes.POINTER(ctypes.c_int64)]
-        lib.etc_splitk_gemm.restype = ctypes.c_int
-        lib.etc_splitk_gemm.argtypes = [c_i32] * 4 + [c_p, c_p, c_p, c_p, c_sz, ctypes.c_int, c_u32,
-                                                      c_i32, c_p]
-        lib.etc_splitk_workspace_size.restype = c_sz
-        lib.etc_splitk_workspace_size.argtypes = [c_i32] * 3
-        lib.etc_workspace_init.restype = ctypes.c_int
-        lib.etc_workspace_init.argtypes = [c_p, c_sz, c_p]
-        lib.etc_query_device_status.restype = ctypes.c_int
-        lib.etc_query_device_status.argtypes = [c_p, c_p]
-        lib.etc_default_workers.restype = c_i32
-        lib.etc_default_workers.argtypes = [c_i32, ctypes.c_int]
-        if lib.etc_abi_version() != ABI_VERSION:
-            raise EtcLibraryError(f"{path} has ABI {lib.etc_abi_version():#x}, expected {ABI_VERSION:#x}")
-        _lib = lib
-        return lib
+        if _lib is None:
+            _lib = open_library(path or LIB_PATH)
+        return _lib
 
 
 def _check(status, where):
@@ -174,7 +177,7 @@ class SplitKWorkspace(Workspace):
         super().__init__(n, device)
 
 
-def moe_layer(x, layers, top_k, *, eps=1e-6, mode="dynamic", combine="atomic", workspace=None,
+def moe_layer(x, layers, top_k, *, eps=1e-6, mode="static", combine="atomic", workspace=None,
               max_tokens=None, return_routing=False, return_layer_outputs=False, workers=0,
               flags=0):
     """Run len(layers) chained MoE layers on x [T][H] (float32 or bfloat16 device tensor).

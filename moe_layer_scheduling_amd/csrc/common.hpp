@@ -92,6 +92,12 @@ ETC_DEV void ev_store_relaxed(int* p, int v) {
 ETC_DEV long long q_load(const long long* p) {
   return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
 }
+ETC_DEV long long q_load_relaxed(const long long* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+ETC_DEV void q_store(long long* p, long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
 ETC_DEV void q_store_relaxed(long long* p, long long v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -122,22 +128,36 @@ enum SchedWord {
   W_NWORDS = 16
 };
 
+// Waits poll with relaxed loads (no cache invalidation per poll: an agent-scope acquire
+// invalidates this CU's L1 and the XCD's L2 lines, which would keep evicting the operands
+// of the tiles running beside the waiter) and, once the condition holds, take one
+// acquire load of the same location, which synchronises with the producers.  Every wait
+// is bounded twice: by the 100 MHz real-time clock and by an iteration count, so a wait
+// ends even if the clock did not advance.
+constexpr int SPIN_MAX_ITERS = 1 << 24;
+
+ETC_DEV bool wait_give_up(int* sched, uint64_t deadline, int it, int where) {
+  if ((it & 15) != 0) return false;
+  if (ev_load_relaxed(sched + W_ABORT)) return true;
+  if (now_ticks() > deadline || it >= SPIN_MAX_ITERS) {
+    ev_store_relaxed(sched + W_STATUS, 5 /* ETC_ERR_TIMEOUT */);
+    ev_store_relaxed(sched + W_AUX, where);
+    ev_store(sched + W_ABORT, 1);
+    return true;
+  }
+  return false;
+}
+
 // Spin (one lane) until *ctr >= target.  Returns false if the call was aborted, by
 // this wait timing out or by another workgroup.
 ETC_DEV bool spin_until_geq(const int* ctr, int target, int* sched, uint64_t deadline,
                             int where) {
-  int it = 0;
-  while (true) {
-    if (ev_load(ctr) >= target) return true;
-    if ((++it & 15) == 0) {
-      if (ev_load_relaxed(sched + W_ABORT)) return false;
-      if (now_ticks() > deadline) {
-        ev_store_relaxed(sched + W_STATUS, 5 /* ETC_ERR_TIMEOUT */);
-        ev_store_relaxed(sched + W_AUX, where);
-        ev_store(sched + W_ABORT, 1);
-        return false;
-      }
+  for (int it = 1;; ++it) {
+    if (ev_load_relaxed(ctr) >= target) {
+      (void)ev_load(ctr);  // acquire: everything released before the counter reached it
+      return true;
     }
+    if (wait_give_up(sched, deadline, it, where)) return false;
     __builtin_amdgcn_s_sleep(2);
   }
 }

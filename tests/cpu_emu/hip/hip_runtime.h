@@ -1,0 +1,143 @@
+// CPU stand-in for <hip/hip_runtime.h>, used only to compile the library's HIP sources
+// unchanged as host C++ for the CPU execution harness in tests/ (never for the GPU).
+//
+// Model: a kernel launch runs every workgroup as an OS thread; the lanes of a
+// workgroup are cooperative fibers on that thread.  __syncthreads is a barrier over
+// the workgroup's fibers; shuffles and MFMA are wave-collective (the 64 lanes of a
+// wave deposit their operands, meet, compute, meet again); global-memory atomics are
+// host atomics; s_sleep yields.  The MFMA lane layouts are the ones the kernels assume
+// (and that an on-GPU probe confirmed): lane l holds row / column l % 16 and k values
+// 8*(l/16)..+7 (bf16 16x16x32) or k = l/16 (f32 16x16x4); result element r of lane l is
+// row 4*(l/16) + r, column l % 16.
+#pragma once
+
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <functional>
+
+#define __global__
+#define __device__
+#define __host__
+#define __forceinline__ inline
+#define __launch_bounds__(...)
+// __shared__ objects are per-workgroup: one OS thread runs each workgroup.
+#define __shared__ static thread_local
+
+typedef int hipError_t;
+enum { hipSuccess = 0, hipErrorInvalidValue = 1 };
+typedef struct ihipStream_t* hipStream_t;
+enum hipMemcpyKind { hipMemcpyHostToDevice = 1, hipMemcpyDeviceToHost = 2, hipMemcpyDeviceToDevice = 3 };
+enum hipDeviceAttribute_t { hipDeviceAttributeMultiprocessorCount = 1 };
+
+struct hipDeviceProp_t {
+  char gcnArchName[256];
+};
+
+struct dim3 {
+  unsigned x, y, z;
+  dim3(unsigned a = 1, unsigned b = 1, unsigned c = 1) : x(a), y(b), z(c) {}
+};
+struct uint2 { unsigned x, y; };
+struct uint4 { unsigned x, y, z, w; };
+struct float4 { float x, y, z, w; };
+inline uint2 make_uint2(unsigned a, unsigned b) { return uint2{a, b}; }
+inline uint4 make_uint4(unsigned a, unsigned b, unsigned c, unsigned d) { return uint4{a, b, c, d}; }
+inline float4 make_float4(float a, float b, float c, float d) { return float4{a, b, c, d}; }
+
+typedef __bf16 emu_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float emu_f32x4 __attribute__((ext_vector_type(4)));
+
+struct EmuDim { unsigned x, y, z; };
+EmuDim emu_thread_idx();
+EmuDim emu_block_idx();
+EmuDim emu_grid_dim();
+#define threadIdx emu_thread_idx()
+#define blockIdx emu_block_idx()
+#define gridDim emu_grid_dim()
+#define blockDim (EmuDim{256, 1, 1})
+
+void emu_syncthreads();
+void emu_wave_barrier();
+void emu_yield();
+void* emu_wave_scratch(int bytes_per_lane);  // this wave's exchange buffer (64 lanes)
+int emu_lane();
+uint64_t emu_realtime();
+#define __syncthreads() emu_syncthreads()
+
+template <typename T>
+inline T emu_exchange(T v, int src) {
+  unsigned char* buf = static_cast<unsigned char*>(emu_wave_scratch(sizeof(T)));
+  const int lane = emu_lane();
+  memcpy(buf + lane * sizeof(T), &v, sizeof(T));
+  emu_wave_barrier();
+  T out;
+  memcpy(&out, buf + src * sizeof(T), sizeof(T));
+  emu_wave_barrier();
+  return out;
+}
+template <typename T>
+inline T __shfl_xor(T v, int mask, int width = 64) {
+  const int lane = emu_lane();
+  const int base = lane & ~(width - 1);
+  return emu_exchange(v, base + ((lane - base) ^ mask) % width);
+}
+template <typename T>
+inline T __shfl_up(T v, unsigned delta, int width = 64) {
+  const int lane = emu_lane();
+  const int base = lane & ~(width - 1);
+  const int src = lane - (int)delta;
+  return emu_exchange(v, src < base ? lane : src);
+}
+
+template <typename T>
+inline T min(T a, T b) { return b < a ? b : a; }
+template <typename T>
+inline T max(T a, T b) { return a < b ? b : a; }
+
+inline float __uint_as_float(unsigned u) { float f; memcpy(&f, &u, 4); return f; }
+inline unsigned __float_as_uint(float f) { unsigned u; memcpy(&u, &f, 4); return u; }
+
+inline int atomicAdd(int* p, int v) { return __atomic_fetch_add(p, v, __ATOMIC_SEQ_CST); }
+inline float atomicAdd(float* p, float v) {
+  unsigned* u = reinterpret_cast<unsigned*>(p);
+  unsigned old = __atomic_load_n(u, __ATOMIC_RELAXED);
+  while (true) {
+    const unsigned nw = __float_as_uint(__uint_as_float(old) + v);
+    if (__atomic_compare_exchange_n(u, &old, nw, false, __ATOMIC_SEQ_CST, __ATOMIC_RELAXED))
+      return __uint_as_float(old);
+  }
+}
+
+#define __HIP_MEMORY_SCOPE_AGENT 3
+#define __hip_atomic_load(p, order, scope) __atomic_load_n((p), (order))
+#define __hip_atomic_store(p, v, order, scope) __atomic_store_n((p), (v), (order))
+#define __hip_atomic_fetch_add(p, v, order, scope) __atomic_fetch_add((p), (v), (order))
+#define __builtin_amdgcn_fence(order, scope) __atomic_thread_fence(order)
+#define __builtin_amdgcn_s_waitcnt(x) ((void)0)
+#define __builtin_amdgcn_s_sleep(x) emu_yield()
+#define __builtin_amdgcn_s_memrealtime() emu_realtime()
+
+emu_f32x4 emu_mfma_bf16(emu_bf16x8 a, emu_bf16x8 b, emu_f32x4 c);
+emu_f32x4 emu_mfma_f32(float a, float b, emu_f32x4 c);
+#define __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, x, y, z) emu_mfma_bf16((a), (b), (c))
+#define __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, x, y, z) emu_mfma_f32((a), (b), (c))
+
+// ---- host API
+hipError_t hipGetDevice(int* d);
+hipError_t hipGetDeviceProperties(hipDeviceProp_t* p, int d);
+hipError_t hipDeviceGetAttribute(int* v, hipDeviceAttribute_t a, int d);
+hipError_t hipMemsetAsync(void* p, int v, size_t n, hipStream_t s);
+hipError_t hipMemcpyAsync(void* d, const void* s, size_t n, hipMemcpyKind k, hipStream_t st);
+hipError_t hipStreamSynchronize(hipStream_t s);
+hipError_t hipGetLastError();
+template <typename F>
+hipError_t hipOccupancyMaxActiveBlocksPerMultiprocessor(int* v, F, int, size_t) {
+  *v = 1;
+  return hipSuccess;
+}
+void emu_launch(unsigned grid, unsigned block, std::function<void()> fn);
+#define hipLaunchKernelGGL(kernel, grid, block, shm, stream, ...) \
+  emu_launch((grid).x, (block).x, [=]() { kernel(__VA_ARGS__); })

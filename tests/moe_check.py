@@ -8,7 +8,9 @@ Rules, per layer:
     later layers, whose input already differs by bfloat16 rounding flips of the previous
     layer's output (one flip of a 2**-8-relative step moves a logit by about
     |w| * |x| * 2**-8 ~ 1e-4 here);
-  * gates: within 1e-5 absolute of the oracle's for the same expert;
+  * gates: within 1e-5 absolute of the oracle's for the same expert in the first layer;
+    in later layers within 0.25 * TIE_LATER = 5e-4 (a softmax moves by at most a quarter
+    of the logit change, and the logits there move by up to TIE_LATER);
   * counts and sorted_assign: bit-exact to the oracle's while every token's expert set
     agrees with the oracle; otherwise (and always) they must be the stable grouping of
     the GPU's own topk_idx;
@@ -24,6 +26,7 @@ from oracle import moe as om
 TIE_FIRST = 1e-5
 TIE_LATER = 2e-3
 GATE_TOL = 1e-5
+GATE_TOL_LATER = 0.25 * TIE_LATER
 OUT_TOL = {"bf16": 2e-2, "f32": 1e-4}
 
 
@@ -80,8 +83,9 @@ def compare(x, layers, k, eps, act, gpu, tokens=None):
                 for j in range(k):
                     assert abs(lg[gs[j]] - lg[os_[j]]) < tie, f"layer {l} token {t}: slot order {gs} vs {os_}"
             og = dict(zip(os_, r.gates[i]))
+            gtol = GATE_TOL if l == 0 else GATE_TOL_LATER
             for j, e in enumerate(gs):
-                assert abs(gw[i][j] - og[e]) <= GATE_TOL, f"layer {l} token {t}: gate {gw[i][j]} vs {og[e]}"
+                assert abs(gw[i][j] - og[e]) <= gtol, f"layer {l} token {t}: gate {gw[i][j]} vs {og[e]}"
         gout = gpu["outs"][l][check].astype(np.float64)
         ref_max = float(np.max(np.abs(out_ref)))
         err = float(np.max(np.abs(gout - out_ref)))
@@ -104,3 +108,42 @@ def compare(x, layers, k, eps, act, gpu, tokens=None):
             assert bad.size == 0, f"layer 0: tokens {bad[:10]} routed differently with a clear gap"
         h_in = out_ref
     return stats
+
+
+def check_event_tensor(read_i32, layout, T, H, F, k, E, gpu, layers):
+    """Final state of every counter of the event tensor (call made with the counters
+    kept) against the scheduler model, given the GPU's own routing and down split.
+
+    read_i32(byte_offset, count) -> int array from the workspace; layout(l) -> the
+    etc_moe_workspace_layout words of layer l."""
+    from oracle import sched_model as sm
+
+    for l in range(layers):
+        lay = layout(l)
+        max_rt, n1, n_rt_cap, BT, BM, BN1, BN2 = lay[6:13]
+        RT, ngu, nd, nf, nS, gpc = (int(v) for v in read_i32(lay[5], 8)[:6])
+        counts = gpu["counts"][l]
+        sa = gpu["sa"][l]
+        off = np.concatenate([[0], np.cumsum(counts)])
+        tors = [list(sa[off[e]:off[e + 1]] // k) for e in range(E)]
+        plan = sm.Plan(BT=BT, BM=BM, BN1=BN1, BN2=BN2, GPC=gpc)
+        final = sm.expected_final_counters(sm.build_graph(T, H, F, k, [counts], [tors], plan))
+        n_rt, n1m, n2, nSm = sm.layer_shape(T, H, F, plan)
+        assert (n1m, nSm) == (n1, nS) and RT == sum(-(-int(c) // BM) for c in counts)
+        assert ngu == RT * n1 and nd == RT * n2 * nS and nf == n_rt
+        assert int(read_i32(lay[0], 1)[0]) == final[("route", 0)]
+        assert int(read_i32(lay[1], 1)[0]) == 1
+        ev_gu = np.asarray(read_i32(lay[2], max_rt * n1)).reshape(max_rt, n1)
+        rt = 0
+        for e in range(E):
+            for m in range(-(-int(counts[e]) // BM)):
+                for s in range(nS):
+                    assert ev_gu[rt, s] == final[("gu", 0, e, m, s)], (l, e, m, s)
+                rt += 1
+        assert not ev_gu[rt:].any() and not ev_gu[:, nS:].any()
+        comb = np.asarray(read_i32(lay[3], n_rt_cap))
+        done = np.asarray(read_i32(lay[4], n_rt_cap))
+        for tau in range(n_rt):
+            assert comb[tau] == final[("comb", 0, tau)], (l, tau)
+            assert done[tau] == 1
+        assert not comb[n_rt:].any() and not done[n_rt:].any()

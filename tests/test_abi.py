@@ -118,6 +118,13 @@ def test_moe_argument_errors_before_any_hip_call(lib):
     assert _call_moe(lib, wsb=1024) == WS
 
 
+def test_dynamic_moe_refused_by_default(lib, monkeypatch):
+    """The dynamic MoE scheduler is off unless ETC_ENABLE_DYNAMIC_SCHED=1 (host check,
+    before any HIP call)."""
+    monkeypatch.delenv("ETC_ENABLE_DYNAMIC_SCHED", raising=False)
+    assert _call_moe(lib, mode=1) == 2
+
+
 def test_splitk_argument_errors_before_any_hip_call(lib):
     f = lib.etc_splitk_gemm
     ok = dict(M=64, N=4096, K=14336, S=8, A=1 << 20, B=2 << 20, C=3 << 20, ws=4 << 20, wsb=1 << 30)

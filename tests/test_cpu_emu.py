@@ -1,0 +1,102 @@
+"""The library's own kernels executed on the CPU (tests/cpu_emu: the HIP sources compiled
+unchanged as host C++ against a CPU stand-in runtime: workgroups are threads, lanes are
+fibers, MFMA and shuffles are wave-collective).  This covers both schedulers -- the
+dynamic one included, which is disabled on the GPU -- and checks the results against the
+oracle and the event tensor against the scheduler model.  No GPU is involved."""
+
+import ctypes
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from moe_layer_scheduling_amd import binding, synth
+from oracle import splitk as osk
+from tests import moe_check
+from tests.cpu_emu import build_emu, driver
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+MID = synth.MoEConfig("mid", (300,), 512, 16, 6, 384, layers=2, zipf_s=0.5)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    path = os.path.join(HERE, "cpu_emu", "libetc_moe_emu.so")
+    build_emu.build(path)  # always rebuild: the sources may have changed
+    os.environ.setdefault("ETC_EMU_CUS", "4")
+    os.environ.setdefault("ETC_EMU_STACK_KB", "256")
+    return binding.open_library(path)
+
+
+@pytest.fixture(autouse=True)
+def _dynamic_on(monkeypatch):
+    monkeypatch.setenv("ETC_ENABLE_DYNAMIC_SCHED", "1")
+
+
+def _check(cfg, x, layers, g):
+    assert g["status"] == 0
+    return moe_check.compare(synth.as_numpy(x), synth.layers_as_numpy(layers), cfg.top_k, cfg.eps,
+                             cfg.dtype, g)
+
+
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
+@pytest.mark.parametrize("combine", ["atomic", "ordered"])
+def test_tiny(lib, mode, combine):
+    cfg = synth.CONFIGS["tiny"]
+    layers, x = synth.make_layers(cfg), synth.make_x(cfg, 16)
+    _check(cfg, x, layers, driver.moe(lib, cfg, x, layers, mode=mode, combine=combine))
+
+
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
+def test_mid_ragged_one_layer(lib, mode):
+    cfg = MID.with_(layers=1)
+    layers, x = synth.make_layers(cfg), synth.make_x(cfg, 33)
+    _check(cfg, x, layers, driver.moe(lib, cfg, x, layers, mode=mode, max_tokens=300))
+
+
+def test_mid_two_layers_dynamic(lib):
+    cfg = MID
+    layers, x = synth.make_layers(cfg), synth.make_x(cfg, 300)
+    _check(cfg, x, layers, driver.moe(lib, cfg, x, layers, mode="dynamic"))
+
+
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
+def test_single_worker(lib, mode):
+    cfg = synth.CONFIGS["tiny"]
+    layers, x = synth.make_layers(cfg), synth.make_x(cfg, 16, call=2)
+    _check(cfg, x, layers, driver.moe(lib, cfg, x, layers, mode=mode, workers=1))
+
+
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
+def test_event_tensor_final_state(lib, mode):
+    cfg = MID.with_(layers=1)
+    T = 64
+    layers, x = synth.make_layers(cfg), synth.make_x(cfg, T, call=5)
+    g = driver.moe(lib, cfg, x, layers, mode=mode, flags=binding.FLAG_KEEP_COUNTERS)
+    _check(cfg, x, layers, g)
+
+    def layout(l):
+        out = (ctypes.c_int64 * binding.LAYOUT_WORDS)()
+        assert lib.etc_moe_workspace_layout(T, cfg.hidden, cfg.experts, cfg.top_k, cfg.ffn, 1,
+                                            1, 0, l, out) == 0
+        return list(out)
+
+    def read(off, n):
+        return np.array((ctypes.c_int32 * n).from_address(g["wptr"] + off))
+
+    moe_check.check_event_tensor(read, layout, T, cfg.hidden, cfg.ffn, cfg.top_k, cfg.experts, g, 1)
+
+
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
+def test_splitk(lib, mode):
+    M, N, K, S = 37, 256, 1024, 4
+    A, B = synth.make_splitk(M=M, N=N, K=K, seed=2)
+    n = lib.etc_splitk_workspace_size(M, N, S)
+    ws = torch.zeros(n + 256, dtype=torch.uint8)
+    wptr = ws.data_ptr() + (-ws.data_ptr()) % 256
+    C = torch.zeros(M, N, dtype=torch.float32)
+    assert lib.etc_splitk_gemm(M, N, K, S, A.data_ptr(), B.data_ptr(), C.data_ptr(), wptr, n,
+                               binding.MODES[mode], 0, 0, None) == 0
+    ref = osk.splitk_gemm(synth.as_numpy(A), synth.as_numpy(B), S)
+    assert np.max(np.abs(C.numpy() - ref)) <= 1e-3 * np.max(np.abs(ref))
