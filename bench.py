@@ -85,7 +85,7 @@ def expert_bytes(cfg):
     return 3 * cfg.hidden * cfg.ffn * es
 
 
-def bench_moe(cfg, T, steps, warmup, mode, combine, with_cpu=False):
+def bench_moe(cfg, T, steps, warmup, mode, combine, with_cpu=False, trace_out=None):
     log(f"[bench] {cfg.name}: drawing inputs T={T}")
     layers, x, ld = moe_inputs(cfg, T)
     xd = x.cuda()
@@ -105,6 +105,17 @@ def bench_moe(cfg, T, steps, warmup, mode, combine, with_cpu=False):
     st = ws.status()
     if st != 0:
         raise RuntimeError(f"device status {st}")
+    trace_summary = None
+    if trace_out:  # one extra call, outside the timed region, with per-task records
+        from moe_layer_scheduling_amd import trace
+
+        binding.moe_layer(xd, ld, cfg.top_k, eps=cfg.eps, mode=mode, combine=combine, workspace=ws,
+                          flags=binding.FLAG_TRACE)
+        rec = ws.read_trace()
+        trace_summary = trace.summarize(rec)
+        trace.chrome_trace(rec, trace_out)
+        with open(trace_out + ".summary.json", "w") as f:
+            json.dump(trace_summary, f, indent=1)
     es = 2 if cfg.dtype == "bf16" else 4
     touched = int(sum((c > 0).sum() for c in counts))  # expert-layers with work
     flops_bf16 = cfg.layers * T * cfg.top_k * 6 * cfg.hidden * cfg.ffn
@@ -120,6 +131,8 @@ def bench_moe(cfg, T, steps, warmup, mode, combine, with_cpu=False):
         "flops_bf16": flops_bf16, "flops_router_fp32": flops_router, "bytes_alg": bytes_alg,
         "experts_touched": touched,
     }
+    if trace_summary:
+        res["trace"] = trace_summary
     res["mfma_frac"] = res["tflops_bf16"] / PEAK_BF16_TFLOPS
     res["hbm_frac"] = res["gbs_alg"] / PEAK_HBM_GBS
     if with_cpu:
@@ -190,6 +203,8 @@ def main():
     ap.add_argument("--secondary", dest="secondary", action="store_true", default=True)
     ap.add_argument("--no-secondary", dest="secondary", action="store_false")
     ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false", default=True)
+    ap.add_argument("--trace-out", default=None,
+                    help="also run one traced call and write a Chrome trace here")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -203,7 +218,8 @@ def main():
 
     cfg = synth.CONFIGS[args.workload]
     T = args.tokens or cfg.tokens[-1]
-    head = bench_moe(cfg, T, args.steps, args.warmup, args.mode, args.combine, with_cpu=args.cpu)
+    head = bench_moe(cfg, T, args.steps, args.warmup, args.mode, args.combine, with_cpu=args.cpu,
+                     trace_out=args.trace_out)
     mfma_bound = args.workload in ("prefill", "tiny")
     if mfma_bound:
         roof = {"bound": "mfma", "achieved": head["tflops_bf16"], "peak": PEAK_BF16_TFLOPS,

@@ -66,6 +66,15 @@ typedef enum { ETC_COMBINE_ATOMIC = 0, ETC_COMBINE_ORDERED = 1 } etc_combine;
 #define ETC_FLAG_KEEP_COUNTERS 0x1u /* do not clear the event counters on exit, so the
                                        caller can read them (etc_moe_workspace_layout);
                                        call etc_workspace_init before the next call */
+#define ETC_FLAG_TRACE 0x2u /* etc_moe_layer: every task appends one 32-byte record to the
+                               trace region of the workspace (etc_moe_workspace_layout
+                               words 13-14): uint64 task word (kind in bits 0-3: 1 routing,
+                               2 scan, 3 gate/up, 4 down, 5 finalize; layer bits 4-7;
+                               then 14-bit fields a, b, c, d from bit 8 on), uint64 start
+                               of the claim (100 MHz device clock), uint32 workgroup,
+                               uint32 ticks spent claiming and waiting, uint32 ticks
+                               running, uint32 zero.  The number of records is int32 word
+                               10 of the workspace after the call. */
 
 /* Weights of one MoE layer (all device pointers).  dtype is the call's dtype except
  * gamma and router_bias, which are always float32.  Layouts follow nn.Linear
@@ -152,11 +161,11 @@ size_t etc_moe_workspace_size(int32_t max_tokens, int32_t hidden, int32_t expert
  *   [3] ev_comb ([n_rt] int32)   [4] ev_done ([n_rt] int32)   [5] plan words (int32)
  *   [6] max_rt   [7] n1   [8] n_rt(max_tokens)   [9] rows per routing tile
  *   [10] rows per expert tile   [11] ffn columns per gate/up tile
- *   [12] hidden columns per down tile.
+ *   [12] hidden columns per down tile   [13] trace region   [14] trace records it holds.
  * The plan words are: [0] row tiles RT, [1] gate/up tasks, [2] down tasks,
  * [3] finalize tasks, [4] ffn chunks of the down projection nS, [5] gate/up tiles per
  * chunk, [6] first static ticket of the next layer. */
-#define ETC_LAYOUT_WORDS 13
+#define ETC_LAYOUT_WORDS 15
 etc_status etc_moe_workspace_layout(int32_t max_tokens, int32_t hidden, int32_t experts,
                                     int32_t top_k, int32_t ffn, int32_t num_layers,
                                     etc_dtype dtype, etc_combine combine, int32_t layer,

@@ -21,7 +21,9 @@ DTYPES = {torch.float32: 0, torch.bfloat16: 1}
 MODES = {"static": 0, "dynamic": 1}
 COMBINES = {"atomic": 0, "ordered": 1}
 FLAG_KEEP_COUNTERS = 0x1
-LAYOUT_WORDS = 13
+FLAG_TRACE = 0x2
+LAYOUT_WORDS = 15
+W_TRACE_LAST = 10  # control word holding the last traced call's record count
 
 
 class EtcError(RuntimeError):
@@ -166,6 +168,15 @@ class MoEWorkspace(Workspace):
         _check(lib.etc_moe_workspace_layout(*self.shape, DTYPES[self.dtype], COMBINES[self.combine],
                                             layer, out), "etc_moe_workspace_layout")
         return list(out)
+
+    def read_trace(self):
+        """Records of the last call made with FLAG_TRACE, as a (n, 4) uint64 host array
+        (decode with moe_layer_scheduling_amd.trace)."""
+        torch.cuda.synchronize()
+        lay = self.layout(0)
+        n = int(self.view(4 * W_TRACE_LAST, 1, torch.int32).item())
+        n = min(n, lay[14])
+        return self.view(lay[13], 4 * n, torch.int64).cpu().numpy().view("u8").reshape(n, 4)
 
 
 class SplitKWorkspace(Workspace):

@@ -125,6 +125,8 @@ enum SchedWord {
   W_ABORT = 6,    // set when a wait times out: every workgroup leaves
   W_STATUS = 7,   // 0 ok, else an etc_status; survives the end-of-call reset
   W_AUX = 8,      // debug: where the abort came from
+  W_TRACE = 9,    // trace records written so far in this call
+  W_TRACE_LAST = 10,  // trace records of the last traced call (survives the reset)
   W_NWORDS = 16
 };
 

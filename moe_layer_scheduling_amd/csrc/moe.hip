@@ -113,6 +113,8 @@ struct Args {
   float* ybuf;     // [T*k][H] ordered-combine rows
   long long* queue;
   int* sched;
+  unsigned long long* trace;  // ETC_FLAG_TRACE records, 4 words each
+  int trace_cap;
   LayerArgs layer[MAXL];
 };
 
@@ -694,14 +696,92 @@ ETC_DEV void after_scan(const Args& p, int layer, Smem& sm) {
   }
 }
 
+// One task of either scheduler: its body, then its signals (and, in dynamic mode, the
+// tasks its signal releases).  Every thread of the workgroup calls this.
+template <typename TE>
+ETC_DEV void run_task(const Args& p, const LayerArgs& L, const Task& t, Smem& sm) {
+  const int tid = threadIdx.x;
+  if (t.kind == K_R) {
+    route_task<TE>(p, L, t.a, sm);
+    wg_publish();
+    if (tid == 0) {
+      const int old = ev_add(L.ev_route, 1);
+      sm.flag = (p.mode == ETC_SCHED_DYNAMIC && old + 1 == p.n_rt) ? 1 : 0;
+    }
+    __syncthreads();
+    if (sm.flag) {  // last routing tile of the layer: S runs here (dynamic mode)
+      scan_task(p, L, t.layer, sm);
+      after_scan(p, t.layer, sm);
+    }
+  } else if (t.kind == K_S) {
+    scan_task(p, L, t.layer, sm);
+    after_scan(p, t.layer, sm);
+  } else if (t.kind == K_GU) {
+    gateup_task<TE>(p, L, t.a, t.b, t.c, sm);
+    wg_publish();
+    const int gpc = L.plan[PL_GPC];
+    const int s = t.c / gpc;
+    if (tid == 0) {
+      const int rt = L.rt_base[t.a] + t.b;
+      const int need = min(gpc, p.n1 - s * gpc);
+      const int old = ev_add(L.ev_gu + rt * p.n1 + s, 1);
+      sm.flag = (p.mode == ETC_SCHED_DYNAMIC && old + 1 == need) ? 1 : 0;
+    }
+    __syncthreads();
+    if (sm.flag) {
+      const int layer = t.layer, e = t.a, m = t.b;
+      push_many(p, sm, p.n2, [&](int i) {
+        Task d;
+        d.kind = K_D; d.layer = layer; d.a = e; d.b = m; d.c = i; d.d = s;
+        return d;
+      });
+    }
+  } else if (t.kind == K_D) {
+    down_task<TE>(p, L, t.a, t.b, t.c, t.d, L.plan[PL_GPC], sm);
+    wg_publish();
+    // one signal per run of rows in the same routing tile (rows are token-sorted)
+    const int valid = min(BM, L.counts[t.a] - t.b * BM);
+    if (tid < valid) {
+      const int tau = sm.u.t.row_tok[tid] / BT;
+      if (tid == 0 || sm.u.t.row_tok[tid - 1] / BT != tau) {
+        int len = 1;
+        while (tid + len < valid && sm.u.t.row_tok[tid + len] / BT == tau) ++len;
+        const int old = ev_add(L.ev_comb + tau, len);
+        const int target = tile_rows(p, tau) * p.K * p.n2 * L.plan[PL_NS];
+        if (p.mode == ETC_SCHED_DYNAMIC && old + len == target) {
+          Task f;
+          f.kind = K_F; f.layer = t.layer; f.a = tau; f.b = f.c = f.d = 0;
+          push_one(p, f);
+        }
+      }
+    }
+    __syncthreads();
+  } else if (t.kind == K_F) {
+    finalize_task<TE>(p, L, t.a);
+    wg_publish();
+    if (tid == 0) {
+      ev_store(L.ev_done + t.a, 1);
+      if (p.mode == ETC_SCHED_DYNAMIC && t.layer + 1 < p.L) {
+        Task r;
+        r.kind = K_R; r.layer = t.layer + 1; r.a = t.a; r.b = r.c = r.d = 0;
+        push_one(p, r);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <typename TE>
 __global__ __launch_bounds__(NT) void moe_kernel(Args p) {
   __shared__ Smem sm;
   const int tid = threadIdx.x;
   const uint64_t deadline = now_ticks() + p.timeout_ticks;
 
+  const bool tracing = (p.flags & ETC_FLAG_TRACE) != 0;
+  uint64_t t_claim = 0, t_run = 0;
   while (true) {
     if (tid == 0) {
+      if (tracing) t_claim = now_ticks();
       Task t;
       t.kind = K_NONE; t.layer = 0; t.a = t.b = t.c = t.d = 0;
       const bool ok = (p.mode == ETC_SCHED_STATIC) ? claim_static(p, t, deadline)
@@ -710,80 +790,24 @@ __global__ __launch_bounds__(NT) void moe_kernel(Args p) {
       if (ok && t.kind != K_NONE && p.mode == ETC_SCHED_STATIC && !wait_deps(p, t, deadline))
         t.kind = K_NONE;
       sm.task = t;
+      if (tracing) t_run = now_ticks();
     }
     __syncthreads();
     const Task t = sm.task;
     __syncthreads();
     if (t.kind == K_NONE) break;
     const LayerArgs& L = p.layer[t.layer];
-
-    if (t.kind == K_R) {
-      route_task<TE>(p, L, t.a, sm);
-      wg_publish();
-      if (tid == 0) {
-        const int old = ev_add(L.ev_route, 1);
-        sm.flag = (p.mode == ETC_SCHED_DYNAMIC && old + 1 == p.n_rt) ? 1 : 0;
+    run_task<TE>(p, L, t, sm);
+    if (tracing && tid == 0) {
+      const uint64_t t_end = now_ticks();
+      const int i = atomicAdd(p.sched + W_TRACE, 1);
+      if (i < p.trace_cap) {
+        unsigned long long* r = p.trace + 4 * (size_t)i;
+        r[0] = (unsigned long long)enc(t);
+        r[1] = t_claim;
+        r[2] = (unsigned long long)blockIdx.x | ((unsigned long long)(uint32_t)(t_run - t_claim) << 32);
+        r[3] = (unsigned long long)(uint32_t)(t_end - t_run);
       }
-      __syncthreads();
-      if (sm.flag) {  // last routing tile of the layer: S runs here (dynamic mode)
-        scan_task(p, L, t.layer, sm);
-        after_scan(p, t.layer, sm);
-      }
-    } else if (t.kind == K_S) {
-      scan_task(p, L, t.layer, sm);
-      after_scan(p, t.layer, sm);
-    } else if (t.kind == K_GU) {
-      gateup_task<TE>(p, L, t.a, t.b, t.c, sm);
-      wg_publish();
-      const int gpc = L.plan[PL_GPC];
-      const int s = t.c / gpc;
-      if (tid == 0) {
-        const int rt = L.rt_base[t.a] + t.b;
-        const int need = min(gpc, p.n1 - s * gpc);
-        const int old = ev_add(L.ev_gu + rt * p.n1 + s, 1);
-        sm.flag = (p.mode == ETC_SCHED_DYNAMIC && old + 1 == need) ? 1 : 0;
-      }
-      __syncthreads();
-      if (sm.flag) {
-        const int layer = t.layer, e = t.a, m = t.b;
-        push_many(p, sm, p.n2, [&](int i) {
-          Task d;
-          d.kind = K_D; d.layer = layer; d.a = e; d.b = m; d.c = i; d.d = s;
-          return d;
-        });
-      }
-    } else if (t.kind == K_D) {
-      down_task<TE>(p, L, t.a, t.b, t.c, t.d, L.plan[PL_GPC], sm);
-      wg_publish();
-      // one signal per run of rows in the same routing tile (rows are token-sorted)
-      const int valid = min(BM, L.counts[t.a] - t.b * BM);
-      if (tid < valid) {
-        const int tau = sm.u.t.row_tok[tid] / BT;
-        if (tid == 0 || sm.u.t.row_tok[tid - 1] / BT != tau) {
-          int len = 1;
-          while (tid + len < valid && sm.u.t.row_tok[tid + len] / BT == tau) ++len;
-          const int old = ev_add(L.ev_comb + tau, len);
-          const int target = tile_rows(p, tau) * p.K * p.n2 * L.plan[PL_NS];
-          if (p.mode == ETC_SCHED_DYNAMIC && old + len == target) {
-            Task f;
-            f.kind = K_F; f.layer = t.layer; f.a = tau; f.b = f.c = f.d = 0;
-            push_one(p, f);
-          }
-        }
-      }
-      __syncthreads();
-    } else if (t.kind == K_F) {
-      finalize_task<TE>(p, L, t.a);
-      wg_publish();
-      if (tid == 0) {
-        ev_store(L.ev_done + t.a, 1);
-        if (p.mode == ETC_SCHED_DYNAMIC && t.layer + 1 < p.L) {
-          Task r;
-          r.kind = K_R; r.layer = t.layer + 1; r.a = t.a; r.b = r.c = r.d = 0;
-          push_one(p, r);
-        }
-      }
-      __syncthreads();
     }
   }
 
@@ -801,14 +825,17 @@ __global__ __launch_bounds__(NT) void moe_kernel(Args p) {
         ev_store_relaxed(L.ev_done + i, 0);
       }
     }
-    if (tid < W_NWORDS && tid != W_STATUS && tid != W_AUX) ev_store_relaxed(p.sched + tid, 0);
+    if (tid == 0) ev_store_relaxed(p.sched + W_TRACE_LAST, ev_load_relaxed(p.sched + W_TRACE));
+    __syncthreads();
+    if (tid < W_NWORDS && tid != W_STATUS && tid != W_AUX && tid != W_TRACE_LAST)
+      ev_store_relaxed(p.sched + tid, 0);
   }
 }
 
 // ------------------------------------------------------------------ host side
 
 struct Layout {
-  size_t sched, queue, xq, hbuf, out_acc, ybuf, act, total;
+  size_t sched, queue, trace, xq, hbuf, out_acc, ybuf, act, total;
   struct {
     size_t topk_idx, topk_w, lrank, hist, tile_off, counts, offsets, rt_base, sorted_assign, pos,
         plan, ev_route, ev_scan, ev_gu, ev_comb, ev_done;
@@ -837,6 +864,7 @@ inline Layout layout(int Tm, int H, int E, int K, int F, int nl, int es, bool or
   // + room for the one extra slot each worker draws before it sees the end
   Y.queue_len = (int)(Y.n_rt + per_layer * nl + MAX_WORKERS);
   Y.queue = c.take((size_t)Y.queue_len * sizeof(long long));
+  Y.trace = c.take((size_t)Y.queue_len * 32);  // one record per task at most
   for (int l = 0; l < nl; ++l) {
     const size_t pairs = (size_t)Tm * K;
     Y.l[l].topk_idx = c.take(pairs * 4);
@@ -920,6 +948,8 @@ ETC_API etc_status etc_moe_workspace_layout(int32_t max_tokens, int32_t hidden, 
   out[10] = moe::BM;
   out[11] = moe::BN1;
   out[12] = moe::BN2;
+  out[13] = (int64_t)Y.trace;
+  out[14] = Y.queue_len;
   return ETC_OK;
 }
 
@@ -945,6 +975,7 @@ ETC_API etc_status etc_moe_layer(int32_t T, int32_t H, int32_t E, int32_t K, int
   if (mode != ETC_SCHED_STATIC && mode != ETC_SCHED_DYNAMIC) return ETC_ERR_INVALID_ARG;
   if (mode == ETC_SCHED_DYNAMIC && !dynamic_sched_enabled()) return ETC_ERR_UNSUPPORTED;
   if (combine != ETC_COMBINE_ATOMIC && combine != ETC_COMBINE_ORDERED) return ETC_ERR_INVALID_ARG;
+  if (T == 0) return ETC_OK;  // nothing to compute; empty tensors may have null pointers
   if (!weights || !x || !out) return ETC_ERR_INVALID_ARG;
   if (!host::aligned16(x) || !host::aligned16(out) || (layer_out && !host::aligned16(layer_out)))
     return ETC_ERR_INVALID_ARG;
@@ -967,7 +998,6 @@ ETC_API etc_status etc_moe_layer(int32_t T, int32_t H, int32_t E, int32_t K, int
     return ETC_ERR_WORKSPACE;
   const int dev = host::current_gfx950_device();
   if (dev < 0) return ETC_ERR_NO_DEVICE;
-  if (T == 0) return ETC_OK;
 
   char* ws = static_cast<char*>(workspace);
   moe::Args p;
@@ -992,6 +1022,8 @@ ETC_API etc_status etc_moe_layer(int32_t T, int32_t H, int32_t E, int32_t K, int
   p.out_acc = reinterpret_cast<float*>(ws + Y.out_acc);
   p.ybuf = combine == ETC_COMBINE_ORDERED ? reinterpret_cast<float*>(ws + Y.ybuf) : nullptr;
   p.queue = reinterpret_cast<long long*>(ws + Y.queue);
+  p.trace = reinterpret_cast<unsigned long long*>(ws + Y.trace);
+  p.trace_cap = Y.queue_len;
   p.sched = reinterpret_cast<int*>(ws + Y.sched);
   const size_t act_bytes = (size_t)T * H * es;
   for (int l = 0; l < nl; ++l) {

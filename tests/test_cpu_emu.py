@@ -100,3 +100,40 @@ def test_splitk(lib, mode):
                                binding.MODES[mode], 0, 0, None) == 0
     ref = osk.splitk_gemm(synth.as_numpy(A), synth.as_numpy(B), S)
     assert np.max(np.abs(C.numpy() - ref)) <= 1e-3 * np.max(np.abs(ref))
+
+
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
+def test_trace_has_one_record_per_task(lib, mode):
+    from moe_layer_scheduling_amd import trace
+
+    cfg = MID.with_(layers=2)
+    T = 40
+    layers, x = synth.make_layers(cfg), synth.make_x(cfg, T, call=9)
+    g = driver.moe(lib, cfg, x, layers, mode=mode, flags=binding.FLAG_TRACE)
+    _check(cfg, x, layers, g)
+    n = ctypes.c_int32.from_address(g["wptr"] + 4 * binding.W_TRACE_LAST).value
+    out = (ctypes.c_int64 * binding.LAYOUT_WORDS)()
+    assert lib.etc_moe_workspace_layout(T, cfg.hidden, cfg.experts, cfg.top_k, cfg.ffn, 2, 1, 0,
+                                        0, out) == 0
+    rec = np.frombuffer((ctypes.c_uint64 * (4 * n)).from_address(g["wptr"] + out[13]),
+                        dtype=np.uint64).reshape(n, 4)
+    d = trace.decode(rec)
+    n_rt = -(-T // 16)
+    for l in range(2):
+        plan = np.array((ctypes.c_int32 * 8).from_address(g["wptr"] + lib_layout(lib, T, cfg, l)[5]))
+        kinds = d["kind"][d["layer"] == l]
+        got = {k: int((kinds == k).sum()) for k in range(1, 6)}
+        want = {1: n_rt, 3: int(plan[1]), 4: int(plan[2]), 5: int(plan[3])}
+        # the scan runs as its own task in static mode and inside the last routing
+        # task in dynamic mode
+        want[2] = 1 if mode == "static" else 0
+        assert got == want, (l, got, want)
+    s = trace.summarize(rec)
+    assert s["span_us"] > 0 and 0 < s["busy_fraction"] <= 1
+
+
+def lib_layout(lib, T, cfg, l):
+    out = (ctypes.c_int64 * binding.LAYOUT_WORDS)()
+    assert lib.etc_moe_workspace_layout(T, cfg.hidden, cfg.experts, cfg.top_k, cfg.ffn,
+                                        cfg.layers, 1, 0, l, out) == 0
+    return list(out)
