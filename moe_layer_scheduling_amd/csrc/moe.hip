@@ -12,14 +12,14 @@
 // call for online scheduling through atomics (§5.5 Obstacle 3).
 //
 // Tasks of layer l (BT = 16 tokens per routing tile, BM = 128 rows per expert row tile,
-// BN1 = 64 ffn columns per gate/up tile, BN2 = 128 hidden columns per down tile):
+// BN1 = 128 ffn columns per gate/up tile, BN2 = 256 hidden columns per down tile):
 //   R(tau)         RMSNorm, router logits, top-k, softmax for 16 tokens; ranks of their
 //                  (token, slot) pairs inside the tile and the tile's expert histogram
 //                  -> ev_route[l] += 1.  For l > 0 it waits ev_done[l-1][tau] >= 1.
 //   S              waits ev_route[l] >= n_rt: counts, exclusive scan, row tiles per
 //                  expert, permutation; sizes the down split (nS chunks of GPC gate/up
 //                  tiles) from the actual number of row tiles; -> ev_scan[l] = 1.
-//   GU(e, m, n)    gate/up tile of expert e rows m*128.. and ffn columns n*64..;
+//   GU(e, m, n)    gate/up tile of expert e rows m*128.. and ffn columns n*128..;
 //                  h = silu(G) * U -> ev_gu[l][rt(e,m)][n / GPC] += 1.
 //   D(e, m, n2, s) down tile over ffn chunk s; waits ev_gu[l][rt][s] >= tiles in chunk s;
 //                  adds gate * y into the float32 accumulator (or stores y) ->
@@ -43,8 +43,10 @@ namespace etc {
 namespace moe {
 
 constexpr int MAXL = 4, MAXE = 256, MAXK = 16;
-constexpr int BT = 16, BM = 128, BN1 = 64, BN2 = 128;
-constexpr int RCH = 512, XS_STRIDE = RCH + 4;  // routing: hidden chunk staged in LDS
+constexpr int BT = 16, BM = 128, BN1 = 128, BN2 = 256;
+// H: whole 16-byte chunks in each of the router's four K slices; F: whole 64-value chunks
+// (tiles along F and H are masked at the edge)
+constexpr int H_ALIGN = 128, F_ALIGN = 64;
 constexpr int MAX_WORKERS = 2048;
 constexpr int MAX_TOKENS = 262143;  // task fields are 14 bits
 
@@ -119,7 +121,8 @@ struct Args {
 };
 
 struct RouteSmem {
-  float xs[BT][XS_STRIDE];
+  float part[4 * BT * 64 > BT * MAXE ? 4 * BT * 64 : BT * MAXE];  // [KS][BT][E] partial logits
+  float ssp[4][BT];                                              // [KS][BT] partial sums of squares
   float lg[BT][MAXE];
   float rs[BT];
   int sel[BT][MAXK];
@@ -173,90 +176,141 @@ ETC_DEV int owner_expert(const int* rt_base, int E, int idx, int mult) {
 }
 
 // ------------------------------------------------------------------ R: routing tile
+//
+// logits[t][e] = rms_t * sum_h (x[t][h] * gamma[h]) * W_r[e][h] (+ b[e]) on the matrix cores:
+// the float32 values v = x * gamma are split exactly into three bfloat16 parts
+// (hi = bf16(v), mid = bf16(v - hi), lo = bf16(v - hi - mid)); each product of a part with a
+// bfloat16 weight is exact in float32, and the three parts accumulate separately in
+// float32, so the dot product has float32 accuracy.  Float32 layers use the float32 MFMA
+// directly.  Waves take (16-expert block, K slice) items; with fewer than four expert
+// blocks the K range is split across waves and the partial sums are added in slice
+// order.  The sum of squares for the RMS comes from the same loads.
+
+template <typename TE>
+ETC_DEV void router_step(const uint4& xv, const uint4& wv, const float* g, f32x4 (&acc)[3], float& ss);
+
+template <>
+ETC_DEV void router_step<bf16>(const uint4& xv, const uint4& wv, const float* g, f32x4 (&acc)[3],
+                               float& ss) {
+  float x[8];
+  expand16(xv, x, (const bf16*)nullptr);
+  uint32_t hi[4], mid[4], lo[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t ph[2], pm[2], pl[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const float xe = x[2 * i + q];
+      ss += xe * xe;
+      const float v = xe * g[2 * i + q];
+      ph[q] = f32_to_bf16_bits(v);
+      const float r1 = v - bf16_bits_to_f32(ph[q]);
+      pm[q] = f32_to_bf16_bits(r1);
+      pl[q] = f32_to_bf16_bits(r1 - bf16_bits_to_f32(pm[q]));
+    }
+    hi[i] = ph[0] | (ph[1] << 16);
+    mid[i] = pm[0] | (pm[1] << 16);
+    lo[i] = pl[0] | (pl[1] << 16);
+  }
+  const bf16* tag = nullptr;
+  mma16(acc[0], make_uint4(hi[0], hi[1], hi[2], hi[3]), wv, tag);
+  mma16(acc[1], make_uint4(mid[0], mid[1], mid[2], mid[3]), wv, tag);
+  mma16(acc[2], make_uint4(lo[0], lo[1], lo[2], lo[3]), wv, tag);
+}
+
+template <>
+ETC_DEV void router_step<float>(const uint4& xv, const uint4& wv, const float* g, f32x4 (&acc)[3],
+                                float& ss) {
+  float x[4];
+  expand16(xv, x, (const float*)nullptr);
+  float v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ss += x[i] * x[i];
+    v[i] = x[i] * g[i];
+  }
+  mma16(acc[0], make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                           __float_as_uint(v[3])),
+        wv, (const float*)nullptr);
+}
 
 template <typename TE>
 ETC_DEV void route_task(const Args& p, const LayerArgs& L, int tau, Smem& sm) {
   constexpr int EPC = 16 / (int)sizeof(TE);
-  constexpr int QMAX = MAXE * BT / NT;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  constexpr int KSTEP = 4 * EPC;  // K consumed per MFMA step by the four lane groups
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = p.H, E = p.E, K = p.K;
   const int t0 = tau * BT, nt = tile_rows(p, tau);
   const TE* x = static_cast<const TE*>(L.in);
   const TE* wr = static_cast<const TE*>(L.w_router);
   TE* xq = static_cast<TE*>(p.xq);
   RouteSmem& R = sm.u.r;
-  const TE* tag = nullptr;
 
-  // 1. reciprocal RMS per token (wave w: tokens w, w+4, ...)
-  for (int tt = w; tt < BT; tt += 4) {
+  // 1. partial logits and sums of squares per (expert block, K slice)
+  const int NB = cdiv(E, 16);
+  const int KS = NB >= 4 ? 1 : 4 / NB;  // K slices per expert block: 1, 2 or 4
+  const int kslice = H / KS;           // a multiple of KSTEP (H is a multiple of 128)
+  const int row = lane & 15, grp = lane >> 4;
+  const bool tok_ok = row < nt;
+  const TE* xrow = x + (size_t)(t0 + (tok_ok ? row : 0)) * H;
+  for (int it = w; it < NB * KS; it += 4) {
+    const int nb = it / KS, ks = it % KS;
+    const int e = nb * 16 + row;
+    const bool e_ok = e < E;
+    const TE* wrow = wr + (size_t)(e_ok ? e : 0) * H;
+    f32x4 acc[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     float ss = 0.f;
-    if (tt < nt) {
-      const TE* row = x + (size_t)(t0 + tt) * H;
-      for (int h = lane * EPC; h < H; h += WAVE * EPC) {
-        float v[EPC];
-        expand16(*reinterpret_cast<const uint4*>(row + h), v, tag);
+    const int kb = ks * kslice, ke = kb + kslice;
+#pragma unroll 4
+    for (int k0 = kb; k0 < ke; k0 += KSTEP) {
+      const int k = k0 + grp * EPC;
+      const uint4 xv = tok_ok ? *reinterpret_cast<const uint4*>(xrow + k) : zero4();
+      const uint4 wv = e_ok ? *reinterpret_cast<const uint4*>(wrow + k) : zero4();
+      float g[EPC];
 #pragma unroll
-        for (int i = 0; i < EPC; ++i) ss += v[i] * v[i];
-      }
+      for (int i = 0; i < EPC; ++i) g[i] = L.gamma[k + i];
+      router_step<TE>(xv, wv, g, acc, ss);
     }
-    ss = wave_sum(ss);
-    if (lane == 0) R.rs[tt] = (tt < nt) ? 1.0f / sqrtf(ss / (float)H + p.eps) : 0.f;
+    const f32x4 sum = (acc[2] + acc[1]) + acc[0];
+    if (e_ok) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) R.part[(ks * BT + grp * 4 + i) * E + e] = sum[i];
+    }
+    if (nb == 0) {  // the sum of squares of this K slice, once per token
+      ss += __shfl_xor(ss, 16, WAVE);
+      ss += __shfl_xor(ss, 32, WAVE);
+      if (grp == 0) R.ssp[ks][row] = ss;
+    }
+  }
+  __syncthreads();
+  if (tid < BT) {
+    float ss = 0.f;
+    for (int ks = 0; ks < KS; ++ks) ss += R.ssp[ks][tid];
+    R.rs[tid] = (tid < nt) ? 1.0f / sqrtf(ss / (float)H + p.eps) : 0.f;
+  }
+  __syncthreads();
+  for (int o = tid; o < BT * E; o += NT) {
+    const int tt = o / E, e = o % E;
+    float v = 0.f;
+    for (int ks = 0; ks < KS; ++ks) v += R.part[(ks * BT + tt) * E + e];
+    R.lg[tt][e] = R.rs[tt] * v + (L.bias ? L.bias[e] : 0.f);
   }
   __syncthreads();
 
-  // 2. normalised rows chunk by chunk: the storage copy goes to xq for the experts, the
-  //    float32 values feed the router (output o = (token o % 16, expert o / 16))
-  const int nout = BT * E;
-  float logit[QMAX];
+  // 2. normalised rows in storage precision for the experts
+  const int cpr = H / EPC;
+  for (int c = tid; c < nt * cpr; c += NT) {
+    const int tt = c / cpr, h = (c % cpr) * EPC;
+    float v[EPC];
+    expand16(*reinterpret_cast<const uint4*>(x + (size_t)(t0 + tt) * H + h), v, (const TE*)nullptr);
+    const float r = R.rs[tt];
 #pragma unroll
-  for (int q = 0; q < QMAX; ++q) logit[q] = 0.f;
-  for (int h0 = 0; h0 < H; h0 += RCH) {
-    const int hw = min(RCH, H - h0);
-    const int cpr = hw / EPC;  // chunks per row
-    for (int c = tid; c < BT * cpr; c += NT) {
-      const int tt = c / cpr, hc = (c % cpr) * EPC;
-      float v[EPC];
-      if (tt < nt) {
-        expand16(*reinterpret_cast<const uint4*>(x + (size_t)(t0 + tt) * H + h0 + hc), v, tag);
-        const float r = R.rs[tt];
-#pragma unroll
-        for (int i = 0; i < EPC; ++i) v[i] = v[i] * r * L.gamma[h0 + hc + i];
-        *reinterpret_cast<uint4*>(xq + (size_t)(t0 + tt) * H + h0 + hc) = pack16<TE>(v);
-      } else {
-#pragma unroll
-        for (int i = 0; i < EPC; ++i) v[i] = 0.f;
-      }
-#pragma unroll
-      for (int i = 0; i < EPC; ++i) R.xs[tt][hc + i] = v[i];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < QMAX; ++q) {
-      const int o = tid + NT * q;
-      if (o < nout) {
-        const int tt = o % BT, e = o / BT;
-        const TE* wrow = wr + (size_t)e * H + h0;
-        float part = 0.f;
-        for (int hh = 0; hh < hw; hh += EPC) {
-          float wv[EPC];
-          expand16(*reinterpret_cast<const uint4*>(wrow + hh), wv, tag);
-#pragma unroll
-          for (int i = 0; i < EPC; ++i) part += R.xs[tt][hh + i] * wv[i];
-        }
-        logit[q] += part;
-      }
-    }
-    __syncthreads();
+    for (int i = 0; i < EPC; ++i) v[i] = v[i] * r * L.gamma[h + i];
+    *reinterpret_cast<uint4*>(xq + (size_t)(t0 + tt) * H + h) = pack16<TE>(v);
   }
-#pragma unroll
-  for (int q = 0; q < QMAX; ++q) {
-    const int o = tid + NT * q;
-    if (o < nout) {
-      const int tt = o % BT, e = o / BT;
-      R.lg[tt][e] = logit[q] + (L.bias ? L.bias[e] : 0.f);
-    }
-  }
-  __syncthreads();
 
   // 3. top-k by (logit desc, expert asc) with k rounds of a wave argmax; softmax over
   //    the selected logits
@@ -438,6 +492,7 @@ ETC_DEV void scan_task(const Args& p, const LayerArgs& L, int layer, Smem& sm) {
 
 template <typename TE>
 ETC_DEV void gateup_task(const Args& p, const LayerArgs& L, int e, int m, int n, Smem& sm) {
+  using Tile = KTile<TE>;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int H = p.H, F = p.F, K = p.K;
   TileSmem& Ts = sm.u.t;
@@ -449,31 +504,34 @@ ETC_DEV void gateup_task(const Args& p, const LayerArgs& L, int e, int m, int n,
   const TE* xq = static_cast<const TE*>(p.xq);
   const TE* wg = static_cast<const TE*>(L.w_gate);
   const TE* wu = static_cast<const TE*>(L.w_up);
-  const char* rowp[8];
+  const char* rowp[Tile::LOADS];
   const int row0 = tid >> 3;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int tok = Ts.row_tok[row0 + 32 * i];
     rowp[i] = (tok >= 0) ? reinterpret_cast<const char*>(xq + (size_t)tok * H) : nullptr;
-    // B row b: 16-row blocks alternate gate / up over the same 16 ffn columns
-    const int b = row0 + 32 * i, blk = b >> 4;
+  }
+  // B row b: 16-row blocks alternate gate / up over the same 16 ffn columns
+#pragma unroll
+  for (int i = 4; i < Tile::LOADS; ++i) {
+    const int b = row0 + 32 * (i - 4), blk = b >> 4;
     const int f = n * BN1 + (blk >> 1) * 16 + (b & 15);
     const TE* src = (blk & 1) ? wu : wg;
-    rowp[4 + i] = reinterpret_cast<const char*>(src + ((size_t)e * F + f) * H);
+    rowp[i] = (f < F) ? reinterpret_cast<const char*>(src + ((size_t)e * F + f) * H) : nullptr;
   }
-  f32x4 acc[4][4];
-  KTile<TE>::run(Ts.gemm, rowp, H, acc);
+  f32x4 acc[4][8];
+  Tile::run(Ts.gemm, rowp, H, valid, acc);
 
   TE* hb = static_cast<TE*>(p.hbuf);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+    for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-        if (row < valid) {
-          const int f = n * BN1 + (2 * wn + jj) * 16 + (lane & 15);
+        const int f = n * BN1 + (wn * 4 + jj) * 16 + (lane & 15);
+        if (row < valid && f < F) {
           const float g = acc[i][2 * jj][r], u = acc[i][2 * jj + 1][r];
           Elem<TE>::store(hb, (size_t)(r0 + row) * F + f, g / (1.0f + expf(-g)) * u);
         }
@@ -483,6 +541,7 @@ ETC_DEV void gateup_task(const Args& p, const LayerArgs& L, int e, int m, int n,
 template <typename TE>
 ETC_DEV void down_task(const Args& p, const LayerArgs& L, int e, int m, int n2i, int s, int gpc,
                        Smem& sm) {
+  using Tile = KTile<TE>;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int H = p.H, F = p.F, K = p.K;
   TileSmem& Ts = sm.u.t;
@@ -504,26 +563,30 @@ ETC_DEV void down_task(const Args& p, const LayerArgs& L, int e, int m, int n2i,
   const int klen = min(F, kb + gpc * BN1) - kb;
   const TE* hb = static_cast<const TE*>(p.hbuf);
   const TE* wd = static_cast<const TE*>(L.w_down);
-  const char* rowp[8];
+  const char* rowp[Tile::LOADS];
   const int row0 = tid >> 3;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = row0 + 32 * i;
     rowp[i] = (r < valid) ? reinterpret_cast<const char*>(hb + (size_t)(r0 + r) * F + kb) : nullptr;
-    rowp[4 + i] = reinterpret_cast<const char*>(wd + ((size_t)e * H + n2i * BN2 + r) * F + kb);
   }
-  f32x4 acc[4][4];
-  KTile<TE>::run(Ts.gemm, rowp, klen, acc);
+#pragma unroll
+  for (int i = 4; i < Tile::LOADS; ++i) {
+    const int h = n2i * BN2 + row0 + 32 * (i - 4);
+    rowp[i] = (h < H) ? reinterpret_cast<const char*>(wd + ((size_t)e * H + h) * F + kb) : nullptr;
+  }
+  f32x4 acc[4][8];
+  Tile::run(Ts.gemm, rowp, klen, valid, acc);
 
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-        if (row < valid) {
-          const int col = n2i * BN2 + wn * 64 + j * 16 + (lane & 15);
+        const int col = n2i * BN2 + wn * 128 + j * 16 + (lane & 15);
+        if (row < valid && col < H) {
           if (p.combine == ETC_COMBINE_ATOMIC)
             atomicAdd(p.out_acc + (size_t)Ts.row_tok[row] * H + col, Ts.row_gate[row] * acc[i][j][r]);
           else
@@ -847,8 +910,8 @@ inline Layout layout(int Tm, int H, int E, int K, int F, int nl, int es, bool or
   Layout Y;
   Y.n_rt = cdiv(Tm, BT);
   Y.max_rt = (Tm * K) / BM + (E < Tm * K ? E : Tm * K);
-  Y.n1 = F / BN1;
-  Y.n2 = H / BN2;
+  Y.n1 = cdiv(F, BN1);
+  Y.n2 = cdiv(H, BN2);
   host::Carve c;
   Y.sched = c.take(W_NWORDS * sizeof(int));
   for (int l = 0; l < nl; ++l) {  // counters first: the control region
@@ -910,7 +973,7 @@ static etc_status moe_shape_check(int32_t Tm, int32_t H, int32_t E, int32_t K, i
   if (Tm < 0 || H < 1 || E < 1 || K < 1 || F < 1 || nl < 1) return ETC_ERR_INVALID_ARG;
   if (dt != ETC_DTYPE_F32 && dt != ETC_DTYPE_BF16) return ETC_ERR_INVALID_ARG;
   if (K > E) return ETC_ERR_INVALID_ARG;
-  if (H % moe::BN2 || F % moe::BN1 || E > moe::MAXE || K > moe::MAXK || nl > moe::MAXL ||
+  if (H % moe::H_ALIGN || F % moe::F_ALIGN || E > moe::MAXE || K > moe::MAXK || nl > moe::MAXL ||
       Tm > moe::MAX_TOKENS)
     return ETC_ERR_UNSUPPORTED;
   return ETC_OK;

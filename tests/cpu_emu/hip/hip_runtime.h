@@ -12,6 +12,8 @@
 #pragma once
 
 #include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
@@ -91,6 +93,17 @@ inline T __shfl_up(T v, unsigned delta, int width = 64) {
   const int src = lane - (int)delta;
   return emu_exchange(v, src < base ? lane : src);
 }
+
+// lane 0's value; every use in the kernels passes a wave-uniform value, which is checked
+inline int emu_readfirstlane(int v) {
+  const int first = emu_exchange(v, 0);
+  if (first != v) {
+    fprintf(stderr, "readfirstlane of a non-uniform value\n");
+    abort();
+  }
+  return first;
+}
+#define __builtin_amdgcn_readfirstlane(x) emu_readfirstlane(x)
 
 template <typename T>
 inline T min(T a, T b) { return b < a ? b : a; }

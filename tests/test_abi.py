@@ -62,7 +62,8 @@ def test_workspace_sizes(lib):
     assert _moe_ws(lib, 4096, comb=1) > _moe_ws(lib, 4096)  # ordered keeps y rows
     assert _moe_ws(lib, 4096, dt=0) > _moe_ws(lib, 4096)  # float32 activations
     assert _moe_ws(lib, 16, H=100) == 0  # hidden not a multiple of 128
-    assert _moe_ws(lib, 16, F=100) == 0
+    assert _moe_ws(lib, 16, F=100) == 0  # ffn not a multiple of 64
+    assert _moe_ws(lib, 16, H=384, F=320) > 0  # ragged tiles along H and F are masked
     assert _moe_ws(lib, 16, E=300, k=2) == 0
     assert _moe_ws(lib, 16, E=4, k=5) == 0
     assert _moe_ws(lib, 16, L=5) == 0
@@ -80,7 +81,8 @@ def test_layout_offsets_inside_workspace(lib):
         assert all(0 < o < n and o % 4 == 0 for o in offs[:6] + [offs[13]])
         assert offs[14] > 0 and offs[13] + 32 * offs[14] <= n
         assert offs[6] == 4096 * 6 // 128 + 64  # row-tile capacity
-        assert offs[7] == 1408 // 64 and offs[8] == 4096 // 16
+        bn1 = offs[11]
+        assert offs[7] == (1408 + bn1 - 1) // bn1 and offs[8] == 4096 // offs[9]
     assert lib.etc_moe_workspace_layout(4096, 4096, 64, 6, 1408, 2, 1, 0, 2, out) == 1
 
 

@@ -55,6 +55,18 @@ def test_mid_ragged_one_layer(lib, mode):
     _check(cfg, x, layers, driver.moe(lib, cfg, x, layers, mode=mode, max_tokens=300))
 
 
+EDGE = synth.MoEConfig("edge", (70,), 384, 6, 2, 320, layers=2, zipf_s=0.3)
+
+
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
+def test_ragged_hidden_and_ffn_tiles(lib, mode):
+    """H = 384 and F = 320 end inside a column tile of both GEMMs and inside a split of
+    the down projection."""
+    cfg = EDGE
+    layers, x = synth.make_layers(cfg), synth.make_x(cfg, 70)
+    _check(cfg, x, layers, driver.moe(lib, cfg, x, layers, mode=mode))
+
+
 def test_mid_two_layers_dynamic(lib):
     cfg = MID
     layers, x = synth.make_layers(cfg), synth.make_x(cfg, 300)

@@ -66,6 +66,19 @@ def test_mid_two_layers(mode, combine):
     say(_compare(cfg, x, lnp, gpu))
 
 
+EDGE = synth.MoEConfig("edge", (70,), 384, 6, 2, 320, layers=2, zipf_s=0.3)
+
+
+@pytest.mark.parametrize("combine", ["atomic", "ordered"])
+def test_ragged_hidden_and_ffn_tiles(combine):
+    """H = 384 and F = 320 end inside a column tile of both GEMMs."""
+    cfg = EDGE
+    x, layers, ld, lnp = _setup(cfg, 70)
+    say(f"edge H=384 F=320 combine={combine}")
+    gpu = run_moe(x.cuda(), ld, cfg.top_k, mode="static", combine=combine)
+    say(_compare(cfg, x, lnp, gpu))
+
+
 def test_ordered_combine_is_bit_reproducible():
     """Ordered combine: three calls give bit-identical outputs."""
     cfg = MID
