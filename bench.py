@@ -191,6 +191,18 @@ def bench_splitk(steps, warmup, mode="static", copies=4):
             "mode": mode}
 
 
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A plain device copy of known size (one elementwise kernel reading nbytes and writing
+    nbytes per call): the reference against which the L2 fetch/write byte counters of the
+    MoE kernel are scaled to HBM bytes."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    ms, launch_ms, _ = time_steps(lambda: torch.mul(src, 1.0, out=dst), reps, 1)
+    return {"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "calls": reps + 1,
+            "launch_ms": launch_ms, "gbs": 2 * nbytes / (launch_ms / 1e3) / 1e9}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,6 +217,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", dest="cpu", action="store_false", default=True)
     ap.add_argument("--trace-out", default=None,
                     help="also run one traced call and write a Chrome trace here")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB elementwise copy (counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -214,6 +228,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        print(json.dumps(copy_calibration()), flush=True)
+        return
     binding.load_library()
 
     cfg = synth.CONFIGS[args.workload]

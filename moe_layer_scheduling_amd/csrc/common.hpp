@@ -127,8 +127,10 @@ enum SchedWord {
   W_AUX = 8,      // debug: where the abort came from
   W_TRACE = 9,    // trace records written so far in this call
   W_TRACE_LAST = 10,  // trace records of the last traced call (survives the reset)
-  W_NWORDS = 16
+  W_XTICKET = 16,     // static: next ticket of each of the (up to 8) XCD queues
+  W_NWORDS = 32
 };
+constexpr int MAX_XCD_QUEUES = 8;  // MI355X: 8 XCDs of 32 CUs, each with its own L2
 
 // Waits poll with relaxed loads (no cache invalidation per poll: an agent-scope acquire
 // invalidates this CU's L1 and the XCD's L2 lines, which would keep evicting the operands

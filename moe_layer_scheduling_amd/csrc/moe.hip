@@ -630,8 +630,26 @@ ETC_DEV void finalize_task(const Args& p, const LayerArgs& L, int tau) {
 // ------------------------------------------------------------------ scheduling
 
 // Static: the ticket's task; waits for S of a layer before decoding past it.
+// Static mode: the fixed task order (per layer: all R, S, all GU, all D, all F) is cut
+// into chunks of G consecutive tasks, chunk c belonging to queue c mod Q; workgroup b
+// draws from queue b mod Q.  The dispatcher places workgroup b on XCD b mod 8, so with
+// Q = 8 each chunk runs on one XCD: the row tiles that share a weight tile and the
+// column tiles that share a token tile are taken together and meet in that XCD's L2
+// instead of being fetched once per XCD.  G = workers / Q, one task per CU of the XCD.
+// Each queue hands out its tasks in the global order and has at least one workgroup
+// (Q <= workers), so the smallest waiting task always has its inputs claimed by
+// workgroups that are not waiting on it: the order stays deadlock-free.
+ETC_DEV int static_ticket(const Args& p) {
+  const int nwg = (int)gridDim.x;
+  const int Q = nwg < MAX_XCD_QUEUES ? nwg : MAX_XCD_QUEUES;
+  const int G = nwg / Q;
+  const int q = (int)blockIdx.x % Q;
+  const int i = atomicAdd(p.sched + W_XTICKET + q, 1);
+  return ((i / G) * Q + q) * G + i % G;
+}
+
 ETC_DEV bool claim_static(const Args& p, Task& t, uint64_t deadline) {
-  const int ticket = atomicAdd(p.sched + W_TICKET, 1);
+  const int ticket = static_ticket(p);
   int base = 0;
   for (int l = 0; l < p.L; ++l) {
     const LayerArgs& L = p.layer[l];

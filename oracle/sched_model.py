@@ -136,20 +136,32 @@ def _signal(task, counters):
         counters[c] = counters.get(c, 0) + amt
 
 
-def simulate_static(graph, workers, rng=None):
-    """Workers draw tickets in order and spin on the drawn task's waits.  Returns the
-    execution order; raises RuntimeError on deadlock (no worker can move)."""
+def queue_ticket(q, i, queues, chunk):
+    """Position in the static order of the i-th ticket of queue q when the order is cut
+    into chunks of `chunk` consecutive tasks dealt round-robin to `queues` queues."""
+    return ((i // chunk) * queues + q) * chunk + i % chunk
+
+
+def simulate_static(graph, workers, rng=None, queues=1, chunk=1):
+    """Workers draw tickets and spin on the drawn task's waits.  With queues > 1 the
+    order is dealt to the queues in chunks (queue_ticket) and worker w draws only from
+    queue w mod queues, each queue in its own order.  Returns the execution order;
+    raises RuntimeError on deadlock (no worker can move)."""
     rng = rng or random.Random(0)
     order = static_order(graph)
     counters, executed = {}, []
-    next_ticket = 0
+    next_local = [0] * queues
     holding = [None] * workers  # task drawn by each worker
     while len(executed) < len(order):
-        # every idle worker draws the next ticket (drawing is an atomic increment)
+        # every idle worker draws its queue's next ticket (an atomic increment); a
+        # ticket past the end of the order means the queue is drained
         for w in range(workers):
-            if holding[w] is None and next_ticket < len(order):
-                holding[w] = order[next_ticket]
-                next_ticket += 1
+            q = w % queues
+            if holding[w] is None:
+                g = queue_ticket(q, next_local[q], queues, chunk)
+                if g < len(order):
+                    holding[w] = order[g]
+                    next_local[q] += 1
         movable = [w for w in range(workers)
                    if holding[w] is not None and _ready(holding[w], counters)]
         if not movable:

@@ -56,6 +56,47 @@ def test_static_and_dynamic_complete(T, H, F, E, k, L, plan):
 
 
 @pytest.mark.parametrize("T,H,F,E,k,L,plan", CASES)
+def test_static_xcd_queues_complete(T, H, F, E, k, L, plan):
+    """The static order dealt in chunks to up to 8 queues (one per XCD), each worker
+    drawing only from its own queue: every task runs once and every counter ends at
+    its target, for worker counts that do and do not divide into the queues."""
+    rng = np.random.default_rng(T + 3 * E)
+    idx = [_random_idx(rng, T, E, k, skew=1.1 if E >= 64 else 0.0) for _ in range(L)]
+    graph = _graph_from_routing(T, H, F, k, E, idx, plan)
+    final = sm.expected_final_counters(graph)
+    for workers in (1, 2, 8, 17, 64):
+        queues = min(8, workers)
+        for seed in range(2):
+            ex, ctr = sm.simulate_static(graph, workers, random.Random(seed), queues=queues,
+                                         chunk=workers // queues)
+            assert sm.check_execution(ex, graph) == final
+            assert ctr == final
+
+
+def test_queue_tickets_partition_the_order():
+    """Queue tickets cover every position of the order exactly once, in increasing
+    order within each queue."""
+    for queues, chunk in ((1, 1), (8, 32), (8, 2), (3, 5)):
+        seen = []
+        for q in range(queues):
+            pos = [sm.queue_ticket(q, i, queues, chunk) for i in range(200)]
+            assert pos == sorted(pos)
+            seen += pos
+        n = 200 * queues
+        assert sorted(p for p in seen if p < n - queues * chunk) == list(range(n - queues * chunk))
+
+
+def test_unserved_queue_deadlocks():
+    """More queues than workers leaves a queue nobody draws from: the model reports the
+    deadlock (the kernel therefore uses at most as many queues as workgroups)."""
+    rng = np.random.default_rng(5)
+    plan = sm.Plan(BT=8, BM=16, BN1=32, BN2=64, GPC=2)
+    graph = _graph_from_routing(24, 128, 128, 2, 8, [_random_idx(rng, 24, 8, 2)], plan)
+    with pytest.raises(RuntimeError, match="deadlocked"):
+        sm.simulate_static(graph, 2, queues=3, chunk=1)
+
+
+@pytest.mark.parametrize("T,H,F,E,k,L,plan", CASES)
 def test_targets_equal_final_counts(T, H, F, E, k, L, plan):
     """Every wait target is exactly the value its counter reaches: the targets computed
     from the routing (counts, rows per routing tile) match what the producers signal."""
