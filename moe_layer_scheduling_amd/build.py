@@ -21,6 +21,10 @@ FLAGS = [
     "-fvisibility=hidden",
     # keep the compiler from forming packed float32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: with accumulation registers the allocator
+    # splits the 128 accumulators of a 64 x 128 wave tile across both register files and
+    # copies them around every MFMA of the GEMM loop
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-Wno-unused-command-line-argument",
 ]
 

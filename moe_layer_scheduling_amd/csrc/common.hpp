@@ -16,6 +16,8 @@ constexpr int WAVE = 64;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// 16 raw bytes as a native vector: copies are register moves, never memcpy through memory
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 struct bf16 {
   uint16_t bits;
@@ -103,6 +105,29 @@ ETC_DEV void q_store_relaxed(long long* p, long long v) {
 }
 ETC_DEV void fence_release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
 ETC_DEV void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+// Direct copy of 16 bytes per lane from global memory into LDS (gfx950
+// global_load_lds_dwordx4): lane l of the wave writes lds_wave_base + 16 * l, so
+// lds_wave_base must be the same in every lane of the wave.  The copy completes
+// asynchronously; it counts as an outstanding vector-memory operation of the wave
+// until the data is in LDS (see vm_wait_barrier).
+ETC_DEV void lds_dma16(const void* src, void* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_wave_base, 16, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding (and all
+// of its LDS operations are done), then meet the workgroup at a barrier.  The
+// compiler-only fences keep LDS reads and copies from moving across the wait.
+template <int N>
+ETC_DEV void vm_wait_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  // s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4] (7: no wait), lgkmcnt [11:8]
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // Every thread waits until all of its own memory operations have completed, then the
 // workgroup meets at a barrier: after this, one thread's agent-scope release covers

@@ -20,6 +20,18 @@ ETC_DEV void mma16(f32x4& c, const uint4& a, const uint4& b, const bf16*) {
   c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, c, 0, 0, 0);
 }
 
+ETC_DEV void mma16(f32x4& c, const u32x4& a, const u32x4& b, const bf16*) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                              c, 0, 0, 0);
+}
+
+ETC_DEV void mma16(f32x4& c, const u32x4& a, const u32x4& b, const float*) {
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), c, 0, 0, 0);
+}
+
 ETC_DEV void mma16(f32x4& c, const uint4& a, const uint4& b, const float*) {
   c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), c, 0, 0, 0);
   c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), c, 0, 0, 0);
@@ -35,6 +47,12 @@ ETC_DEV int swz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) &
 
 ETC_DEV uint4 lds_chunk(const char* base, int row, int chunk) {
   return *reinterpret_cast<const uint4*>(base + swz(row, chunk));
+}
+// The same read as a native vector.  Reads of this type are what the compiler can tell
+// apart from direct global-to-LDS copies still in flight, so it does not make them wait
+// for every outstanding copy (the tile pipeline orders them with explicit waits).
+ETC_DEV u32x4 lds_chunk_v(const char* base, int row, int chunk) {
+  return *reinterpret_cast<const u32x4*>(base + swz(row, chunk));
 }
 ETC_DEV void lds_put_chunk(char* base, int row, int chunk, const uint4& v) {
   *reinterpret_cast<uint4*>(base + swz(row, chunk)) = v;

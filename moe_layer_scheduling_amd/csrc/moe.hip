@@ -133,7 +133,7 @@ struct ScanSmem {
   int tmp[8];
 };
 struct TileSmem {
-  char gemm[KTile<float>::LDS_BYTES];
+  alignas(16) char gemm[KTile<float>::LDS_BYTES];  // 16-byte LDS reads and copies
   int row_tok[BM];
   float row_gate[BM];
 };
@@ -505,19 +505,21 @@ ETC_DEV void gateup_task(const Args& p, const LayerArgs& L, int e, int m, int n,
   const TE* wg = static_cast<const TE*>(L.w_gate);
   const TE* wu = static_cast<const TE*>(L.w_up);
   const char* rowp[Tile::LOADS];
-  const int row0 = tid >> 3;
+  const int row0 = tid >> 3, lc = Tile::load_chunk(tid) * 16;
+  // rows past the expert's count read the first row, columns past F read row F-1: their
+  // results are never stored
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int tok = Ts.row_tok[row0 + 32 * i];
-    rowp[i] = (tok >= 0) ? reinterpret_cast<const char*>(xq + (size_t)tok * H) : nullptr;
+    rowp[i] = reinterpret_cast<const char*>(xq + (size_t)(tok >= 0 ? tok : Ts.row_tok[0]) * H) + lc;
   }
   // B row b: 16-row blocks alternate gate / up over the same 16 ffn columns
 #pragma unroll
   for (int i = 4; i < Tile::LOADS; ++i) {
     const int b = row0 + 32 * (i - 4), blk = b >> 4;
-    const int f = n * BN1 + (blk >> 1) * 16 + (b & 15);
+    const int f = min(n * BN1 + (blk >> 1) * 16 + (b & 15), F - 1);
     const TE* src = (blk & 1) ? wu : wg;
-    rowp[i] = (f < F) ? reinterpret_cast<const char*>(src + ((size_t)e * F + f) * H) : nullptr;
+    rowp[i] = reinterpret_cast<const char*>(src + ((size_t)e * F + f) * H) + lc;
   }
   f32x4 acc[4][8];
   Tile::run(Ts.gemm, rowp, H, valid, acc);
@@ -564,16 +566,18 @@ ETC_DEV void down_task(const Args& p, const LayerArgs& L, int e, int m, int n2i,
   const TE* hb = static_cast<const TE*>(p.hbuf);
   const TE* wd = static_cast<const TE*>(L.w_down);
   const char* rowp[Tile::LOADS];
-  const int row0 = tid >> 3;
+  const int row0 = tid >> 3, lc = Tile::load_chunk(tid) * 16;
+  // rows past the expert's count read the first row, columns past H read row H-1: their
+  // results are never stored
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = row0 + 32 * i;
-    rowp[i] = (r < valid) ? reinterpret_cast<const char*>(hb + (size_t)(r0 + r) * F + kb) : nullptr;
+    rowp[i] = reinterpret_cast<const char*>(hb + (size_t)(r0 + (r < valid ? r : 0)) * F + kb) + lc;
   }
 #pragma unroll
   for (int i = 4; i < Tile::LOADS; ++i) {
-    const int h = n2i * BN2 + row0 + 32 * (i - 4);
-    rowp[i] = (h < H) ? reinterpret_cast<const char*>(wd + ((size_t)e * H + h) * F + kb) : nullptr;
+    const int h = min(n2i * BN2 + row0 + 32 * (i - 4), H - 1);
+    rowp[i] = reinterpret_cast<const char*>(wd + ((size_t)e * H + h) * F + kb) + lc;
   }
   f32x4 acc[4][8];
   Tile::run(Ts.gemm, rowp, klen, valid, acc);

@@ -51,7 +51,7 @@ struct Args {
 };
 
 struct Smem {
-  char stage[2][STAGE];
+  alignas(16) char stage[2][STAGE];
   int task;  // broadcast slot
   int flag;
 };

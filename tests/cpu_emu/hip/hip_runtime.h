@@ -133,6 +133,15 @@ inline float atomicAdd(float* p, float v) {
 #define __builtin_amdgcn_s_sleep(x) emu_yield()
 #define __builtin_amdgcn_s_memrealtime() emu_realtime()
 
+// global_load_lds: lane l writes 16 bytes at the wave's LDS base + 16 * l; the CPU copy
+// is synchronous, so the waits that order it on the GPU are no-ops here
+inline void emu_global_load_lds(const void* src, void* lds_base, int size, int off) {
+  memcpy(static_cast<char*>(lds_base) + off + emu_lane() * size, src, size);
+}
+#define __builtin_amdgcn_global_load_lds(src, dst, size, off, aux) \
+  emu_global_load_lds((const void*)(src), (void*)(dst), (size), (off))
+#define __builtin_amdgcn_s_barrier() emu_syncthreads()
+
 emu_f32x4 emu_mfma_bf16(emu_bf16x8 a, emu_bf16x8 b, emu_f32x4 c);
 emu_f32x4 emu_mfma_f32(float a, float b, emu_f32x4 c);
 #define __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, x, y, z) emu_mfma_bf16((a), (b), (c))
