@@ -117,16 +117,25 @@ ETC_DEV void lds_dma16(const void* src, void* lds_wave_base) {
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding (and all
-// of its LDS operations are done), then meet the workgroup at a barrier.  The
-// compiler-only fences keep LDS reads and copies from moving across the wait.
+// of its LDS operations are done), then meet the workgroup at a barrier.  Nothing moves
+// across it: the compiler-only fences keep memory operations in place, the scheduling
+// barriers keep every other instruction (MFMAs above all) on its side.
 template <int N>
 ETC_DEV void vm_wait_barrier() {
   static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_sched_barrier(0);
   // s_waitcnt fields: vmcnt [3:0] and [15:14], expcnt [6:4] (7: no wait), lgkmcnt [11:8]
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
   __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Wait until this wave's LDS reads (and scalar loads) have completed; vector-memory
+// operations may stay outstanding.
+ETC_DEV void lgkm_wait_all() {
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));  // vmcnt 63, expcnt 7, lgkmcnt 0
 }
 
 // Every thread waits until all of its own memory operations have completed, then the

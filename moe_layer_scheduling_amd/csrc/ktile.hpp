@@ -1,35 +1,41 @@
-// 128 x 256 output tile over K-contiguous operands on bf16 (or float32) MFMA.
+// 128 x 256 output tile over K-contiguous operands on bf16 (or float32) MFMA, computed
+// by a workgroup of 4 or 8 waves (NTH = 256 or 512 threads).
 //
 // Both operands are lists of rows whose K values are contiguous in memory: A rows are
 // token activations (gathered through the MoE permutation), B rows are weight rows in
-// nn.Linear layout.  The tile stages 384 rows (i < 4: A rows 32i..32i+31, i >= 4: B rows
-// 32(i-4)..) through LDS, 128 bytes of K per row per stage (64 bf16 or 32 float values,
-// 48 KiB), in three rotating slots (144 KiB).
+// nn.Linear layout.  The tile stages 384 rows (128 A rows, then 256 B rows) through
+// LDS, 128 bytes of K per row per stage (64 bf16 or 32 float values, 48 KiB), in three
+// rotating slots (144 KiB).
 //
 // Operands go from global memory straight into LDS (16 bytes per lane per copy, no
-// staging registers).  For copy i, wave w fills rows 8w + 32i .. +7 of the slot, one
-// 1 KiB run of LDS: lane l lands at byte 16 l of the run, i.e. row 8w + 32i + l/8 at
-// chunk position l % 8.  The LDS layout is swizzled (chunk c of row r sits at position
-// c ^ ((r >> 1) & 7), see mfma.hpp), so lane l fetches the global chunk that belongs at
-// its position: c = (l % 8) ^ ((4w + l/16) % 8).  Thread t therefore reads rows
-// t/8 + 32i at chunk c(t); rowp[i] is that row's address at k = 0.  Every pointer must
-// address a readable row: callers point rows past an expert's token count or past the
-// matrix edge at a valid row and discard those output rows and columns.
+// staging registers).  Thread t makes LOADS = 384 * 8 / NTH copies per stage, copy i
+// covering tile row t/8 + RSTEP*i (RSTEP = NTH/8).  For copy i, wave w fills rows
+// 8w + RSTEP*i .. +7, one 1 KiB run of LDS: lane l lands at byte 16 l of the run, i.e.
+// row 8w + RSTEP*i + l/8 at chunk position l % 8.  The LDS layout is swizzled (chunk c
+// of row r sits at position c ^ ((r >> 1) & 7), see mfma.hpp), so lane l fetches the
+// global chunk that belongs at its position: c = (l % 8) ^ ((4w + l/16) % 8).  rowp[i]
+// is the address of thread t's row at k = 0 plus 16 c.  Every pointer must address a
+// readable row: callers point rows past an expert's token count or past the matrix edge
+// at a valid row and discard those output rows and columns.
 //
-// Pipeline: the copies for stage k+2 are issued right after the barrier of step k and
-// run under the MFMAs of stages k and k+1.  Before the barrier of step k each thread
-// waits until only its 12 copies of stage k+1 are outstanding (its part of stage k has
-// landed); after the barrier every wave's part has landed and every wave has finished
-// reading slot (k-1) mod 3, the slot stage k+2 then overwrites.  Past the last stage
-// the copies re-read the last stage into a slot no step reads, so every step issues the
-// same 12 copies and the wait count is a constant; the run drains them before returning.
+// Pipeline: the copies run three stages ahead of the MFMAs, and each half-stage of
+// MFMAs (one 16 x 16 x 32 step per fragment pair) overlaps the LDS reads of the next
+// half-stage.  In step k the wave reads the second half of stage k, runs the MFMAs of
+// the first half (read at the end of step k-1), then waits until only its copies of
+// stage k+2 are outstanding and meets the workgroup at a barrier: stage k+1 has landed
+// everywhere and every wave's reads of slot k mod 3 have completed, so the copies of
+// stage k+3 go into that slot; the wave then reads the first half of stage k+1 and runs
+// the MFMAs of the second half of stage k.  Copies past the last stage re-read the last
+// stage into a slot no step reads, so every step issues the same copies and the wait
+// count is a constant; the run drains them before returning.
 //
-// Waves form a 2 x 2 grid; wave (wm, wn) owns rows wm*64.. and columns wn*128.. of the
-// tile as 4 x 8 blocks of 16 x 16 (acc[i][j]): element r of acc[i][j] in lane l is
-// row wm*64 + 16*i + 4*(l/16) + r, column wn*128 + 16*j + (l % 16).  Row blocks past
-// `rows` (the valid row count) skip their MFMAs: the count of live blocks is fixed per
-// tile and selects one of five branch-free instances of the loop.  Register arrays are
-// indexed through static_for, so every index is a compile-time constant.
+// Waves form a 2 x WN grid (WN = NTH/128); wave (wm, wn) owns rows wm*64.. and columns
+// wn*WCOLS.. (WCOLS = 256/WN) of the tile as 4 x NJ blocks of 16 x 16 (acc[i][j]):
+// element r of acc[i][j] in lane l is row wm*64 + 16*i + 4*(l/16) + r, column
+// wn*WCOLS + 16*j + (l % 16).  Row blocks past `rows` (the valid row count) skip their
+// MFMAs: the count of live blocks is fixed per tile and selects one of five branch-free
+// instances of the loop.  Register arrays are indexed through static_for, so every
+// index is a compile-time constant.
 #pragma once
 
 #include <utility>
@@ -50,33 +56,45 @@ ETC_DEV void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-template <typename TE>
+template <typename TE, int NTH = NT>
 struct KTile {
+  static_assert(NTH == 256 || NTH == 512, "4 or 8 waves");
   static constexpr int BM = 128, BN = 256;
   static constexpr int ROWS = BM + BN;              // 384
-  static constexpr int LOADS = ROWS * 8 / NT;       // 16-byte copies per thread per stage: 12
+  static constexpr int LOADS = ROWS * 8 / NTH;      // 16-byte copies per thread per stage: 12 or 6
+  static constexpr int RSTEP = NTH / 8;             // rows between a thread's copies: 32 or 64
+  static constexpr int ALOADS = BM / RSTEP;         // copies of A rows: 4 or 2
   static constexpr int STAGE_BYTES = ROWS * 128;    // 48 KiB
   static constexpr int NSTAGE = 3;
   static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;  // 144 KiB
   static constexpr int EPC = 16 / (int)sizeof(TE);  // elements per 16-byte chunk
   static constexpr int BK = 128 / (int)sizeof(TE);  // K per stage
+  static constexpr int WN = NTH / 128;              // wave columns: 2 or 4 (2 wave rows)
+  static constexpr int WCOLS = BN / WN;             // columns per wave: 128 or 64
+  static constexpr int NJ = WCOLS / 16;             // 16-column blocks per wave: 8 or 4
 
   // The 16-byte chunk of its rows (within each 128-byte stage) that thread tid copies.
   ETC_DEV static int load_chunk(int tid) {
     const int l = tid & 63, w = tid >> 6;
     return (l & 7) ^ ((4 * w + (l >> 4)) & 7);
   }
+  // Row of the tile that copy i of thread tid reads (i < ALOADS: A rows, else B rows
+  // counted from the first B row).
+  ETC_DEV static int load_row(int tid, int i) { return (tid >> 3) + RSTEP * i; }
 
-  // rowp[i]: byte pointer of row (tid/8 + 32*i) at k = 0.  klen: K values, a positive
-  // multiple of BK.  rows: valid A rows (MFMAs of row blocks past it are skipped).
+  // rowp[i]: byte pointer of row load_row(tid, i) (minus BM for B rows) at k = 0, plus
+  // load_chunk(tid) * 16.  klen: K values, a positive multiple of BK.  rows: valid A
+  // rows (MFMAs of row blocks past it are skipped).  Wave w owns rows (w / WN) * 64 ..
+  // +63 and columns (w % WN) * WCOLS .. of the tile; acc[i][j] holds the 16 x 16 block
+  // (16 i, 16 j) of that region.
   ETC_DEV static void run(char* smem, const char* const (&rowp)[LOADS], int klen, int rows,
-                          f32x4 (&acc)[4][8]) {
+                          f32x4 (&acc)[4][NJ]) {
     static_for<4>([&](auto i) ETC_INLINE {
-      static_for<8>([&](auto j) ETC_INLINE { acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f}; });
+      static_for<NJ>([&](auto j) ETC_INLINE { acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f}; });
     });
     // the wave index is uniform across the wave: say so, so that per-wave choices become
     // scalar branches instead of exec-masked code
-    const int wm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) >> 1;
+    const int wm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) / WN;
     const int live = __builtin_amdgcn_readfirstlane(min(4, max(0, cdiv(rows - wm * 64, 16))));
     switch (live) {
       case 4: pipeline<4>(smem, rowp, klen, acc); break;
@@ -91,43 +109,84 @@ struct KTile {
   }
 
  private:
+  // Operand fragments of one K half-stage (32 bf16 / 16 float values) for this wave.
+  struct Half {
+    u32x4 a[4], b[NJ];
+  };
+
   template <int LIVE>
   ETC_DEV static void pipeline(char* smem, const char* const (&rowp)[LOADS], int klen,
-                               f32x4 (&acc)[4][8]) {
+                               f32x4 (&acc)[4][NJ]) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = w >> 1, wn = w & 1;
+    const int wm = w / WN, wn = w % WN;
     const int nk = klen / BK, last = nk - 1;
     const TE* tag = nullptr;
+    // per-lane LDS byte offsets of the fragment rows within a slot, chunk kk * 4 + l/16
+    int aoff[2][4], boff[2][NJ];
+    static_for<2>([&](auto kk) ETC_INLINE {
+      const int c = kk * 4 + (lane >> 4);
+      static_for<4>([&](auto i) ETC_INLINE { aoff[kk][i] = swz(wm * 64 + i * 16 + (lane & 15), c); });
+      static_for<NJ>([&](auto j) ETC_INLINE { boff[kk][j] = swz(BM + wn * WCOLS + j * 16 + (lane & 15), c); });
+    });
 
     auto issue = [&](int kt) ETC_INLINE {
-      const size_t off = (size_t)kt * 128;
+      const int st = min(kt, last);  // past the last stage: re-read it into an unread slot
+      const size_t off = (size_t)st * 128;
       char* slot = smem + (kt % NSTAGE) * STAGE_BYTES + w * 8 * 128;
-      static_for<LOADS>([&](auto i) ETC_INLINE { lds_dma16(rowp[i] + off, slot + i * 32 * 128); });
+      static_for<LOADS>([&](auto i) ETC_INLINE { lds_dma16(rowp[i] + off, slot + i * RSTEP * 128); });
     };
-    auto compute = [&](int kt) ETC_INLINE {
+    auto read = [&](Half& f, int kt, auto kk) ETC_INLINE {
       const char* base = smem + (kt % NSTAGE) * STAGE_BYTES;
-      static_for<2>([&](auto kk) ETC_INLINE {
-        const int c = kk * 4 + (lane >> 4);
-        u32x4 a[4], b[8];
-        static_for<8>([&](auto j) ETC_INLINE {
-          b[j] = lds_chunk_v(base, BM + wn * 128 + j * 16 + (lane & 15), c);
-        });
-        static_for<LIVE>([&](auto i) ETC_INLINE {
-          a[i] = lds_chunk_v(base, wm * 64 + i * 16 + (lane & 15), c);
-        });
-        static_for<LIVE>([&](auto i) ETC_INLINE {
-          static_for<8>([&](auto j) ETC_INLINE { mma16(acc[i][j], a[i], b[j], tag); });
-        });
+      static_for<NJ>([&](auto j) ETC_INLINE { f.b[j] = *reinterpret_cast<const u32x4*>(base + boff[kk][j]); });
+      static_for<LIVE>([&](auto i) ETC_INLINE { f.a[i] = *reinterpret_cast<const u32x4*>(base + aoff[kk][i]); });
+    };
+    auto mma = [&](const Half& f) ETC_INLINE {
+      static_for<LIVE>([&](auto i) ETC_INLINE {
+        static_for<NJ>([&](auto j) ETC_INLINE { mma16(acc[i][j], f.a[i], f.b[j], tag); });
       });
     };
+    constexpr auto K0 = std::integral_constant<int, 0>{};
+    constexpr auto K1 = std::integral_constant<int, 1>{};
+    // Issue order within each half-step: the copies and LDS reads are spread over the
+    // MFMAs (one memory instruction, then one MFMA) instead of going out in a burst that
+    // stalls the wave on a full vector-memory queue before its first MFMA.
+    constexpr int NMMA = LIVE * NJ, NRD = NJ + LIVE;
+    auto interleave = [&](auto ncopy) ETC_INLINE {
+      if constexpr (NMMA >= (int)decltype(ncopy)::value + NRD) {
+        static_for<decltype(ncopy)::value>([&](auto) ETC_INLINE {
+          __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // vector-memory read
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        });
+        static_for<NRD>([&](auto) ETC_INLINE {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        });
+        __builtin_amdgcn_sched_group_barrier(0x008, NMMA - decltype(ncopy)::value - NRD, 0);
+      }
+    };
 
+    Half h0, h1;
     issue(0);
-    issue(min(1, last));
+    issue(1);
+    issue(2);
+    vm_wait_barrier<2 * LOADS>();  // stage 0 has landed
+    read(h0, 0, K0);
     for (int kt = 0; kt < nk; ++kt) {
+      // the first-half fragments were read before the previous MFMAs and have arrived;
+      // waiting for them here leaves the compiler nothing outstanding that the MFMAs
+      // below depend on, so it does not wait for the reads issued next
+      lgkm_wait_all();
+      read(h1, kt, K1);
+      mma(h0);
+      interleave(std::integral_constant<int, 0>{});
+      // stage kt+1 has landed everywhere, and every wave has finished reading slot
+      // kt mod 3 (its reads completed before the barrier): stage kt+3 may overwrite it
       vm_wait_barrier<LOADS>();
-      issue(min(kt + 2, last));
-      compute(kt);
+      issue(kt + 3);
+      read(h0, kt + 1, K0);  // past the last stage: unused reads of an unused slot
+      mma(h1);
+      interleave(std::integral_constant<int, LOADS>{});
     }
   }
 };

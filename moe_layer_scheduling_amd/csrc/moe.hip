@@ -44,11 +44,19 @@ namespace moe {
 
 constexpr int MAXL = 4, MAXE = 256, MAXK = 16;
 constexpr int BT = 16, BM = 128, BN1 = 128, BN2 = 256;
+// workgroup of the persistent kernel: 8 waves, two per SIMD, so that one wave's MFMAs
+// run while the other waits on LDS
+constexpr int MNT = 512, NWAVE = MNT / 64;
 // H: whole 16-byte chunks in each of the router's four K slices; F: whole 64-value chunks
 // (tiles along F and H are masked at the edge)
 constexpr int H_ALIGN = 128, F_ALIGN = 64;
 constexpr int MAX_WORKERS = 2048;
 constexpr int MAX_TOKENS = 262143;  // task fields are 14 bits
+
+// Task bodies are separate functions: each gets its own register allocation instead of
+// sharing one with the scheduler loop and every other task (inlined together they spill
+// inside the GEMM loop).  A call per task costs nothing next to the task itself.
+#define ETC_TASK __device__ __attribute__((noinline))
 
 enum Kind { K_NONE = 0, K_R = 1, K_S = 2, K_GU = 3, K_D = 4, K_F = 5 };
 enum PlanWord { PL_RT = 0, PL_NGU, PL_ND, PL_NF, PL_NS, PL_GPC, PL_NEXTBASE, PL_WORDS = 8 };
@@ -130,10 +138,11 @@ struct RouteSmem {
 struct ScanSmem {
   int off[MAXE + 1];
   int rtb[MAXE + 1];
-  int tmp[8];
+  int tmp[NWAVE];
+  int part[MNT];  // per-thread partial counts over a chunk of routing tiles
 };
 struct TileSmem {
-  alignas(16) char gemm[KTile<float>::LDS_BYTES];  // 16-byte LDS reads and copies
+  alignas(16) char gemm[KTile<float, MNT>::LDS_BYTES];  // 16-byte LDS reads and copies
   int row_tok[BM];
   float row_gate[BM];
 };
@@ -235,7 +244,7 @@ ETC_DEV void router_step<float>(const uint4& xv, const uint4& wv, const float* g
 }
 
 template <typename TE>
-ETC_DEV void route_task(const Args& p, const LayerArgs& L, int tau, Smem& sm) {
+ETC_TASK void route_task(const Args& p, const LayerArgs& L, int tau, Smem& sm) {
   constexpr int EPC = 16 / (int)sizeof(TE);
   constexpr int KSTEP = 4 * EPC;  // K consumed per MFMA step by the four lane groups
   const int tid = threadIdx.x, lane = tid & 63;
@@ -249,12 +258,12 @@ ETC_DEV void route_task(const Args& p, const LayerArgs& L, int tau, Smem& sm) {
 
   // 1. partial logits and sums of squares per (expert block, K slice)
   const int NB = cdiv(E, 16);
-  const int KS = NB >= 4 ? 1 : 4 / NB;  // K slices per expert block: 1, 2 or 4
+  const int KS = NB >= NWAVE ? 1 : min(4, NWAVE / NB);  // K slices per expert block: 1, 2 or 4
   const int kslice = H / KS;           // a multiple of KSTEP (H is a multiple of 128)
   const int row = lane & 15, grp = lane >> 4;
   const bool tok_ok = row < nt;
   const TE* xrow = x + (size_t)(t0 + (tok_ok ? row : 0)) * H;
-  for (int it = w; it < NB * KS; it += 4) {
+  for (int it = w; it < NB * KS; it += NWAVE) {
     const int nb = it / KS, ks = it % KS;
     const int e = nb * 16 + row;
     const bool e_ok = e < E;
@@ -292,7 +301,7 @@ ETC_DEV void route_task(const Args& p, const LayerArgs& L, int tau, Smem& sm) {
     R.rs[tid] = (tid < nt) ? 1.0f / sqrtf(ss / (float)H + p.eps) : 0.f;
   }
   __syncthreads();
-  for (int o = tid; o < BT * E; o += NT) {
+  for (int o = tid; o < BT * E; o += MNT) {
     const int tt = o / E, e = o % E;
     float v = 0.f;
     for (int ks = 0; ks < KS; ++ks) v += R.part[(ks * BT + tt) * E + e];
@@ -302,7 +311,7 @@ ETC_DEV void route_task(const Args& p, const LayerArgs& L, int tau, Smem& sm) {
 
   // 2. normalised rows in storage precision for the experts
   const int cpr = H / EPC;
-  for (int c = tid; c < nt * cpr; c += NT) {
+  for (int c = tid; c < nt * cpr; c += MNT) {
     const int tt = c / cpr, h = (c % cpr) * EPC;
     float v[EPC];
     expand16(*reinterpret_cast<const uint4*>(x + (size_t)(t0 + tt) * H + h), v, (const TE*)nullptr);
@@ -314,7 +323,7 @@ ETC_DEV void route_task(const Args& p, const LayerArgs& L, int tau, Smem& sm) {
 
   // 3. top-k by (logit desc, expert asc) with k rounds of a wave argmax; softmax over
   //    the selected logits
-  for (int tt = w; tt < nt; tt += 4) {
+  for (int tt = w; tt < nt; tt += NWAVE) {
     float v[4];
     int id[4];
 #pragma unroll
@@ -369,14 +378,14 @@ ETC_DEV void route_task(const Args& p, const LayerArgs& L, int tau, Smem& sm) {
 
   // 4. rank of each pair among the tile's pairs of the same expert (tokens ascending;
   //    a token never holds one expert twice) and the tile's expert histogram
-  for (int a = tid; a < nt * K; a += NT) {
+  for (int a = tid; a < nt * K; a += MNT) {
     const int tt = a / K, j = a % K, e = R.sel[tt][j];
     int rank = 0;
     for (int u = 0; u < tt; ++u)
       for (int jj = 0; jj < K; ++jj) rank += (R.sel[u][jj] == e);
     L.lrank[(t0 + tt) * K + j] = rank;
   }
-  for (int e = tid; e < E; e += NT) {
+  for (int e = tid; e < E; e += MNT) {
     int c = 0;
     for (int u = 0; u < nt; ++u)
       for (int jj = 0; jj < K; ++jj) c += (R.sel[u][jj] == e);
@@ -386,7 +395,7 @@ ETC_DEV void route_task(const Args& p, const LayerArgs& L, int tau, Smem& sm) {
   // 5. clear this tile's accumulator rows for the atomic combine
   if (p.combine == ETC_COMBINE_ATOMIC) {
     float4* acc = reinterpret_cast<float4*>(p.out_acc + (size_t)t0 * H);
-    for (int i = tid; i < nt * H / 4; i += NT) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int i = tid; i < nt * H / 4; i += MNT) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
 }
 
@@ -403,28 +412,41 @@ ETC_DEV int block_exclusive_scan(int v, int* tmp, int& total) {
   if (lane == 63) tmp[w] = x;
   __syncthreads();
   int before = 0;
-  for (int i = 0; i < w; ++i) before += tmp[i];
-  total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVE; ++i) {
+    before += (i < w) ? tmp[i] : 0;
+    total += tmp[i];
+  }
   __syncthreads();
   return before + x - v;
 }
 
-ETC_DEV void scan_task(const Args& p, const LayerArgs& L, int layer, Smem& sm) {
+ETC_TASK void scan_task(const Args& p, const LayerArgs& L, int layer, Smem& sm) {
   const int tid = threadIdx.x;
   const int E = p.E, K = p.K, n_rt = p.n_rt;
   ScanSmem& S = sm.u.s;
 
-  // counts per expert (thread e), then exclusive scans of counts and of row tiles
-  int cnt = 0;
-  if (tid < E) {
-    for (int tau = 0; tau < n_rt; tau += 8) {
+  // counts per expert: thread t sums the histogram of expert t / C over chunk t % C of
+  // the routing tiles (C = MNT / E chunks per expert, so every thread takes part)
+  const int C = MNT / E, e_t = tid / C, c_t = tid % C;
+  const int span = cdiv(n_rt, C), tau0 = c_t * span, tau1 = min(n_rt, tau0 + span);
+  const bool owner = e_t < E;
+  int part = 0;
+  if (owner) {
+    for (int tau = tau0; tau < tau1; tau += 8) {
       int v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = (tau + u < n_rt) ? L.hist[(tau + u) * E + tid] : 0;
+      for (int u = 0; u < 8; ++u) v[u] = (tau + u < tau1) ? L.hist[(tau + u) * E + e_t] : 0;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) cnt += v[u];
+      for (int u = 0; u < 8; ++u) part += v[u];
     }
   }
+  S.part[tid] = part;
+  __syncthreads();
+  int cnt = 0;
+  if (tid < E)
+    for (int c = 0; c < C; ++c) cnt += S.part[tid * C + c];
   int total_rows = 0, RT = 0;
   const int off = block_exclusive_scan(cnt, S.tmp, total_rows);
   const int rtb = block_exclusive_scan(cdiv(cnt, BM), S.tmp, RT);
@@ -441,17 +463,20 @@ ETC_DEV void scan_task(const Args& p, const LayerArgs& L, int layer, Smem& sm) {
     L.offsets[E] = total_rows;
     L.rt_base[E] = RT;
   }
-  // first sorted row of every (routing tile, expert) block
-  if (tid < E) {
-    int run = off;
-    for (int tau = 0; tau < n_rt; tau += 8) {
+  __syncthreads();
+  // first sorted row of every (routing tile, expert) block: each thread continues the
+  // running offset of its expert through its chunk
+  if (owner) {
+    int run = S.off[e_t];
+    for (int c = 0; c < c_t; ++c) run += S.part[e_t * C + c];
+    for (int tau = tau0; tau < tau1; tau += 8) {
       int v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = (tau + u < n_rt) ? L.hist[(tau + u) * E + tid] : 0;
+      for (int u = 0; u < 8; ++u) v[u] = (tau + u < tau1) ? L.hist[(tau + u) * E + e_t] : 0;
 #pragma unroll
       for (int u = 0; u < 8; ++u)
-        if (tau + u < n_rt) {
-          L.tile_off[(tau + u) * E + tid] = run;
+        if (tau + u < tau1) {
+          L.tile_off[(tau + u) * E + e_t] = run;
           run += v[u];
         }
     }
@@ -479,60 +504,83 @@ ETC_DEV void scan_task(const Args& p, const LayerArgs& L, int layer, Smem& sm) {
   wg_publish();
   fence_acquire_agent();  // tile_off written above by other lanes of this workgroup
 
-  // scatter: pair a = t*k + j goes to row tile_off[tau][e] + rank
-  for (int a = tid; a < p.T * K; a += NT) {
-    const int t = a / K, e = L.topk_idx[a];
-    const int r = L.tile_off[(t / BT) * E + e] + L.lrank[a];
-    L.sorted_assign[r] = a;
-    L.pos[a] = r;
+  // scatter: pair a = t*k + j goes to row tile_off[tau][e] + rank; eight pairs per
+  // thread at a time, so their loads are in flight together
+  const int npairs = p.T * K;
+  for (int a0 = tid; a0 < npairs; a0 += 8 * MNT) {
+    int e[8], rk[8], to[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int a = min(a0 + u * MNT, npairs - 1);
+      e[u] = L.topk_idx[a];
+      rk[u] = L.lrank[a];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int a = min(a0 + u * MNT, npairs - 1);
+      to[u] = L.tile_off[(a / K / BT) * E + e[u]];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int a = a0 + u * MNT;
+      if (a < npairs) {
+        const int r = to[u] + rk[u];
+        L.sorted_assign[r] = a;
+        L.pos[a] = r;
+      }
+    }
   }
 }
 
 // ------------------------------------------------------------------ GU / D / F
 
 template <typename TE>
-ETC_DEV void gateup_task(const Args& p, const LayerArgs& L, int e, int m, int n, Smem& sm) {
-  using Tile = KTile<TE>;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+ETC_TASK void gateup_task(const Args& p, const LayerArgs& L, int e, int m, int n, Smem& sm) {
+  using Tile = KTile<TE, MNT>;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w / Tile::WN, wn = w % Tile::WN;
   const int H = p.H, F = p.F, K = p.K;
   TileSmem& Ts = sm.u.t;
   const int r0 = L.offsets[e] + m * BM;
   const int valid = min(BM, L.counts[e] - m * BM);
-  for (int i = tid; i < BM; i += NT) Ts.row_tok[i] = (i < valid) ? L.sorted_assign[r0 + i] / K : -1;
+  for (int i = tid; i < BM; i += MNT) Ts.row_tok[i] = (i < valid) ? L.sorted_assign[r0 + i] / K : -1;
   __syncthreads();
 
   const TE* xq = static_cast<const TE*>(p.xq);
   const TE* wg = static_cast<const TE*>(L.w_gate);
   const TE* wu = static_cast<const TE*>(L.w_up);
   const char* rowp[Tile::LOADS];
-  const int row0 = tid >> 3, lc = Tile::load_chunk(tid) * 16;
+  const int lc = Tile::load_chunk(tid) * 16;
   // rows past the expert's count read the first row, columns past F read row F-1: their
   // results are never stored
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int tok = Ts.row_tok[row0 + 32 * i];
-    rowp[i] = reinterpret_cast<const char*>(xq + (size_t)(tok >= 0 ? tok : Ts.row_tok[0]) * H) + lc;
+  for (int i = 0; i < Tile::LOADS; ++i) {
+    const int r = Tile::load_row(tid, i);
+    if (i < Tile::ALOADS) {
+      const int tok = Ts.row_tok[r];
+      rowp[i] = reinterpret_cast<const char*>(xq + (size_t)(tok >= 0 ? tok : Ts.row_tok[0]) * H) + lc;
+    } else {
+      // B row b: 16-row blocks alternate gate / up over the same 16 ffn columns
+      const int b = r - BM, blk = b >> 4;
+      const int f = min(n * BN1 + (blk >> 1) * 16 + (b & 15), F - 1);
+      const TE* src = (blk & 1) ? wu : wg;
+      rowp[i] = reinterpret_cast<const char*>(src + ((size_t)e * F + f) * H) + lc;
+    }
   }
-  // B row b: 16-row blocks alternate gate / up over the same 16 ffn columns
-#pragma unroll
-  for (int i = 4; i < Tile::LOADS; ++i) {
-    const int b = row0 + 32 * (i - 4), blk = b >> 4;
-    const int f = min(n * BN1 + (blk >> 1) * 16 + (b & 15), F - 1);
-    const TE* src = (blk & 1) ? wu : wg;
-    rowp[i] = reinterpret_cast<const char*>(src + ((size_t)e * F + f) * H) + lc;
-  }
-  f32x4 acc[4][8];
+  f32x4 acc[4][Tile::NJ];
   Tile::run(Ts.gemm, rowp, H, valid, acc);
 
+  // column block j of this wave is gate (j even) or up (j odd) for ffn columns
+  // n*BN1 + (wn*NJ + j)/2 * 16 ..
   TE* hb = static_cast<TE*>(p.hbuf);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj)
+    for (int jj = 0; jj < Tile::NJ / 2; ++jj)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-        const int f = n * BN1 + (wn * 4 + jj) * 16 + (lane & 15);
+        const int f = n * BN1 + (wn * Tile::NJ / 2 + jj) * 16 + (lane & 15);
         if (row < valid && f < F) {
           const float g = acc[i][2 * jj][r], u = acc[i][2 * jj + 1][r];
           Elem<TE>::store(hb, (size_t)(r0 + row) * F + f, g / (1.0f + expf(-g)) * u);
@@ -541,15 +589,16 @@ ETC_DEV void gateup_task(const Args& p, const LayerArgs& L, int e, int m, int n,
 }
 
 template <typename TE>
-ETC_DEV void down_task(const Args& p, const LayerArgs& L, int e, int m, int n2i, int s, int gpc,
+ETC_TASK void down_task(const Args& p, const LayerArgs& L, int e, int m, int n2i, int s, int gpc,
                        Smem& sm) {
-  using Tile = KTile<TE>;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  using Tile = KTile<TE, MNT>;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w / Tile::WN, wn = w % Tile::WN;
   const int H = p.H, F = p.F, K = p.K;
   TileSmem& Ts = sm.u.t;
   const int r0 = L.offsets[e] + m * BM;
   const int valid = min(BM, L.counts[e] - m * BM);
-  for (int i = tid; i < BM; i += NT) {
+  for (int i = tid; i < BM; i += MNT) {
     if (i < valid) {
       const int a = L.sorted_assign[r0 + i];
       Ts.row_tok[i] = a / K;
@@ -566,30 +615,30 @@ ETC_DEV void down_task(const Args& p, const LayerArgs& L, int e, int m, int n2i,
   const TE* hb = static_cast<const TE*>(p.hbuf);
   const TE* wd = static_cast<const TE*>(L.w_down);
   const char* rowp[Tile::LOADS];
-  const int row0 = tid >> 3, lc = Tile::load_chunk(tid) * 16;
+  const int lc = Tile::load_chunk(tid) * 16;
   // rows past the expert's count read the first row, columns past H read row H-1: their
   // results are never stored
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = row0 + 32 * i;
-    rowp[i] = reinterpret_cast<const char*>(hb + (size_t)(r0 + (r < valid ? r : 0)) * F + kb) + lc;
+  for (int i = 0; i < Tile::LOADS; ++i) {
+    const int r = Tile::load_row(tid, i);
+    if (i < Tile::ALOADS) {
+      rowp[i] = reinterpret_cast<const char*>(hb + (size_t)(r0 + (r < valid ? r : 0)) * F + kb) + lc;
+    } else {
+      const int h = min(n2i * BN2 + r - BM, H - 1);
+      rowp[i] = reinterpret_cast<const char*>(wd + ((size_t)e * H + h) * F + kb) + lc;
+    }
   }
-#pragma unroll
-  for (int i = 4; i < Tile::LOADS; ++i) {
-    const int h = min(n2i * BN2 + row0 + 32 * (i - 4), H - 1);
-    rowp[i] = reinterpret_cast<const char*>(wd + ((size_t)e * H + h) * F + kb) + lc;
-  }
-  f32x4 acc[4][8];
+  f32x4 acc[4][Tile::NJ];
   Tile::run(Ts.gemm, rowp, klen, valid, acc);
 
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < Tile::NJ; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-        const int col = n2i * BN2 + wn * 128 + j * 16 + (lane & 15);
+        const int col = n2i * BN2 + wn * Tile::WCOLS + j * 16 + (lane & 15);
         if (row < valid && col < H) {
           if (p.combine == ETC_COMBINE_ATOMIC)
             atomicAdd(p.out_acc + (size_t)Ts.row_tok[row] * H + col, Ts.row_gate[row] * acc[i][j][r]);
@@ -600,12 +649,12 @@ ETC_DEV void down_task(const Args& p, const LayerArgs& L, int e, int m, int n2i,
 }
 
 template <typename TE>
-ETC_DEV void finalize_task(const Args& p, const LayerArgs& L, int tau) {
+ETC_TASK void finalize_task(const Args& p, const LayerArgs& L, int tau) {
   constexpr int EPC = 16 / (int)sizeof(TE);
   const int tid = threadIdx.x, H = p.H, K = p.K;
   const int t0 = tau * BT, nt = tile_rows(p, tau);
   TE* out = static_cast<TE*>(L.out);
-  for (int c = tid; c < nt * H / EPC; c += NT) {
+  for (int c = tid; c < nt * H / EPC; c += MNT) {
     const int t = t0 + (c * EPC) / H, h = (c * EPC) % H;
     float v[EPC];
     if (p.combine == ETC_COMBINE_ATOMIC) {
@@ -746,7 +795,7 @@ ETC_DEV void push_many(const Args& p, Smem& sm, int n, Gen gen) {
   __syncthreads();
   const int base = sm.ibuf[0];
   fence_release_agent();
-  for (int i = threadIdx.x; i < n; i += NT) q_store_relaxed(p.queue + base + i, enc(gen(i)));
+  for (int i = threadIdx.x; i < n; i += MNT) q_store_relaxed(p.queue + base + i, enc(gen(i)));
   __syncthreads();
 }
 
@@ -857,9 +906,21 @@ ETC_DEV void run_task(const Args& p, const LayerArgs& L, const Task& t, Smem& sm
 }
 
 template <typename TE>
-__global__ __launch_bounds__(NT) void moe_kernel(Args p) {
+__global__ __launch_bounds__(MNT) void moe_kernel(Args pk) {
   __shared__ Smem sm;
+  // The task bodies are separate functions that take the arguments by reference; a
+  // reference to the kernel argument itself would make every lane copy it to scratch,
+  // so the workgroup copies it once into LDS and hands out references to that copy.
+  __shared__ Args p_lds;
   const int tid = threadIdx.x;
+  static_assert(sizeof(Args) % 4 == 0, "Args copies as words");
+  {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(&pk);
+    uint32_t* dst = reinterpret_cast<uint32_t*>(&p_lds);
+    for (int i = tid; i < (int)(sizeof(Args) / 4); i += MNT) dst[i] = src[i];
+  }
+  __syncthreads();
+  const Args& p = p_lds;
   const uint64_t deadline = now_ticks() + p.timeout_ticks;
 
   const bool tracing = (p.flags & ETC_FLAG_TRACE) != 0;
@@ -904,8 +965,8 @@ __global__ __launch_bounds__(NT) void moe_kernel(Args p) {
     for (int l = 0; l < p.L; ++l) {
       const LayerArgs& L = p.layer[l];
       if (tid == 0) { ev_store_relaxed(L.ev_route, 0); ev_store_relaxed(L.ev_scan, 0); }
-      for (int i = tid; i < p.max_rt * p.n1; i += NT) ev_store_relaxed(L.ev_gu + i, 0);
-      for (int i = tid; i < p.n_rt_cap; i += NT) {
+      for (int i = tid; i < p.max_rt * p.n1; i += MNT) ev_store_relaxed(L.ev_gu + i, 0);
+      for (int i = tid; i < p.n_rt_cap; i += MNT) {
         ev_store_relaxed(L.ev_comb + i, 0);
         ev_store_relaxed(L.ev_done + i, 0);
       }
@@ -982,8 +1043,8 @@ static int moe_occupancy(int dev, etc_dtype dt) {
   if (occ[dev][dt] == 0) {
     int v = 0;
     hipError_t e = (dt == ETC_DTYPE_BF16)
-                       ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, moe::moe_kernel<bf16>, NT, 0)
-                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, moe::moe_kernel<float>, NT, 0);
+                       ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, moe::moe_kernel<bf16>, moe::MNT, 0)
+                       : hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, moe::moe_kernel<float>, moe::MNT, 0);
     if (e != hipSuccess || v < 1) v = 1;
     occ[dev][dt] = v;
   }
@@ -1149,9 +1210,9 @@ ETC_API etc_status etc_moe_layer(int32_t T, int32_t H, int32_t E, int32_t K, int
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (dtype == ETC_DTYPE_BF16)
-    hipLaunchKernelGGL(moe::moe_kernel<bf16>, dim3(grid), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL(moe::moe_kernel<bf16>, dim3(grid), dim3(moe::MNT), 0, s, p);
   else
-    hipLaunchKernelGGL(moe::moe_kernel<float>, dim3(grid), dim3(NT), 0, s, p);
+    hipLaunchKernelGGL(moe::moe_kernel<float>, dim3(grid), dim3(moe::MNT), 0, s, p);
   return hipGetLastError() == hipSuccess ? ETC_OK : ETC_ERR_HIP;
 }
 

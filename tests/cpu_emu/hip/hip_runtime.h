@@ -141,6 +141,8 @@ inline void emu_global_load_lds(const void* src, void* lds_base, int size, int o
 #define __builtin_amdgcn_global_load_lds(src, dst, size, off, aux) \
   emu_global_load_lds((const void*)(src), (void*)(dst), (size), (off))
 #define __builtin_amdgcn_s_barrier() emu_syncthreads()
+#define __builtin_amdgcn_sched_barrier(mask) ((void)0)
+#define __builtin_amdgcn_sched_group_barrier(mask, n, id) ((void)0)
 
 emu_f32x4 emu_mfma_bf16(emu_bf16x8 a, emu_bf16x8 b, emu_f32x4 c);
 emu_f32x4 emu_mfma_f32(float a, float b, emu_f32x4 c);
