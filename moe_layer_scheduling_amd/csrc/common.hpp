@@ -85,6 +85,12 @@ ETC_DEV int ev_load_relaxed(const int* p) {
 ETC_DEV int ev_add(int* p, int v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
 }
+ETC_DEV int ev_add_acquire(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+ETC_DEV int ev_add_relaxed(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 ETC_DEV void ev_store(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -105,6 +111,36 @@ ETC_DEV void q_store_relaxed(long long* p, long long v) {
 }
 ETC_DEV void fence_release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
 ETC_DEV void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+// Shared results.  Every store of data that another workgroup reads after an event
+// goes through these: agent-scope atomic stores, which reach the point of coherence
+// of all XCDs by themselves.  An event then needs no release (on this GPU an
+// agent-scope release writes back the whole L2 of the XCD, several microseconds):
+// publish_shared() waits until this workgroup's stores have completed, and the signal
+// that follows is a relaxed atomic.  Readers still acquire (invalidating their L2), so
+// no stale line from an earlier call or layer is read.
+ETC_DEV void st_shared(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+ETC_DEV void st_shared(int* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+ETC_DEV void st_shared(float* p, float v) { st_shared(reinterpret_cast<uint32_t*>(p), __float_as_uint(v)); }
+ETC_DEV void st_shared8(void* p, uint64_t v) {
+  __hip_atomic_store(static_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16 bytes at a 16-byte aligned address, as two 8-byte stores
+ETC_DEV void st_shared16(void* p, const uint4& v) {
+  uint64_t* q = static_cast<uint64_t*>(p);
+  st_shared8(q, (uint64_t)v.x | ((uint64_t)v.y << 32));
+  st_shared8(q + 1, (uint64_t)v.z | ((uint64_t)v.w << 32));
+}
+// Every thread's stores have completed (so every shared result of the workgroup has
+// reached the point of coherence), then the workgroup meets.
+ETC_DEV void publish_shared() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // Direct copy of 16 bytes per lane from global memory into LDS (gfx950
 // global_load_lds_dwordx4): lane l of the wave writes lds_wave_base + 16 * l, so

@@ -318,7 +318,7 @@ ETC_TASK void route_task(const Args& p, const LayerArgs& L, int tau, Smem& sm) {
     const float r = R.rs[tt];
 #pragma unroll
     for (int i = 0; i < EPC; ++i) v[i] = v[i] * r * L.gamma[h + i];
-    *reinterpret_cast<uint4*>(xq + (size_t)(t0 + tt) * H + h) = pack16<TE>(v);
+    st_shared16(xq + (size_t)(t0 + tt) * H + h, pack16<TE>(v));
   }
 
   // 3. top-k by (logit desc, expert asc) with k rounds of a wave argmax; softmax over
@@ -368,8 +368,8 @@ ETC_TASK void route_task(const Args& p, const LayerArgs& L, int tau, Smem& sm) {
 #pragma unroll
       for (int j = 0; j < MAXK; ++j)
         if (j < K) {
-          L.topk_idx[t * K + j] = sele[j];
-          L.topk_w[t * K + j] = z[j] / zsum;
+          st_shared(L.topk_idx + t * K + j, sele[j]);
+          st_shared(L.topk_w + t * K + j, z[j] / zsum);
           R.sel[tt][j] = sele[j];
         }
     }
@@ -383,19 +383,19 @@ ETC_TASK void route_task(const Args& p, const LayerArgs& L, int tau, Smem& sm) {
     int rank = 0;
     for (int u = 0; u < tt; ++u)
       for (int jj = 0; jj < K; ++jj) rank += (R.sel[u][jj] == e);
-    L.lrank[(t0 + tt) * K + j] = rank;
+    st_shared(L.lrank + (t0 + tt) * K + j, rank);
   }
   for (int e = tid; e < E; e += MNT) {
     int c = 0;
     for (int u = 0; u < nt; ++u)
       for (int jj = 0; jj < K; ++jj) c += (R.sel[u][jj] == e);
-    L.hist[tau * E + e] = c;
+    st_shared(L.hist + tau * E + e, c);
   }
 
   // 5. clear this tile's accumulator rows for the atomic combine
   if (p.combine == ETC_COMBINE_ATOMIC) {
-    float4* acc = reinterpret_cast<float4*>(p.out_acc + (size_t)t0 * H);
-    for (int i = tid; i < nt * H / 4; i += MNT) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+    uint64_t* acc = reinterpret_cast<uint64_t*>(p.out_acc + (size_t)t0 * H);
+    for (int i = tid; i < nt * H / 2; i += MNT) st_shared8(acc + i, 0);
   }
 }
 
@@ -453,15 +453,15 @@ ETC_TASK void scan_task(const Args& p, const LayerArgs& L, int layer, Smem& sm) 
   if (tid < E) {
     S.off[tid] = off;
     S.rtb[tid] = rtb;
-    L.counts[tid] = cnt;
-    L.offsets[tid] = off;
-    L.rt_base[tid] = rtb;
+    st_shared(L.counts + tid, cnt);
+    st_shared(L.offsets + tid, off);
+    st_shared(L.rt_base + tid, rtb);
   }
   if (tid == 0) {
     S.off[E] = total_rows;
     S.rtb[E] = RT;
-    L.offsets[E] = total_rows;
-    L.rt_base[E] = RT;
+    st_shared(L.offsets + E, total_rows);
+    st_shared(L.rt_base + E, RT);
   }
   __syncthreads();
   // first sorted row of every (routing tile, expert) block: each thread continues the
@@ -476,7 +476,7 @@ ETC_TASK void scan_task(const Args& p, const LayerArgs& L, int layer, Smem& sm) 
 #pragma unroll
       for (int u = 0; u < 8; ++u)
         if (tau + u < tau1) {
-          L.tile_off[(tau + u) * E + e_t] = run;
+          st_shared(L.tile_off + (tau + u) * E + e_t, run);
           run += v[u];
         }
     }
@@ -493,15 +493,15 @@ ETC_TASK void scan_task(const Args& p, const LayerArgs& L, int layer, Smem& sm) 
     nS = cdiv(p.n1, gpc);
     const int ngu = RT * p.n1, nd = RT * p.n2 * nS, nf = n_rt;
     const int base = (layer == 0) ? 0 : p.layer[layer - 1].plan[PL_NEXTBASE];
-    L.plan[PL_RT] = RT;
-    L.plan[PL_NGU] = ngu;
-    L.plan[PL_ND] = nd;
-    L.plan[PL_NF] = nf;
-    L.plan[PL_NS] = nS;
-    L.plan[PL_GPC] = gpc;
-    L.plan[PL_NEXTBASE] = base + n_rt + 1 + ngu + nd + nf;
+    st_shared(L.plan + PL_RT, RT);
+    st_shared(L.plan + PL_NGU, ngu);
+    st_shared(L.plan + PL_ND, nd);
+    st_shared(L.plan + PL_NF, nf);
+    st_shared(L.plan + PL_NS, nS);
+    st_shared(L.plan + PL_GPC, gpc);
+    st_shared(L.plan + PL_NEXTBASE, base + n_rt + 1 + ngu + nd + nf);
   }
-  wg_publish();
+  publish_shared();
   fence_acquire_agent();  // tile_off written above by other lanes of this workgroup
 
   // scatter: pair a = t*k + j goes to row tile_off[tau][e] + rank; eight pairs per
@@ -525,8 +525,8 @@ ETC_TASK void scan_task(const Args& p, const LayerArgs& L, int layer, Smem& sm) 
       const int a = a0 + u * MNT;
       if (a < npairs) {
         const int r = to[u] + rk[u];
-        L.sorted_assign[r] = a;
-        L.pos[a] = r;
+        st_shared(L.sorted_assign + r, a);
+        st_shared(L.pos + a, r);
       }
     }
   }
@@ -570,9 +570,12 @@ ETC_TASK void gateup_task(const Args& p, const LayerArgs& L, int e, int m, int n
   f32x4 acc[4][Tile::NJ];
   Tile::run(Ts.gemm, rowp, H, valid, acc);
 
+  // SwiGLU into LDS (float, row stride BN1 + 1 words), then whole rows out to hbuf:
   // column block j of this wave is gate (j even) or up (j odd) for ffn columns
   // n*BN1 + (wn*NJ + j)/2 * 16 ..
-  TE* hb = static_cast<TE*>(p.hbuf);
+  constexpr int HSTR = BN1 + 1;
+  static_assert(BM * HSTR * 4 <= (int)sizeof(Ts.gemm), "staged tile fits the GEMM buffer");
+  float* hs = reinterpret_cast<float*>(Ts.gemm);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -580,12 +583,30 @@ ETC_TASK void gateup_task(const Args& p, const LayerArgs& L, int e, int m, int n
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-        const int f = n * BN1 + (wn * Tile::NJ / 2 + jj) * 16 + (lane & 15);
-        if (row < valid && f < F) {
-          const float g = acc[i][2 * jj][r], u = acc[i][2 * jj + 1][r];
-          Elem<TE>::store(hb, (size_t)(r0 + row) * F + f, g / (1.0f + expf(-g)) * u);
-        }
+        const int col = (wn * Tile::NJ / 2 + jj) * 16 + (lane & 15);
+        const float g = acc[i][2 * jj][r], u = acc[i][2 * jj + 1][r];
+        hs[row * HSTR + col] = g / (1.0f + expf(-g)) * u;
       }
+  __syncthreads();
+  // 8 bytes per store: 4 bf16 or 2 float columns (F is a multiple of 64, so a store never
+  // straddles the edge)
+  constexpr int CPS = 8 / (int)sizeof(TE), SPR = BN1 / CPS;  // columns per store, stores per row
+  TE* hb = static_cast<TE*>(p.hbuf);
+  const int f0 = n * BN1, ncols = min(BN1, F - f0);
+  for (int q = tid; q < valid * SPR; q += MNT) {
+    const int row = q / SPR, c = (q % SPR) * CPS;
+    if (c < ncols) {
+      const float* src = hs + row * HSTR + c;
+      uint64_t v;
+      if constexpr (sizeof(TE) == 2) {
+        v = (uint64_t)(f32_to_bf16_bits(src[0]) | (f32_to_bf16_bits(src[1]) << 16)) |
+            ((uint64_t)(f32_to_bf16_bits(src[2]) | (f32_to_bf16_bits(src[3]) << 16)) << 32);
+      } else {
+        v = (uint64_t)__float_as_uint(src[0]) | ((uint64_t)__float_as_uint(src[1]) << 32);
+      }
+      st_shared8(hb + (size_t)(r0 + row) * F + f0 + c, v);
+    }
+  }
 }
 
 template <typename TE>
@@ -631,21 +652,43 @@ ETC_TASK void down_task(const Args& p, const LayerArgs& L, int e, int m, int n2i
   f32x4 acc[4][Tile::NJ];
   Tile::run(Ts.gemm, rowp, klen, valid, acc);
 
+  // The tile goes through LDS first (row stride BN2 + 1 words: both passes free of bank
+  // conflicts; the LDS of the GEMM is free once Tile::run has returned), so that the
+  // results leave as whole rows: each atomic instruction adds 64 consecutive columns of
+  // one token row (two cache lines) rather than 16 columns of four different rows, and
+  // the ordered combine writes its rows with 8-byte stores.
+  constexpr int CSTR = BN2 + 1;
+  static_assert(BM * CSTR * 4 <= (int)sizeof(Ts.gemm), "staged tile fits the GEMM buffer");
+  float* ct = reinterpret_cast<float*>(Ts.gemm);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < Tile::NJ; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
-        const int col = n2i * BN2 + wn * Tile::WCOLS + j * 16 + (lane & 15);
-        if (row < valid && col < H) {
-          if (p.combine == ETC_COMBINE_ATOMIC)
-            atomicAdd(p.out_acc + (size_t)Ts.row_tok[row] * H + col, Ts.row_gate[row] * acc[i][j][r]);
-          else
-            p.ybuf[(size_t)(r0 + row) * H + col] = acc[i][j][r];
-        }
+      for (int r = 0; r < 4; ++r)
+        ct[(wm * 64 + i * 16 + (lane >> 4) * 4 + r) * CSTR + wn * Tile::WCOLS + j * 16 + (lane & 15)] =
+            acc[i][j][r];
+  __syncthreads();
+  const int c0 = n2i * BN2, ncols = min(BN2, H - c0);
+  if (p.combine == ETC_COMBINE_ATOMIC) {
+    for (int row = w; row < valid; row += NWAVE) {
+      float* dst = p.out_acc + (size_t)Ts.row_tok[row] * H + c0;
+      const float g = Ts.row_gate[row];
+#pragma unroll
+      for (int c = lane; c < BN2; c += 64)
+        if (c < ncols) atomicAdd(dst + c, g * ct[row * CSTR + c]);
+    }
+  } else {
+    // H is a multiple of 128: a pair of columns never straddles the edge
+    for (int q = tid; q < valid * (BN2 / 2); q += MNT) {
+      const int row = q / (BN2 / 2), c = (q % (BN2 / 2)) * 2;
+      if (c < ncols) {
+        const float* src = ct + row * CSTR + c;
+        st_shared8(p.ybuf + (size_t)(r0 + row) * H + c0 + c,
+                   (uint64_t)__float_as_uint(src[0]) | ((uint64_t)__float_as_uint(src[1]) << 32));
       }
+    }
+  }
 }
 
 template <typename TE>
@@ -676,7 +719,7 @@ ETC_TASK void finalize_task(const Args& p, const LayerArgs& L, int tau) {
         }
       }
     }
-    *reinterpret_cast<uint4*>(out + (size_t)t * H + h) = pack16<TE>(v);
+    st_shared16(out + (size_t)t * H + h, pack16<TE>(v));
   }
 }
 
@@ -794,22 +837,23 @@ ETC_DEV void push_many(const Args& p, Smem& sm, int n, Gen gen) {
   if (threadIdx.x == 0) sm.ibuf[0] = p.n_rt + atomicAdd(p.sched + W_QTAIL, n);
   __syncthreads();
   const int base = sm.ibuf[0];
-  fence_release_agent();
+  // the results these tasks read were published (publish_shared) before the call
   for (int i = threadIdx.x; i < n; i += MNT) q_store_relaxed(p.queue + base + i, enc(gen(i)));
   __syncthreads();
 }
 
+// The results the task reads were published (publish_shared) before the call.
 ETC_DEV void push_one(const Args& p, const Task& t) {
   const int slot = p.n_rt + atomicAdd(p.sched + W_QTAIL, 1);
-  q_store(p.queue + slot, enc(t));
+  q_store_relaxed(p.queue + slot, enc(t));
 }
 
 // After S: static mode publishes ev_scan; dynamic mode enqueues every gate/up task and
 // adds the layer's task count to the queue total.
 ETC_DEV void after_scan(const Args& p, int layer, Smem& sm) {
   const LayerArgs& L = p.layer[layer];
-  wg_publish();
-  if (threadIdx.x == 0) ev_store(L.ev_scan, 1);  // both modes: the event tensor is complete
+  publish_shared();
+  if (threadIdx.x == 0) ev_store_relaxed(L.ev_scan, 1);  // both modes: the event tensor is complete
   if (p.mode == ETC_SCHED_STATIC) return;
   const int RT = sm.u.s.rtb[p.E];
   const int n1 = p.n1;
@@ -822,7 +866,7 @@ ETC_DEV void after_scan(const Args& p, int layer, Smem& sm) {
     return t;
   });
   if (threadIdx.x == 0) {
-    // the plan words are in global memory, written by this thread before wg_publish
+    // the plan words are in global memory, written by this thread before publish_shared
     const int added = L.plan[PL_NGU] + L.plan[PL_ND] + L.plan[PL_NF] +
                       (layer + 1 < p.L ? p.n_rt : 0) + (layer == 0 ? p.n_rt : 0);
     atomicAdd(p.sched + W_QTOTAL, added);
@@ -837,9 +881,11 @@ ETC_DEV void run_task(const Args& p, const LayerArgs& L, const Task& t, Smem& sm
   const int tid = threadIdx.x;
   if (t.kind == K_R) {
     route_task<TE>(p, L, t.a, sm);
-    wg_publish();
+    publish_shared();
     if (tid == 0) {
-      const int old = ev_add(L.ev_route, 1);
+      // dynamic mode: the last arriver runs S, which reads every tile's results
+      const int old = (p.mode == ETC_SCHED_DYNAMIC) ? ev_add_acquire(L.ev_route, 1)
+                                                    : ev_add_relaxed(L.ev_route, 1);
       sm.flag = (p.mode == ETC_SCHED_DYNAMIC && old + 1 == p.n_rt) ? 1 : 0;
     }
     __syncthreads();
@@ -852,13 +898,14 @@ ETC_DEV void run_task(const Args& p, const LayerArgs& L, const Task& t, Smem& sm
     after_scan(p, t.layer, sm);
   } else if (t.kind == K_GU) {
     gateup_task<TE>(p, L, t.a, t.b, t.c, sm);
-    wg_publish();
+    publish_shared();
     const int gpc = L.plan[PL_GPC];
     const int s = t.c / gpc;
     if (tid == 0) {
       const int rt = L.rt_base[t.a] + t.b;
       const int need = min(gpc, p.n1 - s * gpc);
-      const int old = ev_add(L.ev_gu + rt * p.n1 + s, 1);
+      const int old = (p.mode == ETC_SCHED_DYNAMIC) ? ev_add_acquire(L.ev_gu + rt * p.n1 + s, 1)
+                                                    : ev_add_relaxed(L.ev_gu + rt * p.n1 + s, 1);
       sm.flag = (p.mode == ETC_SCHED_DYNAMIC && old + 1 == need) ? 1 : 0;
     }
     __syncthreads();
@@ -872,15 +919,19 @@ ETC_DEV void run_task(const Args& p, const LayerArgs& L, const Task& t, Smem& sm
     }
   } else if (t.kind == K_D) {
     down_task<TE>(p, L, t.a, t.b, t.c, t.d, L.plan[PL_GPC], sm);
-    wg_publish();
-    // one signal per run of rows in the same routing tile (rows are token-sorted)
+    // The results are published once for the whole task, then one signal goes out per
+    // run of rows in the same routing tile (rows are token-sorted; a tile's rows can
+    // span dozens of routing tiles).  In dynamic mode the signals acquire, for the last
+    // arriver that enqueues the finalize task.
+    publish_shared();
     const int valid = min(BM, L.counts[t.a] - t.b * BM);
     if (tid < valid) {
       const int tau = sm.u.t.row_tok[tid] / BT;
       if (tid == 0 || sm.u.t.row_tok[tid - 1] / BT != tau) {
         int len = 1;
         while (tid + len < valid && sm.u.t.row_tok[tid + len] / BT == tau) ++len;
-        const int old = ev_add(L.ev_comb + tau, len);
+        const int old = (p.mode == ETC_SCHED_DYNAMIC) ? ev_add_acquire(L.ev_comb + tau, len)
+                                                      : ev_add_relaxed(L.ev_comb + tau, len);
         const int target = tile_rows(p, tau) * p.K * p.n2 * L.plan[PL_NS];
         if (p.mode == ETC_SCHED_DYNAMIC && old + len == target) {
           Task f;
@@ -892,9 +943,9 @@ ETC_DEV void run_task(const Args& p, const LayerArgs& L, const Task& t, Smem& sm
     __syncthreads();
   } else if (t.kind == K_F) {
     finalize_task<TE>(p, L, t.a);
-    wg_publish();
+    publish_shared();
     if (tid == 0) {
-      ev_store(L.ev_done + t.a, 1);
+      ev_store_relaxed(L.ev_done + t.a, 1);
       if (p.mode == ETC_SCHED_DYNAMIC && t.layer + 1 < p.L) {
         Task r;
         r.kind = K_R; r.layer = t.layer + 1; r.a = t.a; r.b = r.c = r.d = 0;
