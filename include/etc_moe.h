@@ -161,11 +161,12 @@ size_t etc_moe_workspace_size(int32_t max_tokens, int32_t hidden, int32_t expert
  *   [3] ev_comb ([n_rt] int32)   [4] ev_done ([n_rt] int32)   [5] plan words (int32)
  *   [6] max_rt   [7] n1   [8] n_rt(max_tokens)   [9] rows per routing tile
  *   [10] rows per expert tile   [11] ffn columns per gate/up tile
- *   [12] hidden columns per down tile   [13] trace region   [14] trace records it holds.
+ *   [12] hidden columns per down tile   [13] trace region   [14] trace records it holds
+ *   [15] ev_perm (1 int32: routing tiles whose pairs are placed in the permutation).
  * The plan words are: [0] row tiles RT, [1] gate/up tasks, [2] down tasks,
  * [3] finalize tasks, [4] ffn chunks of the down projection nS, [5] gate/up tiles per
  * chunk, [6] first static ticket of the next layer. */
-#define ETC_LAYOUT_WORDS 15
+#define ETC_LAYOUT_WORDS 16
 etc_status etc_moe_workspace_layout(int32_t max_tokens, int32_t hidden, int32_t experts,
                                     int32_t top_k, int32_t ffn, int32_t num_layers,
                                     etc_dtype dtype, etc_combine combine, int32_t layer,

@@ -22,7 +22,7 @@ MODES = {"static": 0, "dynamic": 1}
 COMBINES = {"atomic": 0, "ordered": 1}
 FLAG_KEEP_COUNTERS = 0x1
 FLAG_TRACE = 0x2
-LAYOUT_WORDS = 15
+LAYOUT_WORDS = 16
 W_TRACE_LAST = 10  # control word holding the last traced call's record count
 
 

@@ -28,11 +28,11 @@ struct bf16 {
 ETC_DEV float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 // Round to nearest even; NaN stays NaN (quiet).
-ETC_DEV uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+// float -> bfloat16 bits, round to nearest even (gfx950 converts in hardware, two values
+// per v_cvt_pk_bf16_f32)
+ETC_DEV uint32_t f32_to_bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+ETC_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
 template <typename TE>

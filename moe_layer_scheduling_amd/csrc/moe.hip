@@ -17,19 +17,23 @@
 //                  (token, slot) pairs inside the tile and the tile's expert histogram
 //                  -> ev_route[l] += 1.  For l > 0 it waits ev_done[l-1][tau] >= 1.
 //   S              waits ev_route[l] >= n_rt: counts, exclusive scan, row tiles per
-//                  expert, permutation; sizes the down split (nS chunks of GPC gate/up
-//                  tiles) from the actual number of row tiles; -> ev_scan[l] = 1.
-//   GU(e, m, n)    gate/up tile of expert e rows m*128.. and ffn columns n*128..;
-//                  h = silu(G) * U -> ev_gu[l][rt(e,m)][n / GPC] += 1.
+//                  expert, first sorted row of every (routing tile, expert) block;
+//                  sizes the down split (nS chunks of GPC gate/up tiles) from the actual
+//                  number of row tiles; -> ev_scan[l] = 1.
+//   P(tau)         waits ev_scan[l] >= 1: places the (token, slot) pairs of routing
+//                  tile tau in the permutation -> ev_perm[l] += 1.
+//   GU(e, m, n)    waits ev_perm[l] >= n_rt: gate/up tile of expert e rows m*128.. and
+//                  ffn columns n*128..; h = silu(G) * U -> ev_gu[l][rt(e,m)][n / GPC] += 1.
 //   D(e, m, n2, s) down tile over ffn chunk s; waits ev_gu[l][rt][s] >= tiles in chunk s;
 //                  adds gate * y into the float32 accumulator (or stores y) ->
 //                  ev_comb[l][tau] += its rows in tau, per routing tile tau it touches.
 //   F(tau)         waits ev_comb[l][tau] >= rows(tau) * k * n2 * nS; writes the layer
 //                  output rows -> ev_done[l][tau] = 1.
-// Static mode: workgroups draw tickets of the order [R.. S GU.. D.. F..] per layer and
-// spin on each task's counter.  Dynamic mode: a queue of ready tasks; the R tasks of the
-// first layer are implicit in slots 0..n_rt-1, the last R runs S inline, S enqueues the
-// GU tasks, and whichever signal completes a counter enqueues the tasks it releases.
+// Static mode: workgroups draw tickets of the order [R.. S P.. GU.. D.. F..] per layer
+// and spin on each task's counter.  Dynamic mode: a queue of ready tasks; the R tasks of
+// the first layer are implicit in slots 0..n_rt-1, the last R runs S inline, S enqueues
+// the P tasks, the last P enqueues the GU tasks, and whichever signal completes a counter
+// enqueues the tasks it releases.
 // The token count T is a kernel argument; nothing in the code depends on its value.
 #include <float.h>
 #include <stdlib.h>
@@ -58,7 +62,7 @@ constexpr int MAX_TOKENS = 262143;  // task fields are 14 bits
 // inside the GEMM loop).  A call per task costs nothing next to the task itself.
 #define ETC_TASK __device__ __attribute__((noinline))
 
-enum Kind { K_NONE = 0, K_R = 1, K_S = 2, K_GU = 3, K_D = 4, K_F = 5 };
+enum Kind { K_NONE = 0, K_R = 1, K_S = 2, K_GU = 3, K_D = 4, K_F = 5, K_P = 6 };
 enum PlanWord { PL_RT = 0, PL_NGU, PL_ND, PL_NF, PL_NS, PL_GPC, PL_NEXTBASE, PL_WORDS = 8 };
 
 struct Task {
@@ -105,6 +109,7 @@ struct LayerArgs {
   int* plan;           // [PL_WORDS]
   int* ev_route;       // 1
   int* ev_scan;        // 1
+  int* ev_perm;        // 1
   int* ev_gu;          // [max_rt][n1]
   int* ev_comb;        // [n_rt]
   int* ev_done;        // [n_rt]
@@ -261,8 +266,11 @@ ETC_TASK void route_task(const Args& p, const LayerArgs& L, int tau, Smem& sm) {
   const int KS = NB >= NWAVE ? 1 : min(4, NWAVE / NB);  // K slices per expert block: 1, 2 or 4
   const int kslice = H / KS;           // a multiple of KSTEP (H is a multiple of 128)
   const int row = lane & 15, grp = lane >> 4;
-  const bool tok_ok = row < nt;
-  const TE* xrow = x + (size_t)(t0 + (tok_ok ? row : 0)) * H;
+  // Rows past the tile's tokens read the first token and columns past E read expert 0,
+  // so every load is unconditional; those results are never used.  Loads go out eight
+  // K steps at a time before any of them is consumed.
+  const TE* xrow = x + (size_t)(t0 + (row < nt ? row : 0)) * H;
+  constexpr int U = 8;
   for (int it = w; it < NB * KS; it += NWAVE) {
     const int nb = it / KS, ks = it % KS;
     const int e = nb * 16 + row;
@@ -273,16 +281,27 @@ ETC_TASK void route_task(const Args& p, const LayerArgs& L, int tau, Smem& sm) {
     for (int q = 0; q < 3; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     float ss = 0.f;
     const int kb = ks * kslice, ke = kb + kslice;
-#pragma unroll 4
-    for (int k0 = kb; k0 < ke; k0 += KSTEP) {
-      const int k = k0 + grp * EPC;
-      const uint4 xv = tok_ok ? *reinterpret_cast<const uint4*>(xrow + k) : zero4();
-      const uint4 wv = e_ok ? *reinterpret_cast<const uint4*>(wrow + k) : zero4();
-      float g[EPC];
-#pragma unroll
-      for (int i = 0; i < EPC; ++i) g[i] = L.gamma[k + i];
-      router_step<TE>(xv, wv, g, acc, ss);
-    }
+    auto steps = [&](int k0, auto nsteps) ETC_INLINE {
+      constexpr int N = decltype(nsteps)::value;
+      uint4 xv[N], wv[N];
+      float4 gv[N][EPC / 4];
+      static_for<N>([&](auto u) ETC_INLINE {
+        const int k = k0 + u * KSTEP + grp * EPC;
+        xv[u] = *reinterpret_cast<const uint4*>(xrow + k);
+        wv[u] = *reinterpret_cast<const uint4*>(wrow + k);
+        static_for<EPC / 4>([&](auto q) ETC_INLINE { gv[u][q] = *reinterpret_cast<const float4*>(L.gamma + k + 4 * q); });
+      });
+      static_for<N>([&](auto u) ETC_INLINE {
+        float g[EPC];
+        static_for<EPC / 4>([&](auto q) ETC_INLINE {
+          g[4 * q] = gv[u][q].x; g[4 * q + 1] = gv[u][q].y; g[4 * q + 2] = gv[u][q].z; g[4 * q + 3] = gv[u][q].w;
+        });
+        router_step<TE>(xv[u], wv[u], g, acc, ss);
+      });
+    };
+    int k0 = kb;
+    for (; k0 + U * KSTEP <= ke; k0 += U * KSTEP) steps(k0, std::integral_constant<int, U>{});
+    for (; k0 < ke; k0 += KSTEP) steps(k0, std::integral_constant<int, 1>{});
     const f32x4 sum = (acc[2] + acc[1]) + acc[0];
     if (e_ok) {
 #pragma unroll
@@ -309,16 +328,34 @@ ETC_TASK void route_task(const Args& p, const LayerArgs& L, int tau, Smem& sm) {
   }
   __syncthreads();
 
-  // 2. normalised rows in storage precision for the experts
-  const int cpr = H / EPC;
-  for (int c = tid; c < nt * cpr; c += MNT) {
-    const int tt = c / cpr, h = (c % cpr) * EPC;
-    float v[EPC];
-    expand16(*reinterpret_cast<const uint4*>(x + (size_t)(t0 + tt) * H + h), v, (const TE*)nullptr);
-    const float r = R.rs[tt];
-#pragma unroll
-    for (int i = 0; i < EPC; ++i) v[i] = v[i] * r * L.gamma[h + i];
-    st_shared16(xq + (size_t)(t0 + tt) * H + h, pack16<TE>(v));
+  // 2. normalised rows in storage precision for the experts, eight chunks per thread at
+  //    a time so their loads are in flight together
+  const int cpr = H / EPC, nchunks = nt * cpr;
+  for (int c0 = tid; c0 < nchunks; c0 += 8 * MNT) {
+    uint4 xv[8];
+    float4 gv[8][EPC / 4];
+    static_for<8>([&](auto u) ETC_INLINE {
+      const int c = min(c0 + u * MNT, nchunks - 1);
+      const int tt = c / cpr, h = (c % cpr) * EPC;
+      xv[u] = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + tt) * H + h);
+      static_for<EPC / 4>([&](auto q) ETC_INLINE { gv[u][q] = *reinterpret_cast<const float4*>(L.gamma + h + 4 * q); });
+    });
+    static_for<8>([&](auto u) ETC_INLINE {
+      const int c = c0 + u * MNT;
+      if (c < nchunks) {
+        const int tt = c / cpr, h = (c % cpr) * EPC;
+        float v[EPC];
+        expand16(xv[u], v, (const TE*)nullptr);
+        const float r = R.rs[tt];
+        static_for<EPC / 4>([&](auto q) ETC_INLINE {
+          v[4 * q] = v[4 * q] * r * gv[u][q].x;
+          v[4 * q + 1] = v[4 * q + 1] * r * gv[u][q].y;
+          v[4 * q + 2] = v[4 * q + 2] * r * gv[u][q].z;
+          v[4 * q + 3] = v[4 * q + 3] * r * gv[u][q].w;
+        });
+        st_shared16(xq + (size_t)(t0 + tt) * H + h, pack16<TE>(v));
+      }
+    });
   }
 
   // 3. top-k by (logit desc, expert asc) with k rounds of a wave argmax; softmax over
@@ -499,36 +536,21 @@ ETC_TASK void scan_task(const Args& p, const LayerArgs& L, int layer, Smem& sm) 
     st_shared(L.plan + PL_NF, nf);
     st_shared(L.plan + PL_NS, nS);
     st_shared(L.plan + PL_GPC, gpc);
-    st_shared(L.plan + PL_NEXTBASE, base + n_rt + 1 + ngu + nd + nf);
+    st_shared(L.plan + PL_NEXTBASE, base + n_rt + 1 + n_rt + ngu + nd + nf);
   }
-  publish_shared();
-  fence_acquire_agent();  // tile_off written above by other lanes of this workgroup
+}
 
-  // scatter: pair a = t*k + j goes to row tile_off[tau][e] + rank; eight pairs per
-  // thread at a time, so their loads are in flight together
-  const int npairs = p.T * K;
-  for (int a0 = tid; a0 < npairs; a0 += 8 * MNT) {
-    int e[8], rk[8], to[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int a = min(a0 + u * MNT, npairs - 1);
-      e[u] = L.topk_idx[a];
-      rk[u] = L.lrank[a];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int a = min(a0 + u * MNT, npairs - 1);
-      to[u] = L.tile_off[(a / K / BT) * E + e[u]];
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int a = a0 + u * MNT;
-      if (a < npairs) {
-        const int r = to[u] + rk[u];
-        st_shared(L.sorted_assign + r, a);
-        st_shared(L.pos + a, r);
-      }
-    }
+// P(tau): the (token, slot) pairs of routing tile tau go to their rows of the
+// permutation: pair a = t*k + j of expert e lands at tile_off[tau][e] + its rank among
+// the tile's pairs of e (tokens ascending), so each expert's rows stay in token order.
+ETC_TASK void perm_task(const Args& p, const LayerArgs& L, int tau) {
+  const int K = p.K, E = p.E;
+  const int a0 = tau * BT * K, npairs = tile_rows(p, tau) * K;
+  for (int i = threadIdx.x; i < npairs; i += MNT) {
+    const int a = a0 + i;
+    const int r = L.tile_off[tau * E + L.topk_idx[a]] + L.lrank[a];
+    st_shared(L.sorted_assign + r, a);
+    st_shared(L.pos + a, r);
   }
 }
 
@@ -752,8 +774,10 @@ ETC_DEV bool claim_static(const Args& p, Task& t, uint64_t deadline) {
     t.layer = l;
     if (ticket < base + p.n_rt) { t.kind = K_R; t.a = ticket - base; return true; }
     if (ticket == base + p.n_rt) { t.kind = K_S; return true; }
-    if (!spin_until_geq(L.ev_scan, 1, p.sched, deadline, 10 + l)) return false;
     int off = ticket - base - p.n_rt - 1;
+    if (off < p.n_rt) { t.kind = K_P; t.a = off; return true; }
+    off -= p.n_rt;
+    if (!spin_until_geq(L.ev_scan, 1, p.sched, deadline, 10 + l)) return false;
     const int ngu = L.plan[PL_NGU], nd = L.plan[PL_ND], nf = L.plan[PL_NF], nS = L.plan[PL_NS];
     if (off < ngu) {
       const int e = owner_expert(L.rt_base, p.E, off, p.n1);
@@ -816,6 +840,10 @@ ETC_DEV bool wait_deps(const Args& p, const Task& t, uint64_t deadline) {
       return spin_until_geq(p.layer[t.layer - 1].ev_done + t.a, 1, p.sched, deadline, 20);
     case K_S:
       return spin_until_geq(L.ev_route, p.n_rt, p.sched, deadline, 21);
+    case K_P:
+      return spin_until_geq(L.ev_scan, 1, p.sched, deadline, 24);
+    case K_GU:
+      return spin_until_geq(L.ev_perm, p.n_rt, p.sched, deadline, 25);
     case K_D: {
       const int gpc = L.plan[PL_GPC];
       const int rt = L.rt_base[t.a] + t.b;
@@ -848,26 +876,21 @@ ETC_DEV void push_one(const Args& p, const Task& t) {
   q_store_relaxed(p.queue + slot, enc(t));
 }
 
-// After S: static mode publishes ev_scan; dynamic mode enqueues every gate/up task and
-// adds the layer's task count to the queue total.
+// After S: static mode publishes ev_scan; dynamic mode enqueues every permutation task
+// and adds the layer's task count to the queue total.
 ETC_DEV void after_scan(const Args& p, int layer, Smem& sm) {
   const LayerArgs& L = p.layer[layer];
   publish_shared();
   if (threadIdx.x == 0) ev_store_relaxed(L.ev_scan, 1);  // both modes: the event tensor is complete
   if (p.mode == ETC_SCHED_STATIC) return;
-  const int RT = sm.u.s.rtb[p.E];
-  const int n1 = p.n1;
-  push_many(p, sm, RT * n1, [&](int i) {
-    const int e = owner_expert(sm.u.s.rtb, p.E, i, n1);
-    const int me = sm.u.s.rtb[e + 1] - sm.u.s.rtb[e];
-    const int loc = i - sm.u.s.rtb[e] * n1;
+  push_many(p, sm, p.n_rt, [&](int i) {
     Task t;
-    t.kind = K_GU; t.layer = layer; t.a = e; t.b = loc % me; t.c = loc / me; t.d = 0;
+    t.kind = K_P; t.layer = layer; t.a = i; t.b = t.c = t.d = 0;
     return t;
   });
   if (threadIdx.x == 0) {
     // the plan words are in global memory, written by this thread before publish_shared
-    const int added = L.plan[PL_NGU] + L.plan[PL_ND] + L.plan[PL_NF] +
+    const int added = p.n_rt + L.plan[PL_NGU] + L.plan[PL_ND] + L.plan[PL_NF] +
                       (layer + 1 < p.L ? p.n_rt : 0) + (layer == 0 ? p.n_rt : 0);
     atomicAdd(p.sched + W_QTOTAL, added);
     ev_add(p.sched + W_PLANNED, 1);
@@ -896,6 +919,26 @@ ETC_DEV void run_task(const Args& p, const LayerArgs& L, const Task& t, Smem& sm
   } else if (t.kind == K_S) {
     scan_task(p, L, t.layer, sm);
     after_scan(p, t.layer, sm);
+  } else if (t.kind == K_P) {
+    perm_task(p, L, t.a);
+    publish_shared();
+    if (tid == 0) {
+      const int old = (p.mode == ETC_SCHED_DYNAMIC) ? ev_add_acquire(L.ev_perm, 1)
+                                                    : ev_add_relaxed(L.ev_perm, 1);
+      sm.flag = (p.mode == ETC_SCHED_DYNAMIC && old + 1 == p.n_rt) ? 1 : 0;
+    }
+    __syncthreads();
+    if (sm.flag) {  // the permutation is complete: every gate/up task is ready
+      const int layer = t.layer, n1 = p.n1, E = p.E;
+      push_many(p, sm, L.plan[PL_NGU], [&](int i) {
+        const int e = owner_expert(L.rt_base, E, i, n1);
+        const int me = L.rt_base[e + 1] - L.rt_base[e];
+        const int loc = i - L.rt_base[e] * n1;
+        Task g;
+        g.kind = K_GU; g.layer = layer; g.a = e; g.b = loc % me; g.c = loc / me; g.d = 0;
+        return g;
+      });
+    }
   } else if (t.kind == K_GU) {
     gateup_task<TE>(p, L, t.a, t.b, t.c, sm);
     publish_shared();
@@ -1015,7 +1058,11 @@ __global__ __launch_bounds__(MNT) void moe_kernel(Args pk) {
   if (sm.flag && !(p.flags & ETC_FLAG_KEEP_COUNTERS)) {
     for (int l = 0; l < p.L; ++l) {
       const LayerArgs& L = p.layer[l];
-      if (tid == 0) { ev_store_relaxed(L.ev_route, 0); ev_store_relaxed(L.ev_scan, 0); }
+      if (tid == 0) {
+        ev_store_relaxed(L.ev_route, 0);
+        ev_store_relaxed(L.ev_scan, 0);
+        ev_store_relaxed(L.ev_perm, 0);
+      }
       for (int i = tid; i < p.max_rt * p.n1; i += MNT) ev_store_relaxed(L.ev_gu + i, 0);
       for (int i = tid; i < p.n_rt_cap; i += MNT) {
         ev_store_relaxed(L.ev_comb + i, 0);
@@ -1035,7 +1082,7 @@ struct Layout {
   size_t sched, queue, trace, xq, hbuf, out_acc, ybuf, act, total;
   struct {
     size_t topk_idx, topk_w, lrank, hist, tile_off, counts, offsets, rt_base, sorted_assign, pos,
-        plan, ev_route, ev_scan, ev_gu, ev_comb, ev_done;
+        plan, ev_route, ev_scan, ev_perm, ev_gu, ev_comb, ev_done;
   } l[MAXL];
   int n_rt, max_rt, n1, n2, queue_len;
 };
@@ -1051,12 +1098,13 @@ inline Layout layout(int Tm, int H, int E, int K, int F, int nl, int es, bool or
   for (int l = 0; l < nl; ++l) {  // counters first: the control region
     Y.l[l].ev_route = c.take(sizeof(int));
     Y.l[l].ev_scan = c.take(sizeof(int));
+    Y.l[l].ev_perm = c.take(sizeof(int));
     Y.l[l].ev_gu = c.take((size_t)Y.max_rt * Y.n1 * sizeof(int));
     Y.l[l].ev_comb = c.take((size_t)Y.n_rt * sizeof(int));
     Y.l[l].ev_done = c.take((size_t)Y.n_rt * sizeof(int));
     Y.l[l].plan = c.take(PL_WORDS * sizeof(int));
   }
-  const long per_layer = (long)Y.n_rt * 3 + (long)Y.max_rt * Y.n1 + 2L * MAX_WORKERS +
+  const long per_layer = (long)Y.n_rt * 4 + (long)Y.max_rt * Y.n1 + 2L * MAX_WORKERS +
                          (long)Y.max_rt * Y.n2 + 64;
   // + room for the one extra slot each worker draws before it sees the end
   Y.queue_len = (int)(Y.n_rt + per_layer * nl + MAX_WORKERS);
@@ -1147,6 +1195,7 @@ ETC_API etc_status etc_moe_workspace_layout(int32_t max_tokens, int32_t hidden, 
   out[12] = moe::BN2;
   out[13] = (int64_t)Y.trace;
   out[14] = Y.queue_len;
+  out[15] = (int64_t)Y.l[layer].ev_perm;
   return ETC_OK;
 }
 
@@ -1254,6 +1303,7 @@ ETC_API etc_status etc_moe_layer(int32_t T, int32_t H, int32_t E, int32_t K, int
     L.plan = reinterpret_cast<int*>(ws + Y.l[l].plan);
     L.ev_route = reinterpret_cast<int*>(ws + Y.l[l].ev_route);
     L.ev_scan = reinterpret_cast<int*>(ws + Y.l[l].ev_scan);
+    L.ev_perm = reinterpret_cast<int*>(ws + Y.l[l].ev_perm);
     L.ev_gu = reinterpret_cast<int*>(ws + Y.l[l].ev_gu);
     L.ev_comb = reinterpret_cast<int*>(ws + Y.l[l].ev_comb);
     L.ev_done = reinterpret_cast<int*>(ws + Y.l[l].ev_done);

@@ -8,7 +8,7 @@ import json
 
 import numpy as np
 
-KINDS = {1: "R", 2: "S", 3: "GU", 4: "D", 5: "F"}
+KINDS = {1: "R", 2: "S", 3: "GU", 4: "D", 5: "F", 6: "P"}
 TICK_US = 0.01  # 100 MHz
 
 

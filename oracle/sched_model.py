@@ -16,21 +16,23 @@ down projection split along ffn into chunks of GPC gate/up tiles:
 
   R(tau)          routing tile tau                      waits  done[l-1][tau] >= 1 (l > 0)
                                                         signals route[l] += 1
-  S               counts, scan, permutation             waits  route[l] >= n_rt
+  S               counts, scans, per-tile row offsets   waits  route[l] >= n_rt
                                                         signals scan[l] = 1
-  GU(e, m, n)     gate/up tile                          waits  scan[l] >= 1
+  P(tau)          permutation scatter of tile tau       waits  scan[l] >= 1
+                                                        signals perm[l] += 1
+  GU(e, m, n)     gate/up tile                          waits  perm[l] >= n_rt
                                                         signals gu[l][e,m][n // GPC] += 1
   D(e, m, n2, s)  down tile over ffn chunk s            waits  gu[l][e,m][s] >= tiles in chunk s
                                                         signals comb[l][tau] += rows of (e,m) in tau
   F(tau)          finalize the output rows of tau       waits  comb[l][tau] >= |tau| * k * n2 * nS
                                                         signals done[l][tau] += 1
 
-Static mode runs the tasks in one fixed ticket order (per layer: all R, S, all GU,
-all D, all F) and each worker spins on the dependencies of the task it drew.
+Static mode runs the tasks in one fixed ticket order (per layer: all R, S, all P, all
+GU, all D, all F) and each worker spins on the dependencies of the task it drew.
 Dynamic mode keeps a FIFO ready queue: the R tasks of the first layer are queued at
 the start; the worker whose signal completes a counter (the last arriver) makes the
-dependents ready -- S runs inline after the last R, S queues every GU task, a full
-gu chunk queues its D tasks, a full comb tile queues its F, and F queues the next
+dependents ready -- S runs inline after the last R, S queues every P task, the last P
+queues every GU task, a full gu chunk queues its D tasks, a full comb tile queues its F, and F queues the next
 layer's R for the same tokens.
 """
 
@@ -82,10 +84,11 @@ def build_layer(l, T, H, F, k, counts, plan, tokens_of_rows):
         waits = [(("done", l - 1, tau), 1)] if l > 0 else []
         R.append(Task("R", l, (tau,), waits, [(("route", l), 1)]))
     S = Task("S", l, (), [(("route", l), n_rt)], [(("scan", l), 1)])
+    P = [Task("P", l, (tau,), [(("scan", l), 1)], [(("perm", l), 1)]) for tau in range(n_rt)]
     for e, c in enumerate(counts):
         for m in range(cdiv(int(c), plan.BM)):
             for n in range(n1):
-                GU.append(Task("GU", l, (e, m, n), [(("scan", l), 1)],
+                GU.append(Task("GU", l, (e, m, n), [(("perm", l), n_rt)],
                                [(("gu", l, e, m, n // plan.GPC), 1)]))
     for e, c in enumerate(counts):
         for m in range(cdiv(int(c), plan.BM)):
@@ -101,11 +104,11 @@ def build_layer(l, T, H, F, k, counts, plan, tokens_of_rows):
     for tau in range(n_rt):
         target = tile_rows[tau] * k * n2 * nS
         Fin.append(Task("F", l, (tau,), [(("comb", l, tau), target)], [(("done", l, tau), 1)]))
-    return R, S, GU, D, Fin
+    return R, S, P, GU, D, Fin
 
 
 def build_graph(T, H, F, k, layer_counts, layer_tokens_of_rows, plan):
-    """All layers, each as (R, S, GU, D, F) lists."""
+    """All layers, each as (R, S, P, GU, D, F) lists."""
     return [build_layer(l, T, H, F, k, c, plan, tr)
             for l, (c, tr) in enumerate(zip(layer_counts, layer_tokens_of_rows))]
 
@@ -113,8 +116,8 @@ def build_graph(T, H, F, k, layer_counts, layer_tokens_of_rows, plan):
 def expected_final_counters(graph):
     """Every counter's value once all tasks have signalled."""
     final = {}
-    for R, S, GU, D, Fin in graph:
-        for t in R + [S] + GU + D + Fin:
+    for R, S, P, GU, D, Fin in graph:
+        for t in R + [S] + P + GU + D + Fin:
             for ctr, amt in t.signals:
                 final[ctr] = final.get(ctr, 0) + amt
     return final
@@ -122,8 +125,8 @@ def expected_final_counters(graph):
 
 def static_order(graph):
     order = []
-    for R, S, GU, D, Fin in graph:
-        order += R + [S] + GU + D + Fin
+    for R, S, P, GU, D, Fin in graph:
+        order += R + [S] + P + GU + D + Fin
     return order
 
 
@@ -184,11 +187,12 @@ def simulate_dynamic(graph, workers, rng=None):
     queue = list(graph[0][0])  # R tasks of the first layer
     running = []
     # lookups of the dependents that a completed counter releases
-    gu_by_layer = [g[2] for g in graph]
+    p_by_layer = [g[2] for g in graph]
+    gu_by_layer = [g[3] for g in graph]
     d_by_chunk = []
     f_by_tau = []
     r_by_tau = []
-    for R, S, GU, D, Fin in graph:
+    for R, S, P, GU, D, Fin in graph:
         dd = {}
         for t in D:
             e, m, _, s = t.key
@@ -196,7 +200,7 @@ def simulate_dynamic(graph, workers, rng=None):
         d_by_chunk.append(dd)
         f_by_tau.append({t.key[0]: t for t in Fin})
         r_by_tau.append({t.key[0]: t for t in R})
-    total = sum(len(R) + len(GU) + len(D) + len(Fin) + 1 for R, S, GU, D, Fin in graph)
+    total = sum(len(R) + len(P) + len(GU) + len(D) + len(Fin) + 1 for R, S, P, GU, D, Fin in graph)
     while len(executed) < total:
         while queue and len(running) < workers:
             running.append(queue.pop(0))
@@ -209,7 +213,7 @@ def simulate_dynamic(graph, workers, rng=None):
         _signal(t, counters)
         executed.append(t)
         l = t.layer
-        R, S, GU, D, Fin = graph[l]
+        R, S, P, GU, D, Fin = graph[l]
         for ctr, amt in t.signals:
             old, new = before.get(ctr, 0), counters[ctr]
             kind = ctr[0]
@@ -218,6 +222,8 @@ def simulate_dynamic(graph, workers, rng=None):
                 assert _ready(S, counters)
                 _signal(S, counters)
                 executed.append(S)
+                queue.extend(p_by_layer[l])
+            elif kind == "perm" and new == len(P) and old < new:
                 queue.extend(gu_by_layer[l])
             elif kind == "gu":
                 _, _, e, m, s = ctr
@@ -245,7 +251,7 @@ def check_execution(executed, graph):
         if not _ready(t, counters):
             raise AssertionError(f"{ident} ran before its dependencies")
         _signal(t, counters)
-    n = sum(len(R) + 1 + len(GU) + len(D) + len(Fin) for R, S, GU, D, Fin in graph)
+    n = sum(len(R) + 1 + len(P) + len(GU) + len(D) + len(Fin) for R, S, P, GU, D, Fin in graph)
     if len(seen) != n:
         raise AssertionError(f"{len(seen)} of {n} tasks ran")
     return counters

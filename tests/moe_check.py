@@ -133,6 +133,7 @@ def check_event_tensor(read_i32, layout, T, H, F, k, E, gpu, layers):
         assert ngu == RT * n1 and nd == RT * n2 * nS and nf == n_rt
         assert int(read_i32(lay[0], 1)[0]) == final[("route", 0)]
         assert int(read_i32(lay[1], 1)[0]) == 1
+        assert int(read_i32(lay[15], 1)[0]) == final[("perm", 0)] == n_rt
         ev_gu = np.asarray(read_i32(lay[2], max_rt * n1)).reshape(max_rt, n1)
         rt = 0
         for e in range(E):

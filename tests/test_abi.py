@@ -78,7 +78,7 @@ def test_layout_offsets_inside_workspace(lib):
     for layer in range(2):
         assert lib.etc_moe_workspace_layout(4096, 4096, 64, 6, 1408, 2, 1, 0, layer, out) == 0
         offs = list(out)
-        assert all(0 < o < n and o % 4 == 0 for o in offs[:6] + [offs[13]])
+        assert all(0 < o < n and o % 4 == 0 for o in offs[:6] + [offs[13], offs[15]])
         assert offs[14] > 0 and offs[13] + 32 * offs[14] <= n
         assert offs[6] == 4096 * 6 // 128 + 64  # row-tile capacity
         bn1 = offs[11]

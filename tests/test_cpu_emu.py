@@ -134,8 +134,8 @@ def test_trace_has_one_record_per_task(lib, mode):
     for l in range(2):
         plan = np.array((ctypes.c_int32 * 8).from_address(g["wptr"] + lib_layout(lib, T, cfg, l)[5]))
         kinds = d["kind"][d["layer"] == l]
-        got = {k: int((kinds == k).sum()) for k in range(1, 6)}
-        want = {1: n_rt, 3: int(plan[1]), 4: int(plan[2]), 5: int(plan[3])}
+        got = {k: int((kinds == k).sum()) for k in range(1, 7)}
+        want = {1: n_rt, 3: int(plan[1]), 4: int(plan[2]), 5: int(plan[3]), 6: n_rt}
         # the scan runs as its own task in static mode and inside the last routing
         # task in dynamic mode
         want[2] = 1 if mode == "static" else 0

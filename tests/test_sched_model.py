@@ -104,8 +104,8 @@ def test_targets_equal_final_counts(T, H, F, E, k, L, plan):
     idx = [_random_idx(rng, T, E, k) for _ in range(L)]
     graph = _graph_from_routing(T, H, F, k, E, idx, plan)
     final = sm.expected_final_counters(graph)
-    for R, S, GU, D, Fin in graph:
-        for t in R + [S] + GU + D + Fin:
+    for R, S, P, GU, D, Fin in graph:
+        for t in R + [S] + P + GU + D + Fin:
             for ctr, tgt in t.waits:
                 if t.kind == "R":
                     assert final[ctr] == tgt  # one F per routing tile
@@ -124,7 +124,7 @@ def test_dropped_signal_detected():
     plan = sm.Plan(BT=8, BM=16, BN1=32, BN2=64, GPC=2)
     idx = [_random_idx(rng, 24, 8, 2)]
     graph = _graph_from_routing(24, 128, 128, 2, 8, idx, plan)
-    R, S, GU, D, Fin = graph[0]
+    R, S, P, GU, D, Fin = graph[0]
     GU[5].signals = []  # planted mistake: one gate/up tile never signals
     with pytest.raises(RuntimeError, match="deadlocked"):
         sm.simulate_static(graph, 4)
