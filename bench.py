@@ -35,6 +35,7 @@ sys.path.insert(0, ROOT)
 from moe_layer_scheduling_amd import binding, synth  # noqa: E402
 
 METRIC = "MoE layer tokens/sec + % of roofline (HBM GB/s decode, MFMA TFLOP/s prefill)"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_kernel_hbm_traffic.txt")
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 
@@ -191,6 +192,39 @@ def bench_splitk(steps, warmup, mode="static", copies=4):
             "mode": mode}
 
 
+def source_hash():
+    """sha256 over the HIP sources of the library (names and contents, sorted): the
+    identity of the kernels that counter measurements belong to."""
+    import glob
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "moe_layer_scheduling_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*"))):
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(key):
+    """HBM bytes per launch of the MoE kernel for workload `key`, from the committed
+    rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, scaled by the plain-copy
+    calibration); None when there is none or when the kernel sources have changed since
+    the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+        start = text.index("BEGIN-JSON") + len("BEGIN-JSON")
+        data = json.loads(text[start:text.index("END-JSON")])
+    except (OSError, ValueError):
+        return None
+    if data.get("source_sha256") != source_hash():
+        return None
+    entry = data.get("per_launch", {}).get(key)
+    return None if entry is None else int(entry["fetch_bytes"] + entry["write_bytes"])
+
+
 def copy_calibration(nbytes=1 << 30, reps=3):
     """A plain device copy of known size (one elementwise kernel reading nbytes and writing
     nbytes per call): the reference against which the L2 fetch/write byte counters of the
@@ -219,12 +253,19 @@ def main():
                     help="also run one traced call and write a Chrome trace here")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB elementwise copy (counter calibration)")
+    ap.add_argument("--splitk-only", action="store_true",
+                    help="only time the split-K GEMM (for per-kernel profiles)")
+    ap.add_argument("--source-hash", action="store_true",
+                    help="print the hash that identifies the kernel sources and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.source_hash:
+        print(source_hash())
+        return
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
@@ -232,18 +273,23 @@ def main():
         print(json.dumps(copy_calibration()), flush=True)
         return
     binding.load_library()
+    if args.splitk_only:
+        res = {m: bench_splitk(args.steps, args.warmup, m) for m in ("static", "dynamic")}
+        print(json.dumps({"splitk": res}), flush=True)
+        return
 
     cfg = synth.CONFIGS[args.workload]
     T = args.tokens or cfg.tokens[-1]
     head = bench_moe(cfg, T, args.steps, args.warmup, args.mode, args.combine, with_cpu=args.cpu,
                      trace_out=args.trace_out)
     mfma_bound = args.workload in ("prefill", "tiny")
+    traffic = measured_traffic(f"{cfg.name}_T{T}")
     if mfma_bound:
         roof = {"bound": "mfma", "achieved": head["tflops_bf16"], "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": head["mfma_frac"], "traffic": None}
+                "unit": "TFLOP/s", "frac": head["mfma_frac"], "traffic": traffic}
     else:
         roof = {"bound": "hbm", "achieved": head["gbs_alg"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": head["hbm_frac"], "traffic": None}
+                "frac": head["hbm_frac"], "traffic": traffic}
     roof["kernel"] = "etc::moe::moe_kernel<bf16>" if cfg.dtype == "bf16" else "etc::moe::moe_kernel<float>"
     roof["per_launch"] = {"flops_bf16": head["flops_bf16"], "flops_router_fp32": head["flops_router_fp32"],
                           "bytes_alg": head["bytes_alg"], "launch_ms": head["launch_ms"]}

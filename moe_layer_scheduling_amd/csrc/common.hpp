@@ -8,6 +8,7 @@
 #include <stdint.h>
 
 #define ETC_DEV __device__ __forceinline__
+#define ETC_INLINE __attribute__((always_inline))  // for lambdas
 
 namespace etc {
 
@@ -201,6 +202,23 @@ enum SchedWord {
   W_NWORDS = 32
 };
 constexpr int MAX_XCD_QUEUES = 8;  // MI355X: 8 XCDs of 32 CUs, each with its own L2
+
+// Static tickets through per-XCD queues (thread 0 of a workgroup calls this).  A fixed
+// task order is cut into chunks of G = workers / Q consecutive tasks, chunk c belonging
+// to queue c mod Q (Q = min(8, workers)); workgroup b draws the next ticket of queue
+// b mod Q.  The dispatcher places workgroup b on XCD b mod 8, so with Q = 8 each chunk
+// runs on one XCD and tasks that are adjacent in the order share that XCD's L2.  Each
+// queue hands out its tickets in the global order and has at least one workgroup, so a
+// waiting task's producers, which come earlier in the order, are always claimed by
+// workgroups that can run them: the order stays deadlock-free.
+ETC_DEV int xcd_ticket(int* sched) {
+  const int nwg = (int)gridDim.x;
+  const int Q = nwg < MAX_XCD_QUEUES ? nwg : MAX_XCD_QUEUES;
+  const int G = nwg / Q;
+  const int q = (int)blockIdx.x % Q;
+  const int i = atomicAdd(sched + W_XTICKET + q, 1);
+  return ((i / G) * Q + q) * G + i % G;
+}
 
 // Waits poll with relaxed loads (no cache invalidation per poll: an agent-scope acquire
 // invalidates this CU's L1 and the XCD's L2 lines, which would keep evicting the operands

@@ -45,8 +45,6 @@
 
 namespace etc {
 
-#define ETC_INLINE __attribute__((always_inline))
-
 template <typename F, int... I>
 ETC_DEV void static_for_impl(F& f, std::integer_sequence<int, I...>) {
   (f(std::integral_constant<int, I>{}), ...);

@@ -757,14 +757,7 @@ ETC_TASK void finalize_task(const Args& p, const LayerArgs& L, int tau) {
 // Each queue hands out its tasks in the global order and has at least one workgroup
 // (Q <= workers), so the smallest waiting task always has its inputs claimed by
 // workgroups that are not waiting on it: the order stays deadlock-free.
-ETC_DEV int static_ticket(const Args& p) {
-  const int nwg = (int)gridDim.x;
-  const int Q = nwg < MAX_XCD_QUEUES ? nwg : MAX_XCD_QUEUES;
-  const int G = nwg / Q;
-  const int q = (int)blockIdx.x % Q;
-  const int i = atomicAdd(p.sched + W_XTICKET + q, 1);
-  return ((i / G) * Q + q) * G + i % G;
-}
+ETC_DEV int static_ticket(const Args& p) { return xcd_ticket(p.sched); }
 
 ETC_DEV bool claim_static(const Args& p, Task& t, uint64_t deadline) {
   const int ticket = static_ticket(p);

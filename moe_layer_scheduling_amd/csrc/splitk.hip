@@ -17,10 +17,14 @@
 // mode: only partial tasks are handed out; the partial whose add returns S-1 runs the
 // reduction itself (last arriver).
 //
-// B is [K][N] (N-contiguous) while the MFMA wants 8 consecutive k per lane, so the B
-// stage keeps LDS rows of N (one per k) padded to 132 elements and each lane gathers
-// its 8 k values with 2-byte reads; the 4 k-groups of a quarter-wave then start 16
-// banks apart and do not conflict.
+// Operands go from global memory straight into LDS (16 bytes per lane per copy) through
+// a ring of four stages of 64 k values: the copies run three stages ahead of the MFMAs,
+// which is what keeps enough bytes in flight to stream B from HBM.  A stage holds the
+// A block [64 rows][64 k] (rows of 128 bytes, chunks swizzled as in mfma.hpp) and the B
+// block [64 k][128 n] (rows of 256 bytes).  B is N-contiguous while the MFMA wants 8
+// consecutive k per lane, so each lane gathers its 8 values with 2-byte LDS reads; the
+// 16-byte chunk c of B row r sits at position c ^ ((r / 8) % 16), which puts the four
+// k groups of a quarter-wave in different banks.
 #include "common.hpp"
 #include "host.hpp"
 #include "mfma.hpp"
@@ -29,12 +33,13 @@ namespace etc {
 namespace splitk {
 
 constexpr int TM = 64, TN = 128, BK = 64;
-constexpr int BSTRIDE = TN + 4;                      // elements per LDS row of B
 constexpr int A_STAGE = TM * 128;                    // bytes (64 rows x 64 bf16)
-constexpr int B_STAGE = BK * BSTRIDE * 2;            // bytes (64 k-rows x 132 bf16)
-constexpr int STAGE = A_STAGE + B_STAGE;
-constexpr int A_LOADS = TM * 8 / NT;                 // 16-byte chunks per thread: 2
+constexpr int B_STAGE = BK * TN * 2;                 // bytes (64 k-rows x 128 bf16)
+constexpr int STAGE = A_STAGE + B_STAGE;             // 24 KiB
+constexpr int NSTAGE = 4;
+constexpr int A_LOADS = TM * 8 / NT;                 // 16-byte copies per thread: 2
 constexpr int B_LOADS = BK * (TN / 8) / NT;          // 4
+constexpr int LOADS = A_LOADS + B_LOADS;
 
 struct Args {
   int M, N, K, S;
@@ -51,58 +56,48 @@ struct Args {
 };
 
 struct Smem {
-  alignas(16) char stage[2][STAGE];
+  alignas(16) char stage[NSTAGE][STAGE];
   int task;  // broadcast slot
   int flag;
 };
 
+ETC_DEV int bswz(int krow, int chunk) { return krow * 256 + ((chunk ^ ((krow >> 3) & 15)) << 4); }
+
 ETC_DEV void partial_task(const Args& p, Smem& sm, int tile, int s) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tm = tile / p.tiles_n, tn = tile % p.tiles_n;
   const int m0 = tm * TM, n0 = tn * TN;
   const int ks = p.K / p.S, kbeg = s * ks;
-  const int nk = ks / BK;
+  const int nk = ks / BK, last = nk - 1;
 
-  // this thread's load assignments
-  const bf16* arow[A_LOADS];
-  int achunk[A_LOADS], arowi[A_LOADS];
+  // copy sources: A rows 8w + 32i + lane/8 at the chunk its swizzled LDS position holds
+  // (rows past M repeat row M-1; their results are not stored); B k-rows 16i + 4w +
+  // lane/16 at chunk (lane % 16) ^ ((row / 8) % 16)
+  const char* asrc[A_LOADS];
+  const char* bsrc[B_LOADS];
+  const int lca = (lane & 7) ^ ((4 * w + (lane >> 4)) & 7);
 #pragma unroll
   for (int i = 0; i < A_LOADS; ++i) {
-    int q = tid + NT * i;
-    arowi[i] = q >> 3;
-    achunk[i] = q & 7;
-    int m = m0 + arowi[i];
-    arow[i] = (m < p.M) ? p.A + (long)m * p.K + kbeg + achunk[i] * 8 : nullptr;
+    const int m = min(m0 + 8 * w + 32 * i + (lane >> 3), p.M - 1);
+    asrc[i] = reinterpret_cast<const char*>(p.A + (size_t)m * p.K + kbeg) + lca * 16;
   }
-  int bk[B_LOADS], bc[B_LOADS];
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i) {
-    int q = tid + NT * i;
-    bk[i] = q >> 4;
-    bc[i] = q & 15;
+    const int r = 16 * i + 4 * w + (lane >> 4);
+    const int c = (lane & 15) ^ ((r >> 3) & 15);
+    bsrc[i] = reinterpret_cast<const char*>(p.B + (size_t)(kbeg + r) * p.N + n0) + c * 16;
   }
+  const size_t bstep = (size_t)BK * p.N * 2;  // bytes of B per stage
 
-  uint4 ra[A_LOADS], rb[B_LOADS];
-  auto gload = [&](int kt) {
-    const int k0 = kt * BK;
+  auto issue = [&](int kt) ETC_INLINE {
+    const int st = min(kt, last);  // past the last stage: re-read it into an unread slot
+    char* slot = sm.stage[kt % NSTAGE];
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i)
-      ra[i] = arow[i] ? *reinterpret_cast<const uint4*>(arow[i] + k0) : zero4();
+    for (int i = 0; i < A_LOADS; ++i) lds_dma16(asrc[i] + (size_t)st * 128, slot + (8 * w + 32 * i) * 128);
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i)
-      rb[i] = *reinterpret_cast<const uint4*>(p.B + (long)(kbeg + k0 + bk[i]) * p.N + n0 + bc[i] * 8);
-  };
-  auto sstore = [&](int buf) {
-    char* base = sm.stage[buf];
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) lds_put_chunk(base, arowi[i], achunk[i], ra[i]);
-    char* bb = base + A_STAGE;
-#pragma unroll
-    for (int i = 0; i < B_LOADS; ++i) {
-      uint2* d = reinterpret_cast<uint2*>(bb + (bk[i] * BSTRIDE + bc[i] * 8) * 2);
-      d[0] = make_uint2(rb[i].x, rb[i].y);
-      d[1] = make_uint2(rb[i].z, rb[i].w);
-    }
+      lds_dma16(bsrc[i] + (size_t)st * bstep, slot + A_STAGE + (16 * i + 4 * w) * 256);
   };
 
   f32x4 acc[4][2];
@@ -111,37 +106,44 @@ ETC_DEV void partial_task(const Args& p, Smem& sm, int tile, int s) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
+  issue(0);
+  issue(1);
+  issue(2);
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gload(kt + 1);
-    const char* base = sm.stage[kt & 1];
+    // this thread's copies of stage kt have landed (those of kt+1, kt+2 may not), then
+    // every wave's have, and every wave has finished reading slot (kt-1) mod 4, which
+    // stage kt+3 overwrites
+    vm_wait_barrier<2 * LOADS>();
+    issue(kt + 3);
+    const char* base = sm.stage[kt % NSTAGE];
     const uint16_t* bsm = reinterpret_cast<const uint16_t*>(base + A_STAGE);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      uint4 a[4], b[2];
+      const int g = lane >> 4;
+      u32x4 a[4], b[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = lds_chunk(base, i * 16 + (lane & 15), kk * 4 + (lane >> 4));
+      for (int i = 0; i < 4; ++i) a[i] = lds_chunk_v(base, i * 16 + (lane & 15), kk * 4 + g);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int n = w * 32 + j * 16 + (lane & 15);
-        const int k = kk * 32 + (lane >> 4) * 8;
+        const int k = kk * 32 + g * 8;
+        const uint16_t* col = bsm + (bswz(k, n >> 3) >> 1) + (n & 7);
         uint32_t h[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) h[q] = bsm[(k + q) * BSTRIDE + n];
-        b[j] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                          h[6] | (h[7] << 16));
+        for (int q = 0; q < 8; ++q) h[q] = col[q * 128];  // rows k..k+7 share the swizzle
+        b[j] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) mma16(acc[i][j], a[i], b[j], (const bf16*)nullptr);
     }
-    if (kt + 1 < nk) sstore((kt + 1) & 1);
-    __syncthreads();
   }
+  // the last copies (re-reads past the last stage) land before LDS is reused
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+  __syncthreads();
 
+  // the partial is read by another workgroup: agent-scope stores (see st_shared)
   float* dst = p.part + ((long)tile * p.S + s) * (TM * TN);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -151,7 +153,7 @@ ETC_DEV void partial_task(const Args& p, Smem& sm, int tile, int s) {
       for (int r = 0; r < 4; ++r) {
         const int row = i * 16 + (lane >> 4) * 4 + r;
         const int col = w * 32 + j * 16 + (lane & 15);
-        dst[row * TN + col] = acc[i][j][r];
+        st_shared(dst + row * TN + col, acc[i][j][r]);
       }
 }
 
@@ -181,8 +183,9 @@ __global__ __launch_bounds__(NT) void splitk_kernel(Args p) {
 
   while (true) {
     if (tid == 0) {
-      int t = (p.mode == ETC_SCHED_STATIC) ? atomicAdd(p.sched + W_TICKET, 1)
-                                           : atomicAdd(p.sched + W_QHEAD, 1);
+      // static: partial tickets are slice-major, so a chunk of consecutive tickets (one
+      // XCD queue's share) holds the tiles of one slice, which share its A block
+      int t = (p.mode == ETC_SCHED_STATIC) ? xcd_ticket(p.sched) : atomicAdd(p.sched + W_QHEAD, 1);
       if (ev_load_relaxed(p.sched + W_ABORT)) t = total;
       sm.task = t;
     }
@@ -194,13 +197,15 @@ __global__ __launch_bounds__(NT) void splitk_kernel(Args p) {
     if (t < nparts) {
       const int tile = t % p.tiles, s = t / p.tiles;
       partial_task(p, sm, tile, s);
-      wg_publish();
+      publish_shared();
       if (tid == 0) {
-        const int old = ev_add(p.ev + tile, 1);
+        // dynamic: the last arriver reduces, so its signal acquires every other partial
+        const int old = (p.mode == ETC_SCHED_DYNAMIC) ? ev_add_acquire(p.ev + tile, 1)
+                                                      : ev_add_relaxed(p.ev + tile, 1);
         sm.flag = (p.mode == ETC_SCHED_DYNAMIC && old == p.S - 1) ? 1 : 0;
       }
       __syncthreads();
-      if (sm.flag) reduce_task(p, tile);  // last arriver; its acq_rel add saw every partial
+      if (sm.flag) reduce_task(p, tile);  // last arriver
       __syncthreads();
     } else {
       const int tile = t - nparts;
