@@ -135,7 +135,8 @@ struct Args {
 
 struct RouteSmem {
   float part[4 * BT * 64 > BT * MAXE ? 4 * BT * 64 : BT * MAXE];  // [KS][BT][E] partial logits
-  float ssp[4][BT];                                              // [KS][BT] partial sums of squares
+  float ssp[8][BT];                                              // [KS][BT] partial sums of squares
+  float selv[BT][MAXK];                                          // selected logits
   float lg[BT][MAXE];
   float rs[BT];
   int sel[BT][MAXK];
@@ -263,7 +264,10 @@ ETC_TASK void route_task(const Args& p, const LayerArgs& L, int tau, Smem& sm) {
 
   // 1. partial logits and sums of squares per (expert block, K slice)
   const int NB = cdiv(E, 16);
-  const int KS = NB >= NWAVE ? 1 : min(4, NWAVE / NB);  // K slices per expert block: 1, 2 or 4
+  // K slices per expert block (1, 2, 4 or 8): enough items for every wave, each slice a
+  // whole number of MFMA steps
+  int KS = NB >= NWAVE ? 1 : min(8, NWAVE / NB);
+  while (KS > 1 && H % (KS * KSTEP) != 0) KS >>= 1;
   const int kslice = H / KS;           // a multiple of KSTEP (H is a multiple of 128)
   const int row = lane & 15, grp = lane >> 4;
   // Rows past the tile's tokens read the first token and columns past E read expert 0,
@@ -369,46 +373,34 @@ ETC_TASK void route_task(const Args& p, const LayerArgs& L, int tau, Smem& sm) {
       v[i] = (e < E) ? R.lg[tt][e] : -FLT_MAX;
       id[i] = (e < E) ? e : 0x7fffffff;
     }
-    float selv[MAXK];
-    int sele[MAXK];
+    for (int j = 0; j < K; ++j) {
+      float bv = -FLT_MAX;
+      int be = 0x7fffffff;
 #pragma unroll
-    for (int j = 0; j < MAXK; ++j) {
-      selv[j] = 0.f;
-      sele[j] = 0;
-      if (j < K) {
-        float bv = -FLT_MAX;
-        int be = 0x7fffffff;
+      for (int i = 0; i < 4; ++i)
+        if (v[i] > bv || (v[i] == bv && id[i] < be)) { bv = v[i]; be = id[i]; }
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (v[i] > bv || (v[i] == bv && id[i] < be)) { bv = v[i]; be = id[i]; }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) {
-          const float ov = __shfl_xor(bv, off, WAVE);
-          const int oe = __shfl_xor(be, off, WAVE);
-          if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (id[i] == be) { v[i] = -FLT_MAX; id[i] = 0x7fffffff; }
-        selv[j] = bv;
-        sele[j] = be;
+      for (int off = 32; off > 0; off >>= 1) {
+        const float ov = __shfl_xor(bv, off, WAVE);
+        const int oe = __shfl_xor(be, off, WAVE);
+        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
       }
-    }
-    float z[MAXK], zsum = 0.f;
 #pragma unroll
-    for (int j = 0; j < MAXK; ++j) {
-      z[j] = (j < K) ? expf(selv[j] - selv[0]) : 0.f;
-      zsum += z[j];
+      for (int i = 0; i < 4; ++i)
+        if (id[i] == be) { v[i] = -FLT_MAX; id[i] = 0x7fffffff; }
+      if (lane == 0) {
+        R.selv[tt][j] = bv;
+        R.sel[tt][j] = be;
+      }
     }
     if (lane == 0) {
       const int t = t0 + tt;
-#pragma unroll
-      for (int j = 0; j < MAXK; ++j)
-        if (j < K) {
-          st_shared(L.topk_idx + t * K + j, sele[j]);
-          st_shared(L.topk_w + t * K + j, z[j] / zsum);
-          R.sel[tt][j] = sele[j];
-        }
+      float zsum = 0.f;
+      for (int j = 0; j < K; ++j) zsum += expf(R.selv[tt][j] - R.selv[tt][0]);
+      for (int j = 0; j < K; ++j) {
+        st_shared(L.topk_idx + t * K + j, R.sel[tt][j]);
+        st_shared(L.topk_w + t * K + j, expf(R.selv[tt][j] - R.selv[tt][0]) / zsum);
+      }
     }
   }
   __syncthreads();

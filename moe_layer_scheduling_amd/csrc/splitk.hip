@@ -9,17 +9,18 @@
 //
 // Tasks, for T_out = ceil(M/64) * N/128 output tiles of 64 x 128:
 //   P(tile, s)  float32 partial of slice s (K/S columns of A): 4 waves, each 64 rows x
-//               32 columns of bf16 MFMA 16x16x32, A and B staged through LDS; stores
-//               the partial, then ev[tile] += 1 (release).
-//   R(tile)     waits ev[tile] >= S (acquire), C = P_0 + P_1 + ... + P_{S-1}.
-// Static mode: tickets 0 .. S*T_out-1 are the partials (slice-major, so the first
-// wave of tickets spreads over every tile), then T_out reduction tickets.  Dynamic
-// mode: only partial tasks are handed out; the partial whose add returns S-1 runs the
-// reduction itself (last arriver).
+//               32 columns of bf16 MFMA 16x16x32, A and B staged through LDS; publishes
+//               the partial, then ev[tile] += 1.
+//   R(tile, c)  waits ev[tile] >= S (acquire); rows 8c..8c+7 of the tile are
+//               C = P_0 + P_1 + ... + P_{S-1}.
+// Static mode: tickets 0 .. S*T_out-1 are the partials (slice-major), then 8 reduction
+// tickets per tile.  Dynamic mode: only partial tasks are handed out; the partial whose
+// add returns S-1 runs the tile's reduction itself (last arriver).
 //
 // Operands go from global memory straight into LDS (16 bytes per lane per copy) through
-// a ring of four stages of 64 k values: the copies run three stages ahead of the MFMAs,
-// which is what keeps enough bytes in flight to stream B from HBM.  A stage holds the
+// a ring of six stages of 64 k values: the copies run five stages ahead of the MFMAs
+// (120 KiB in flight per CU), which is what it takes to stream B at HBM rate when every
+// CU streams at once.  A stage holds the
 // A block [64 rows][64 k] (rows of 128 bytes, chunks swizzled as in mfma.hpp) and the B
 // block [64 k][128 n] (rows of 256 bytes).  B is N-contiguous while the MFMA wants 8
 // consecutive k per lane, so each lane gathers its 8 values with 2-byte LDS reads; the
@@ -36,7 +37,9 @@ constexpr int TM = 64, TN = 128, BK = 64;
 constexpr int A_STAGE = TM * 128;                    // bytes (64 rows x 64 bf16)
 constexpr int B_STAGE = BK * TN * 2;                 // bytes (64 k-rows x 128 bf16)
 constexpr int STAGE = A_STAGE + B_STAGE;             // 24 KiB
-constexpr int NSTAGE = 4;
+constexpr int NSTAGE = 6;
+constexpr int AHEAD = NSTAGE - 1;                    // stages in flight beyond the current
+constexpr int RCHUNKS = 8;                           // row chunks of a tile's reduction
 constexpr int A_LOADS = TM * 8 / NT;                 // 16-byte copies per thread: 2
 constexpr int B_LOADS = BK * (TN / 8) / NT;          // 4
 constexpr int LOADS = A_LOADS + B_LOADS;
@@ -106,15 +109,14 @@ ETC_DEV void partial_task(const Args& p, Smem& sm, int tile, int s) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  issue(0);
-  issue(1);
-  issue(2);
+#pragma unroll
+  for (int i = 0; i < AHEAD; ++i) issue(i);
   for (int kt = 0; kt < nk; ++kt) {
-    // this thread's copies of stage kt have landed (those of kt+1, kt+2 may not), then
-    // every wave's have, and every wave has finished reading slot (kt-1) mod 4, which
-    // stage kt+3 overwrites
-    vm_wait_barrier<2 * LOADS>();
-    issue(kt + 3);
+    // this thread's copies of stage kt have landed (those of the next AHEAD-1 stages may
+    // not), then every wave's have, and every wave has finished reading slot
+    // (kt-1) mod NSTAGE, which stage kt+AHEAD overwrites
+    vm_wait_barrier<(AHEAD - 1) * LOADS>();
+    issue(kt + AHEAD);
     const char* base = sm.stage[kt % NSTAGE];
     const uint16_t* bsm = reinterpret_cast<const uint16_t*>(base + A_STAGE);
 #pragma unroll
@@ -157,21 +159,28 @@ ETC_DEV void partial_task(const Args& p, Smem& sm, int tile, int s) {
       }
 }
 
-// C tile = partials summed in slice order.
-ETC_DEV void reduce_task(const Args& p, int tile) {
-  const int tid = threadIdx.x;
+// Rows [rc*TM/RCHUNKS, ...) of a C tile = partials summed in slice order.  Every thread
+// owns one float4 of the chunk and has all of its S loads in flight together.
+ETC_DEV void reduce_task(const Args& p, int tile, int rc) {
+  constexpr int ROWS = TM / RCHUNKS, F4 = ROWS * TN / 4;  // 8 rows: 256 float4
+  static_assert(F4 == NT, "one float4 per thread");
   const int tm = tile / p.tiles_n, tn = tile % p.tiles_n;
-  const float* src = p.part + (long)tile * p.S * (TM * TN);
-  for (int e4 = tid; e4 < TM * TN / 4; e4 += NT) {
-    const int row = (e4 * 4) / TN, col = (e4 * 4) % TN;
-    const int m = tm * TM + row;
-    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = 0; s < p.S; ++s) {
-      const float4 v = *reinterpret_cast<const float4*>(src + (long)s * TM * TN + e4 * 4);
-      sum.x += v.x; sum.y += v.y; sum.z += v.z; sum.w += v.w;
+  const int e4 = threadIdx.x, row = rc * ROWS + (e4 * 4) / TN, col = (e4 * 4) % TN;
+  const float* src = p.part + (long)tile * p.S * (TM * TN) + row * TN + col;
+  float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < p.S; s0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = (s0 + u < p.S) ? *reinterpret_cast<const float4*>(src + (long)(s0 + u) * TM * TN)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      sum.x += v[u].x; sum.y += v[u].y; sum.z += v[u].z; sum.w += v[u].w;
     }
-    if (m < p.M) *reinterpret_cast<float4*>(p.C + (long)m * p.N + tn * TN + col) = sum;
   }
+  const int m = tm * TM + row;
+  if (m < p.M) *reinterpret_cast<float4*>(p.C + (long)m * p.N + tn * TN + col) = sum;
 }
 
 __global__ __launch_bounds__(NT) void splitk_kernel(Args p) {
@@ -179,7 +188,8 @@ __global__ __launch_bounds__(NT) void splitk_kernel(Args p) {
   const int tid = threadIdx.x;
   const uint64_t deadline = now_ticks() + p.timeout_ticks;
   const int nparts = p.tiles * p.S;
-  const int total = (p.mode == ETC_SCHED_STATIC) ? nparts + p.tiles : nparts;
+  // static: the partials, then RCHUNKS reduction tickets per tile
+  const int total = (p.mode == ETC_SCHED_STATIC) ? nparts + p.tiles * RCHUNKS : nparts;
 
   while (true) {
     if (tid == 0) {
@@ -205,13 +215,14 @@ __global__ __launch_bounds__(NT) void splitk_kernel(Args p) {
         sm.flag = (p.mode == ETC_SCHED_DYNAMIC && old == p.S - 1) ? 1 : 0;
       }
       __syncthreads();
-      if (sm.flag) reduce_task(p, tile);  // last arriver
+      if (sm.flag)  // last arriver
+        for (int rc = 0; rc < RCHUNKS; ++rc) reduce_task(p, tile, rc);
       __syncthreads();
     } else {
-      const int tile = t - nparts;
+      const int tile = (t - nparts) / RCHUNKS, rc = (t - nparts) % RCHUNKS;
       if (tid == 0) sm.flag = spin_until_geq(p.ev + tile, p.S, p.sched, deadline, 1) ? 1 : 0;
       __syncthreads();
-      if (sm.flag) reduce_task(p, tile);
+      if (sm.flag) reduce_task(p, tile, rc);
       __syncthreads();
     }
   }
