@@ -255,6 +255,8 @@ def main():
                     help="only run a plain 1 GiB elementwise copy (counter calibration)")
     ap.add_argument("--splitk-only", action="store_true",
                     help="only time the split-K GEMM (for per-kernel profiles)")
+    ap.add_argument("--splitk-copies", type=int, default=4,
+                    help="copies of B rotated between split-K calls (4: B streams from HBM)")
     ap.add_argument("--source-hash", action="store_true",
                     help="print the hash that identifies the kernel sources and exit")
     args = ap.parse_args()
@@ -274,7 +276,7 @@ def main():
         return
     binding.load_library()
     if args.splitk_only:
-        res = {m: bench_splitk(args.steps, args.warmup, m) for m in ("static", "dynamic")}
+        res = {m: bench_splitk(args.steps, args.warmup, m, args.splitk_copies) for m in ("static", "dynamic")}
         print(json.dumps({"splitk": res}), flush=True)
         return
 
