@@ -66,6 +66,38 @@ ETC_DEV void expand16(const uint4& v, float* out4, const float*) {
   out4[2] = __uint_as_float(v.z);
   out4[3] = __uint_as_float(v.w);
 }
+ETC_DEV void expand16(const u32x4& v, float* out8, const bf16* tag) {
+  expand16(make_uint4(v.x, v.y, v.z, v.w), out8, tag);
+}
+ETC_DEV void expand16(const u32x4& v, float* out4, const float* tag) {
+  expand16(make_uint4(v.x, v.y, v.z, v.w), out4, tag);
+}
+
+// ------------------------------------------------------------------ global memory
+//
+// Pointers reach the task bodies through an LDS copy of the kernel arguments, so the
+// compiler cannot tell that they address global memory and would access them with FLAT
+// instructions.  Those count against the LDS wait counter as well, so every wait for an
+// LDS read would also wait for every global load and store still in flight, and a wait
+// for one of several loads could only wait for all of them.  Every access to global
+// memory therefore goes through a pointer in address space 1.
+#ifndef ETC_GLOBAL
+#define ETC_GLOBAL __attribute__((address_space(1)))
+#endif
+#ifndef ETC_LDS
+#define ETC_LDS __attribute__((address_space(3)))
+#endif
+template <typename T>
+ETC_DEV ETC_GLOBAL T* gp(T* p) { return (ETC_GLOBAL T*)p; }
+template <typename T>
+ETC_DEV const ETC_GLOBAL T* gp(const T* p) { return (const ETC_GLOBAL T*)p; }
+// a V (e.g. a 16-byte vector) read from global memory at p
+template <typename V, typename T>
+ETC_DEV V gld(const T* p) { return *(const ETC_GLOBAL V*)p; }
+// relaxed device-scope float addition without a result (the atomic combine)
+ETC_DEV void red_add(float* p, float v) {
+  __hip_atomic_fetch_add(gp(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // ------------------------------------------------------------------ event counters
 //
@@ -78,37 +110,37 @@ ETC_DEV void expand16(const uint4& v, float* out4, const float*) {
 // rest of the workgroup is ordered by barriers around it.
 
 ETC_DEV int ev_load(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(gp(p), __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
 }
 ETC_DEV int ev_load_relaxed(const int* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(gp(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 ETC_DEV int ev_add(int* p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_fetch_add(gp(p), v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
 }
 ETC_DEV int ev_add_acquire(int* p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_fetch_add(gp(p), v, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
 }
 ETC_DEV int ev_add_relaxed(int* p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_fetch_add(gp(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 ETC_DEV void ev_store(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(gp(p), v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 ETC_DEV void ev_store_relaxed(int* p, int v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(gp(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 ETC_DEV long long q_load(const long long* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(gp(p), __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
 }
 ETC_DEV long long q_load_relaxed(const long long* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return __hip_atomic_load(gp(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 ETC_DEV void q_store(long long* p, long long v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(gp(p), v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 ETC_DEV void q_store_relaxed(long long* p, long long v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(gp(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 ETC_DEV void fence_release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
 ETC_DEV void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
@@ -121,12 +153,12 @@ ETC_DEV void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "a
 // that follows is a relaxed atomic.  Readers still acquire (invalidating their L2), so
 // no stale line from an earlier call or layer is read.
 ETC_DEV void st_shared(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(gp(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-ETC_DEV void st_shared(int* p, int v) { __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+ETC_DEV void st_shared(int* p, int v) { __hip_atomic_store(gp(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 ETC_DEV void st_shared(float* p, float v) { st_shared(reinterpret_cast<uint32_t*>(p), __float_as_uint(v)); }
 ETC_DEV void st_shared8(void* p, uint64_t v) {
-  __hip_atomic_store(static_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(gp(static_cast<uint64_t*>(p)), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 // 16 bytes at a 16-byte aligned address, as two 8-byte stores
 ETC_DEV void st_shared16(void* p, const uint4& v) {
@@ -216,7 +248,7 @@ ETC_DEV int xcd_ticket(int* sched) {
   const int Q = nwg < MAX_XCD_QUEUES ? nwg : MAX_XCD_QUEUES;
   const int G = nwg / Q;
   const int q = (int)blockIdx.x % Q;
-  const int i = atomicAdd(sched + W_XTICKET + q, 1);
+  const int i = __hip_atomic_fetch_add(gp(sched + W_XTICKET + q), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return ((i / G) * Q + q) * G + i % G;
 }
 
@@ -255,6 +287,31 @@ ETC_DEV bool spin_until_geq(const int* ctr, int target, int* sched, uint64_t dea
 }
 
 // ------------------------------------------------------------------ wave helpers
+
+// Lane exchanges inside rows of 16 lanes through DPP (no LDS round trip): swap with the
+// neighbour (lane ^ 1), swap pairs (lane ^ 2), mirror each half row (lane i <-> 7 - i)
+// and mirror the row (lane i <-> 15 - i).  Applied in that order with a commutative
+// operation they form a butterfly, so every lane of the row ends with the same result,
+// bit for bit.
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_HALF_MIRROR = 0x141, DPP_MIRROR = 0x140;
+
+template <int CTRL>
+ETC_DEV int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+ETC_DEV float dpp_f(float v) {
+  return __int_as_float(dpp_i<CTRL>(__float_as_int(v)));
+}
+
+// The sum over each row of 16 lanes, identical in every lane of the row.
+ETC_DEV float row16_sum(float v) {
+  v += dpp_f<DPP_XOR1>(v);
+  v += dpp_f<DPP_XOR2>(v);
+  v += dpp_f<DPP_HALF_MIRROR>(v);
+  v += dpp_f<DPP_MIRROR>(v);
+  return v;
+}
 
 ETC_DEV float wave_sum(float v) {
 #pragma unroll

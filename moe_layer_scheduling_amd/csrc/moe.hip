@@ -133,10 +133,13 @@ struct Args {
   LayerArgs layer[MAXL];
 };
 
+// The workgroup's LDS copy of the kernel arguments, seen as LDS by the task bodies (a
+// generic reference would make every field read a FLAT load).
+typedef const ETC_LDS Args KArgs;
+typedef const ETC_LDS LayerArgs KLayer;
+
 struct RouteSmem {
-  float part[4 * BT * 64 > BT * MAXE ? 4 * BT * 64 : BT * MAXE];  // [KS][BT][E] partial logits
-  float ssp[8][BT];                                              // [KS][BT] partial sums of squares
-  float selv[BT][MAXK];                                          // selected logits
+  float part[BT * 512];  // [KS][BT][E] partial logits, KS * E <= 512
   float lg[BT][MAXE];
   float rs[BT];
   int sel[BT][MAXK];
@@ -178,246 +181,268 @@ ETC_DEV uint4 pack16<float>(const float* v) {
   return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
 }
 
-ETC_DEV int tile_rows(const Args& p, int tau) { return min(BT, p.T - tau * BT); }
+ETC_DEV int tile_rows(KArgs& p, int tau) { return min(BT, p.T - tau * BT); }
 
 // Largest e in [0, E) with rt_base[e] * mult <= idx: the expert owning task idx.
 ETC_DEV int owner_expert(const int* rt_base, int E, int idx, int mult) {
   int lo = 0, hi = E;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (rt_base[mid] * mult <= idx) lo = mid; else hi = mid;
+    if (gp(rt_base)[mid] * mult <= idx) lo = mid; else hi = mid;
   }
   return lo;
 }
 
 // ------------------------------------------------------------------ R: routing tile
 //
-// logits[t][e] = rms_t * sum_h (x[t][h] * gamma[h]) * W_r[e][h] (+ b[e]) on the matrix cores:
-// the float32 values v = x * gamma are split exactly into three bfloat16 parts
-// (hi = bf16(v), mid = bf16(v - hi), lo = bf16(v - hi - mid)); each product of a part with a
-// bfloat16 weight is exact in float32, and the three parts accumulate separately in
-// float32, so the dot product has float32 accuracy.  Float32 layers use the float32 MFMA
-// directly.  Waves take (16-expert block, K slice) items; with fewer than four expert
-// blocks the K range is split across waves and the partial sums are added in slice
-// order.  The sum of squares for the RMS comes from the same loads.
+// One task routes a tile of BT tokens: RMSNorm, router logits, top-k with softmax, the
+// tile's per-expert ranks and histogram [P3 §5.5 Obstacle 1: the counts that set the
+// event targets come from here].
+//
+// Router precision.  logits[t][e] = sum_h xn[t][h] * W_r[e][h] (+ b[e]) with
+// xn = x * rs * gamma in float32.  On the matrix cores xn is split into three bfloat16
+// parts (hi = bf16(xn), mid = bf16(xn - hi), lo = bf16(xn - hi - mid)); the product of
+// each part with a bfloat16 weight is exact in float32 and the parts accumulate
+// separately, so the dot product keeps float32 accuracy.  Float32 layers use the float32
+// MFMA on xn directly.
+//
+// Work split.  NB = ceil(E/16) blocks of 16 experts; a wave owns NBW of them (the next
+// power of two >= NB, at most 4) over one of KS = 8 / ceil(NB/NBW) K slices, so every
+// wave has exactly one item.  A wave loads its x rows once per K step for all its expert
+// blocks; the waves of the first expert group also store xn in storage precision (xq,
+// the experts' input).
 
-template <typename TE>
-ETC_DEV void router_step(const uint4& xv, const uint4& wv, const float* g, f32x4 (&acc)[3], float& ss);
-
+template <int NSPLIT>
+struct RouterSplit;
 template <>
-ETC_DEV void router_step<bf16>(const uint4& xv, const uint4& wv, const float* g, f32x4 (&acc)[3],
-                               float& ss) {
-  float x[8];
-  expand16(xv, x, (const bf16*)nullptr);
-  uint32_t hi[4], mid[4], lo[4];
+struct RouterSplit<3> {  // bfloat16 layers: three parts per value
+  ETC_DEV static void run(const float* v, u32x4 (&a)[3]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t ph[2], pm[2], pl[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const float xe = x[2 * i + q];
-      ss += xe * xe;
-      const float v = xe * g[2 * i + q];
-      ph[q] = f32_to_bf16_bits(v);
-      const float r1 = v - bf16_bits_to_f32(ph[q]);
-      pm[q] = f32_to_bf16_bits(r1);
-      pl[q] = f32_to_bf16_bits(r1 - bf16_bits_to_f32(pm[q]));
+    for (int i = 0; i < 4; ++i) {
+      const float x0 = v[2 * i], x1 = v[2 * i + 1];
+      const uint32_t h = pack_bf16x2(x0, x1);
+      const float r0 = x0 - __uint_as_float(h << 16), r1 = x1 - __uint_as_float(h & 0xffff0000u);
+      const uint32_t m = pack_bf16x2(r0, r1);
+      const float q0 = r0 - __uint_as_float(m << 16), q1 = r1 - __uint_as_float(m & 0xffff0000u);
+      a[0][i] = h;
+      a[1][i] = m;
+      a[2][i] = pack_bf16x2(q0, q1);
     }
-    hi[i] = ph[0] | (ph[1] << 16);
-    mid[i] = pm[0] | (pm[1] << 16);
-    lo[i] = pl[0] | (pl[1] << 16);
   }
-  const bf16* tag = nullptr;
-  mma16(acc[0], make_uint4(hi[0], hi[1], hi[2], hi[3]), wv, tag);
-  mma16(acc[1], make_uint4(mid[0], mid[1], mid[2], mid[3]), wv, tag);
-  mma16(acc[2], make_uint4(lo[0], lo[1], lo[2], lo[3]), wv, tag);
-}
-
+};
 template <>
-ETC_DEV void router_step<float>(const uint4& xv, const uint4& wv, const float* g, f32x4 (&acc)[3],
-                                float& ss) {
-  float x[4];
-  expand16(xv, x, (const float*)nullptr);
-  float v[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ss += x[i] * x[i];
-    v[i] = x[i] * g[i];
+struct RouterSplit<1> {  // float32 layers: the values themselves
+  ETC_DEV static void run(const float* v, u32x4 (&a)[1]) {
+    a[0] = u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                 __float_as_uint(v[3])};
   }
-  mma16(acc[0], make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                           __float_as_uint(v[3])),
-        wv, (const float*)nullptr);
-}
+};
 
-template <typename TE>
-ETC_TASK void route_task(const Args& p, const LayerArgs& L, int tau, Smem& sm) {
-  constexpr int EPC = 16 / (int)sizeof(TE);
-  constexpr int KSTEP = 4 * EPC;  // K consumed per MFMA step by the four lane groups
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int H = p.H, E = p.E, K = p.K;
-  const int t0 = tau * BT, nt = tile_rows(p, tau);
-  const TE* x = static_cast<const TE*>(L.in);
-  const TE* wr = static_cast<const TE*>(L.w_router);
-  TE* xq = static_cast<TE*>(p.xq);
-  RouteSmem& R = sm.u.r;
-
-  // 1. partial logits and sums of squares per (expert block, K slice)
-  const int NB = cdiv(E, 16);
-  // K slices per expert block (1, 2, 4 or 8): enough items for every wave, each slice a
-  // whole number of MFMA steps
-  int KS = NB >= NWAVE ? 1 : min(8, NWAVE / NB);
-  while (KS > 1 && H % (KS * KSTEP) != 0) KS >>= 1;
-  const int kslice = H / KS;           // a multiple of KSTEP (H is a multiple of 128)
-  const int row = lane & 15, grp = lane >> 4;
-  // Rows past the tile's tokens read the first token and columns past E read expert 0,
-  // so every load is unconditional; those results are never used.  Loads go out eight
-  // K steps at a time before any of them is consumed.
-  const TE* xrow = x + (size_t)(t0 + (row < nt ? row : 0)) * H;
-  constexpr int U = 8;
-  for (int it = w; it < NB * KS; it += NWAVE) {
-    const int nb = it / KS, ks = it % KS;
-    const int e = nb * 16 + row;
-    const bool e_ok = e < E;
-    const TE* wrow = wr + (size_t)(e_ok ? e : 0) * H;
-    f32x4 acc[3];
+// Wave item: expert blocks g*NBW .. g*NBW+NBW-1 over K steps [s0, s1).  Writes the
+// partial logits of its K slice to R.part[ks][t][e].
+template <typename TE, int NBW>
+ETC_DEV void router_item(KArgs& p, KLayer& L, RouteSmem& R, int t0, int nt, int g,
+                         int ks, int KS) {
+  constexpr int EPC = 16 / (int)sizeof(TE);  // values per 16-byte chunk
+  constexpr int KSTEP = 4 * EPC;              // K per MFMA step (four lane groups)
+  constexpr int NSPLIT = sizeof(TE) == 2 ? 3 : 1;
+  constexpr int U = NBW <= 2 ? 4 : 2;         // K steps whose loads are in flight together
+  const int lane = threadIdx.x & 63, row = lane & 15, grp = lane >> 4;
+  const int H = p.H, E = p.E;
+  const int nsteps = H / KSTEP;
+  const int s0 = ks * nsteps / KS, s1 = (ks + 1) * nsteps / KS;
+  // rows past the tile's tokens repeat its last token and experts past E repeat the last
+  // expert, so every load is unconditional; those results are never used
+  const int tr = row < nt ? row : nt - 1;
+  const TE* xrow = static_cast<const TE*>(L.in) + (size_t)(t0 + tr) * H + grp * EPC;
+  const float* grow = L.gamma + grp * EPC;
+  const TE* wbase = static_cast<const TE*>(L.w_router) + grp * EPC;
+  int woff[NBW];
 #pragma unroll
-    for (int q = 0; q < 3; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float ss = 0.f;
-    const int kb = ks * kslice, ke = kb + kslice;
-    auto steps = [&](int k0, auto nsteps) ETC_INLINE {
-      constexpr int N = decltype(nsteps)::value;
-      uint4 xv[N], wv[N];
-      float4 gv[N][EPC / 4];
-      static_for<N>([&](auto u) ETC_INLINE {
-        const int k = k0 + u * KSTEP + grp * EPC;
-        xv[u] = *reinterpret_cast<const uint4*>(xrow + k);
-        wv[u] = *reinterpret_cast<const uint4*>(wrow + k);
-        static_for<EPC / 4>([&](auto q) ETC_INLINE { gv[u][q] = *reinterpret_cast<const float4*>(L.gamma + k + 4 * q); });
+  for (int b = 0; b < NBW; ++b) woff[b] = min((g * NBW + b) * 16 + row, E - 1) * H;
+  TE* xqrow = static_cast<TE*>(p.xq) + (size_t)(t0 + row) * H + grp * EPC;
+  const bool put = g == 0 && row < nt;
+  const float rs = R.rs[tr];
+  f32x4 acc[NBW][NSPLIT];
+#pragma unroll
+  for (int b = 0; b < NBW; ++b)
+#pragma unroll
+    for (int q = 0; q < NSPLIT; ++q) acc[b][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto steps = [&](int s, auto nst) ETC_INLINE {
+    constexpr int N = decltype(nst)::value;
+    u32x4 xv[N], wv[N][NBW];
+    f32x4 gv[N][EPC / 4];
+    static_for<N>([&](auto u) ETC_INLINE {
+      const int k = (s + u) * KSTEP;
+      xv[u] = gld<u32x4>(xrow + k);
+      static_for<EPC / 4>([&](auto q) ETC_INLINE { gv[u][q] = gld<f32x4>(grow + k + 4 * q); });
+      static_for<NBW>([&](auto b) ETC_INLINE { wv[u][b] = gld<u32x4>(wbase + woff[b] + k); });
+    });
+    static_for<N>([&](auto u) ETC_INLINE {
+      const int k = (s + u) * KSTEP;
+      float v[EPC];
+      expand16(xv[u], v, (const TE*)nullptr);
+      static_for<EPC / 4>([&](auto q) ETC_INLINE {
+        v[4 * q] = v[4 * q] * rs * gv[u][q].x;
+        v[4 * q + 1] = v[4 * q + 1] * rs * gv[u][q].y;
+        v[4 * q + 2] = v[4 * q + 2] * rs * gv[u][q].z;
+        v[4 * q + 3] = v[4 * q + 3] * rs * gv[u][q].w;
       });
-      static_for<N>([&](auto u) ETC_INLINE {
-        float g[EPC];
-        static_for<EPC / 4>([&](auto q) ETC_INLINE {
-          g[4 * q] = gv[u][q].x; g[4 * q + 1] = gv[u][q].y; g[4 * q + 2] = gv[u][q].z; g[4 * q + 3] = gv[u][q].w;
-        });
-        router_step<TE>(xv[u], wv[u], g, acc, ss);
+      if (put) st_shared16(xqrow + k, pack16<TE>(v));
+      u32x4 a[NSPLIT];
+      RouterSplit<NSPLIT>::run(v, a);
+      static_for<NBW>([&](auto b) ETC_INLINE {
+        static_for<NSPLIT>([&](auto q) ETC_INLINE { mma16(acc[b][q], a[q], wv[u][b], (const TE*)nullptr); });
       });
-    };
-    int k0 = kb;
-    for (; k0 + U * KSTEP <= ke; k0 += U * KSTEP) steps(k0, std::integral_constant<int, U>{});
-    for (; k0 < ke; k0 += KSTEP) steps(k0, std::integral_constant<int, 1>{});
-    const f32x4 sum = (acc[2] + acc[1]) + acc[0];
-    if (e_ok) {
+    });
+  };
+  int s = s0;
+  for (; s + U <= s1; s += U) steps(s, std::integral_constant<int, U>{});
+  for (; s < s1; ++s) steps(s, std::integral_constant<int, 1>{});
+
+  // result element (token grp*4+i, expert block column row) of each block
+#pragma unroll
+  for (int b = 0; b < NBW; ++b) {
+    const int e = (g * NBW + b) * 16 + row;
+    f32x4 sum = acc[b][0];
+    if constexpr (NSPLIT == 3) sum = (acc[b][2] + acc[b][1]) + acc[b][0];
+    if (e < E) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) R.part[(ks * BT + grp * 4 + i) * E + e] = sum[i];
     }
-    if (nb == 0) {  // the sum of squares of this K slice, once per token
-      ss += __shfl_xor(ss, 16, WAVE);
-      ss += __shfl_xor(ss, 32, WAVE);
-      if (grp == 0) R.ssp[ks][row] = ss;
-    }
   }
-  __syncthreads();
-  if (tid < BT) {
+}
+
+// Top-k of one token per row of 16 lanes: lane j holds experts j, j+16, ...  k rounds of
+// an argmax by (logit desc, expert asc) across the row; lane j keeps the j-th winner.
+// Softmax over the k selected logits.  Rows past the tile's tokens compute on unused
+// LDS values and store nothing.
+template <int VPL>
+ETC_DEV void topk_row(KArgs& p, KLayer& L, RouteSmem& R, int t0, int nt) {
+  const int tid = threadIdx.x, j = tid & 15, tt = tid >> 4;
+  const int E = p.E, K = p.K;
+  float v[VPL];
+  int id[VPL];
+#pragma unroll
+  for (int i = 0; i < VPL; ++i) {
+    const int e = j + 16 * i;
+    v[i] = e < E ? R.lg[tt][e] : -FLT_MAX;
+    id[i] = e < E ? e : 0x7fffffff;
+  }
+  float mine = 0.f, top = 0.f;
+  int mine_e = 0;
+  for (int r = 0; r < K; ++r) {
+    float bv = v[0];
+    int be = id[0];
+#pragma unroll
+    for (int i = 1; i < VPL; ++i)
+      if (v[i] > bv) { bv = v[i]; be = id[i]; }  // experts ascend with i: ties keep the first
+    auto merge = [&](float ov, int oe) ETC_INLINE {
+      if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
+    };
+    merge(dpp_f<DPP_XOR1>(bv), dpp_i<DPP_XOR1>(be));
+    merge(dpp_f<DPP_XOR2>(bv), dpp_i<DPP_XOR2>(be));
+    merge(dpp_f<DPP_HALF_MIRROR>(bv), dpp_i<DPP_HALF_MIRROR>(be));
+    merge(dpp_f<DPP_MIRROR>(bv), dpp_i<DPP_MIRROR>(be));
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (id[i] == be) { v[i] = -FLT_MAX; id[i] = 0x7fffffff; }
+    if (r == 0) top = bv;
+    if (j == r) { mine = bv; mine_e = be; }
+  }
+  const float z = j < K ? expf(mine - top) : 0.f;
+  const float zsum = row16_sum(z);
+  if (tt < nt && j < K) {
+    const int t = t0 + tt;
+    st_shared(L.topk_idx + t * K + j, mine_e);
+    st_shared(L.topk_w + t * K + j, z / zsum);
+    R.sel[tt][j] = mine_e;
+  }
+}
+
+template <typename TE>
+ETC_TASK void route_task(KArgs& p, KLayer& L, int tau, Smem& sm) {
+  constexpr int EPC = 16 / (int)sizeof(TE);
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int H = p.H, E = p.E, K = p.K;
+  const int t0 = tau * BT, nt = tile_rows(p, tau);
+  RouteSmem& R = sm.u.r;
+
+  // 1. inverse RMS of each token: 32 lanes per token, each summing the squares of every
+  //    32nd chunk of the row (eight chunks in flight), then a butterfly over the 32 lanes
+  {
+    const int tt = tid >> 5, j = tid & 31;
     float ss = 0.f;
-    for (int ks = 0; ks < KS; ++ks) ss += R.ssp[ks][tid];
-    R.rs[tid] = (tid < nt) ? 1.0f / sqrtf(ss / (float)H + p.eps) : 0.f;
-  }
-  __syncthreads();
-  for (int o = tid; o < BT * E; o += MNT) {
-    const int tt = o / E, e = o % E;
-    float v = 0.f;
-    for (int ks = 0; ks < KS; ++ks) v += R.part[(ks * BT + tt) * E + e];
-    R.lg[tt][e] = R.rs[tt] * v + (L.bias ? L.bias[e] : 0.f);
-  }
-  __syncthreads();
-
-  // 2. normalised rows in storage precision for the experts, eight chunks per thread at
-  //    a time so their loads are in flight together
-  const int cpr = H / EPC, nchunks = nt * cpr;
-  for (int c0 = tid; c0 < nchunks; c0 += 8 * MNT) {
-    uint4 xv[8];
-    float4 gv[8][EPC / 4];
-    static_for<8>([&](auto u) ETC_INLINE {
-      const int c = min(c0 + u * MNT, nchunks - 1);
-      const int tt = c / cpr, h = (c % cpr) * EPC;
-      xv[u] = *reinterpret_cast<const uint4*>(x + (size_t)(t0 + tt) * H + h);
-      static_for<EPC / 4>([&](auto q) ETC_INLINE { gv[u][q] = *reinterpret_cast<const float4*>(L.gamma + h + 4 * q); });
-    });
-    static_for<8>([&](auto u) ETC_INLINE {
-      const int c = c0 + u * MNT;
-      if (c < nchunks) {
-        const int tt = c / cpr, h = (c % cpr) * EPC;
-        float v[EPC];
-        expand16(xv[u], v, (const TE*)nullptr);
-        const float r = R.rs[tt];
-        static_for<EPC / 4>([&](auto q) ETC_INLINE {
-          v[4 * q] = v[4 * q] * r * gv[u][q].x;
-          v[4 * q + 1] = v[4 * q + 1] * r * gv[u][q].y;
-          v[4 * q + 2] = v[4 * q + 2] * r * gv[u][q].z;
-          v[4 * q + 3] = v[4 * q + 3] * r * gv[u][q].w;
+    if (tt < nt) {
+      const TE* xr = static_cast<const TE*>(L.in) + (size_t)(t0 + tt) * H;
+      const int cpr = H / EPC;
+      int c = j;
+      for (; c + 7 * 32 < cpr; c += 8 * 32) {
+        u32x4 xv[8];
+        static_for<8>([&](auto u) ETC_INLINE { xv[u] = gld<u32x4>(xr + (c + 32 * u) * EPC); });
+        static_for<8>([&](auto u) ETC_INLINE {
+          float f[EPC];
+          expand16(xv[u], f, (const TE*)nullptr);
+#pragma unroll
+          for (int i = 0; i < EPC; ++i) ss += f[i] * f[i];
         });
-        st_shared16(xq + (size_t)(t0 + tt) * H + h, pack16<TE>(v));
       }
-    });
-  }
-
-  // 3. top-k by (logit desc, expert asc) with k rounds of a wave argmax; softmax over
-  //    the selected logits
-  for (int tt = w; tt < nt; tt += NWAVE) {
-    float v[4];
-    int id[4];
+      for (; c < cpr; c += 32) {
+        float f[EPC];
+        expand16(gld<u32x4>(xr + c * EPC), f, (const TE*)nullptr);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      v[i] = (e < E) ? R.lg[tt][e] : -FLT_MAX;
-      id[i] = (e < E) ? e : 0x7fffffff;
-    }
-    for (int j = 0; j < K; ++j) {
-      float bv = -FLT_MAX;
-      int be = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (v[i] > bv || (v[i] == bv && id[i] < be)) { bv = v[i]; be = id[i]; }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const float ov = __shfl_xor(bv, off, WAVE);
-        const int oe = __shfl_xor(be, off, WAVE);
-        if (ov > bv || (ov == bv && oe < be)) { bv = ov; be = oe; }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (id[i] == be) { v[i] = -FLT_MAX; id[i] = 0x7fffffff; }
-      if (lane == 0) {
-        R.selv[tt][j] = bv;
-        R.sel[tt][j] = be;
+        for (int i = 0; i < EPC; ++i) ss += f[i] * f[i];
       }
     }
-    if (lane == 0) {
-      const int t = t0 + tt;
-      float zsum = 0.f;
-      for (int j = 0; j < K; ++j) zsum += expf(R.selv[tt][j] - R.selv[tt][0]);
-      for (int j = 0; j < K; ++j) {
-        st_shared(L.topk_idx + t * K + j, R.sel[tt][j]);
-        st_shared(L.topk_w + t * K + j, expf(R.selv[tt][j] - R.selv[tt][0]) / zsum);
-      }
-    }
+    ss = row16_sum(ss);
+    ss += __shfl_xor(ss, 16, WAVE);
+    if (j == 0) R.rs[tt] = tt < nt ? 1.0f / sqrtf(ss / (float)H + p.eps) : 0.f;
   }
   __syncthreads();
 
-  // 4. rank of each pair among the tile's pairs of the same expert (tokens ascending;
-  //    a token never holds one expert twice) and the tile's expert histogram
-  for (int a = tid; a < nt * K; a += MNT) {
-    const int tt = a / K, j = a % K, e = R.sel[tt][j];
-    int rank = 0;
-    for (int u = 0; u < tt; ++u)
-      for (int jj = 0; jj < K; ++jj) rank += (R.sel[u][jj] == e);
-    st_shared(L.lrank + (t0 + tt) * K + j, rank);
+  // 2. partial logits per (expert group, K slice), one item per wave; xq on the way
+  const int NB = cdiv(E, 16);
+  const int NBW = NB <= 1 ? 1 : (NB <= 2 ? 2 : 4);
+  const int KS = NWAVE / cdiv(NB, NBW);
+  {
+    const int g = w / KS, ks = w % KS;
+    if (NBW == 1) router_item<TE, 1>(p, L, R, t0, nt, g, ks, KS);
+    else if (NBW == 2) router_item<TE, 2>(p, L, R, t0, nt, g, ks, KS);
+    else router_item<TE, 4>(p, L, R, t0, nt, g, ks, KS);
   }
+  __syncthreads();
+  for (int o = tid; o < nt * E; o += MNT) {
+    const int tt = o / E, e = o - tt * E;
+    float v = 0.f;
+    for (int k = 0; k < KS; ++k) v += R.part[(k * BT + tt) * E + e];
+    R.lg[tt][e] = v + (L.bias ? gp(L.bias)[e] : 0.f);
+  }
+  __syncthreads();
+
+  // 3. top-k and gates: one row of 16 lanes per token (waves 0..3)
+  if (tid < BT * 16) {
+    const int vpl = cdiv(E, 16);
+    if (vpl == 1) topk_row<1>(p, L, R, t0, nt);
+    else if (vpl == 2) topk_row<2>(p, L, R, t0, nt);
+    else if (vpl <= 4) topk_row<4>(p, L, R, t0, nt);
+    else if (vpl <= 8) topk_row<8>(p, L, R, t0, nt);
+    else topk_row<16>(p, L, R, t0, nt);
+  }
+  __syncthreads();
+
+  // 4. per expert: walk the tile's pairs in token order, giving each pair of the expert
+  //    its rank (tokens ascending; a token never holds one expert twice) and counting
+  //    them into the tile's histogram
   for (int e = tid; e < E; e += MNT) {
     int c = 0;
     for (int u = 0; u < nt; ++u)
-      for (int jj = 0; jj < K; ++jj) c += (R.sel[u][jj] == e);
+      for (int jj = 0; jj < K; ++jj)
+        if (R.sel[u][jj] == e) {
+          st_shared(L.lrank + (t0 + u) * K + jj, c);
+          ++c;
+        }
     st_shared(L.hist + tau * E + e, c);
   }
 
@@ -451,7 +476,7 @@ ETC_DEV int block_exclusive_scan(int v, int* tmp, int& total) {
   return before + x - v;
 }
 
-ETC_TASK void scan_task(const Args& p, const LayerArgs& L, int layer, Smem& sm) {
+ETC_TASK void scan_task(KArgs& p, KLayer& L, int layer, Smem& sm) {
   const int tid = threadIdx.x;
   const int E = p.E, K = p.K, n_rt = p.n_rt;
   ScanSmem& S = sm.u.s;
@@ -466,7 +491,7 @@ ETC_TASK void scan_task(const Args& p, const LayerArgs& L, int layer, Smem& sm) 
     for (int tau = tau0; tau < tau1; tau += 8) {
       int v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = (tau + u < tau1) ? L.hist[(tau + u) * E + e_t] : 0;
+      for (int u = 0; u < 8; ++u) v[u] = (tau + u < tau1) ? gp(L.hist)[(tau + u) * E + e_t] : 0;
 #pragma unroll
       for (int u = 0; u < 8; ++u) part += v[u];
     }
@@ -501,7 +526,7 @@ ETC_TASK void scan_task(const Args& p, const LayerArgs& L, int layer, Smem& sm) 
     for (int tau = tau0; tau < tau1; tau += 8) {
       int v[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = (tau + u < tau1) ? L.hist[(tau + u) * E + e_t] : 0;
+      for (int u = 0; u < 8; ++u) v[u] = (tau + u < tau1) ? gp(L.hist)[(tau + u) * E + e_t] : 0;
 #pragma unroll
       for (int u = 0; u < 8; ++u)
         if (tau + u < tau1) {
@@ -521,7 +546,7 @@ ETC_TASK void scan_task(const Args& p, const LayerArgs& L, int layer, Smem& sm) 
     const int gpc = cdiv(p.n1, nS);
     nS = cdiv(p.n1, gpc);
     const int ngu = RT * p.n1, nd = RT * p.n2 * nS, nf = n_rt;
-    const int base = (layer == 0) ? 0 : p.layer[layer - 1].plan[PL_NEXTBASE];
+    const int base = (layer == 0) ? 0 : gp(p.layer[layer - 1].plan)[PL_NEXTBASE];
     st_shared(L.plan + PL_RT, RT);
     st_shared(L.plan + PL_NGU, ngu);
     st_shared(L.plan + PL_ND, nd);
@@ -535,12 +560,12 @@ ETC_TASK void scan_task(const Args& p, const LayerArgs& L, int layer, Smem& sm) 
 // P(tau): the (token, slot) pairs of routing tile tau go to their rows of the
 // permutation: pair a = t*k + j of expert e lands at tile_off[tau][e] + its rank among
 // the tile's pairs of e (tokens ascending), so each expert's rows stay in token order.
-ETC_TASK void perm_task(const Args& p, const LayerArgs& L, int tau) {
+ETC_TASK void perm_task(KArgs& p, KLayer& L, int tau) {
   const int K = p.K, E = p.E;
   const int a0 = tau * BT * K, npairs = tile_rows(p, tau) * K;
   for (int i = threadIdx.x; i < npairs; i += MNT) {
     const int a = a0 + i;
-    const int r = L.tile_off[tau * E + L.topk_idx[a]] + L.lrank[a];
+    const int r = gp(L.tile_off)[tau * E + gp(L.topk_idx)[a]] + gp(L.lrank)[a];
     st_shared(L.sorted_assign + r, a);
     st_shared(L.pos + a, r);
   }
@@ -549,15 +574,15 @@ ETC_TASK void perm_task(const Args& p, const LayerArgs& L, int tau) {
 // ------------------------------------------------------------------ GU / D / F
 
 template <typename TE>
-ETC_TASK void gateup_task(const Args& p, const LayerArgs& L, int e, int m, int n, Smem& sm) {
+ETC_TASK void gateup_task(KArgs& p, KLayer& L, int e, int m, int n, Smem& sm) {
   using Tile = KTile<TE, MNT>;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w / Tile::WN, wn = w % Tile::WN;
   const int H = p.H, F = p.F, K = p.K;
   TileSmem& Ts = sm.u.t;
-  const int r0 = L.offsets[e] + m * BM;
-  const int valid = min(BM, L.counts[e] - m * BM);
-  for (int i = tid; i < BM; i += MNT) Ts.row_tok[i] = (i < valid) ? L.sorted_assign[r0 + i] / K : -1;
+  const int r0 = gp(L.offsets)[e] + m * BM;
+  const int valid = min(BM, gp(L.counts)[e] - m * BM);
+  for (int i = tid; i < BM; i += MNT) Ts.row_tok[i] = (i < valid) ? gp(L.sorted_assign)[r0 + i] / K : -1;
   __syncthreads();
 
   const TE* xq = static_cast<const TE*>(p.xq);
@@ -624,20 +649,20 @@ ETC_TASK void gateup_task(const Args& p, const LayerArgs& L, int e, int m, int n
 }
 
 template <typename TE>
-ETC_TASK void down_task(const Args& p, const LayerArgs& L, int e, int m, int n2i, int s, int gpc,
+ETC_TASK void down_task(KArgs& p, KLayer& L, int e, int m, int n2i, int s, int gpc,
                        Smem& sm) {
   using Tile = KTile<TE, MNT>;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w / Tile::WN, wn = w % Tile::WN;
   const int H = p.H, F = p.F, K = p.K;
   TileSmem& Ts = sm.u.t;
-  const int r0 = L.offsets[e] + m * BM;
-  const int valid = min(BM, L.counts[e] - m * BM);
+  const int r0 = gp(L.offsets)[e] + m * BM;
+  const int valid = min(BM, gp(L.counts)[e] - m * BM);
   for (int i = tid; i < BM; i += MNT) {
     if (i < valid) {
-      const int a = L.sorted_assign[r0 + i];
+      const int a = gp(L.sorted_assign)[r0 + i];
       Ts.row_tok[i] = a / K;
-      Ts.row_gate[i] = L.topk_w[a];
+      Ts.row_gate[i] = gp(L.topk_w)[a];
     } else {
       Ts.row_tok[i] = -1;
       Ts.row_gate[i] = 0.f;
@@ -690,7 +715,7 @@ ETC_TASK void down_task(const Args& p, const LayerArgs& L, int e, int m, int n2i
       const float g = Ts.row_gate[row];
 #pragma unroll
       for (int c = lane; c < BN2; c += 64)
-        if (c < ncols) atomicAdd(dst + c, g * ct[row * CSTR + c]);
+        if (c < ncols) red_add(dst + c, g * ct[row * CSTR + c]);
     }
   } else {
     // H is a multiple of 128: a pair of columns never straddles the edge
@@ -706,7 +731,7 @@ ETC_TASK void down_task(const Args& p, const LayerArgs& L, int e, int m, int n2i
 }
 
 template <typename TE>
-ETC_TASK void finalize_task(const Args& p, const LayerArgs& L, int tau) {
+ETC_TASK void finalize_task(KArgs& p, KLayer& L, int tau) {
   constexpr int EPC = 16 / (int)sizeof(TE);
   const int tid = threadIdx.x, H = p.H, K = p.K;
   const int t0 = tau * BT, nt = tile_rows(p, tau);
@@ -717,19 +742,19 @@ ETC_TASK void finalize_task(const Args& p, const LayerArgs& L, int tau) {
     if (p.combine == ETC_COMBINE_ATOMIC) {
 #pragma unroll
       for (int i = 0; i < EPC; i += 4) {
-        const float4 a = *reinterpret_cast<const float4*>(p.out_acc + (size_t)t * H + h + i);
-        v[i] = a.x; v[i + 1] = a.y; v[i + 2] = a.z; v[i + 3] = a.w;
+        const f32x4 a = gld<f32x4>(p.out_acc + (size_t)t * H + h + i);
+        v[i] = a[0]; v[i + 1] = a[1]; v[i + 2] = a[2]; v[i + 3] = a[3];
       }
     } else {
 #pragma unroll
       for (int i = 0; i < EPC; ++i) v[i] = 0.f;
       for (int j = 0; j < K; ++j) {  // slot order
-        const float g = L.topk_w[t * K + j];
-        const float* y = p.ybuf + (size_t)L.pos[t * K + j] * H + h;
+        const float g = gp(L.topk_w)[t * K + j];
+        const float* y = p.ybuf + (size_t)gp(L.pos)[t * K + j] * H + h;
 #pragma unroll
         for (int i = 0; i < EPC; i += 4) {
-          const float4 a = *reinterpret_cast<const float4*>(y + i);
-          v[i] += g * a.x; v[i + 1] += g * a.y; v[i + 2] += g * a.z; v[i + 3] += g * a.w;
+          const f32x4 a = gld<f32x4>(y + i);
+          v[i] += g * a[0]; v[i + 1] += g * a[1]; v[i + 2] += g * a[2]; v[i + 3] += g * a[3];
         }
       }
     }
@@ -749,13 +774,13 @@ ETC_TASK void finalize_task(const Args& p, const LayerArgs& L, int tau) {
 // Each queue hands out its tasks in the global order and has at least one workgroup
 // (Q <= workers), so the smallest waiting task always has its inputs claimed by
 // workgroups that are not waiting on it: the order stays deadlock-free.
-ETC_DEV int static_ticket(const Args& p) { return xcd_ticket(p.sched); }
+ETC_DEV int static_ticket(KArgs& p) { return xcd_ticket(p.sched); }
 
-ETC_DEV bool claim_static(const Args& p, Task& t, uint64_t deadline) {
+ETC_DEV bool claim_static(KArgs& p, Task& t, uint64_t deadline) {
   const int ticket = static_ticket(p);
   int base = 0;
   for (int l = 0; l < p.L; ++l) {
-    const LayerArgs& L = p.layer[l];
+    KLayer& L = p.layer[l];
     t.layer = l;
     if (ticket < base + p.n_rt) { t.kind = K_R; t.a = ticket - base; return true; }
     if (ticket == base + p.n_rt) { t.kind = K_S; return true; }
@@ -763,33 +788,33 @@ ETC_DEV bool claim_static(const Args& p, Task& t, uint64_t deadline) {
     if (off < p.n_rt) { t.kind = K_P; t.a = off; return true; }
     off -= p.n_rt;
     if (!spin_until_geq(L.ev_scan, 1, p.sched, deadline, 10 + l)) return false;
-    const int ngu = L.plan[PL_NGU], nd = L.plan[PL_ND], nf = L.plan[PL_NF], nS = L.plan[PL_NS];
+    const int ngu = gp(L.plan)[PL_NGU], nd = gp(L.plan)[PL_ND], nf = gp(L.plan)[PL_NF], nS = gp(L.plan)[PL_NS];
     if (off < ngu) {
       const int e = owner_expert(L.rt_base, p.E, off, p.n1);
-      const int me = L.rt_base[e + 1] - L.rt_base[e];
-      const int loc = off - L.rt_base[e] * p.n1;
+      const int me = gp(L.rt_base)[e + 1] - gp(L.rt_base)[e];
+      const int loc = off - gp(L.rt_base)[e] * p.n1;
       t.kind = K_GU; t.a = e; t.b = loc % me; t.c = loc / me;
       return true;
     }
     off -= ngu;
     if (off < nd) {
       const int e = owner_expert(L.rt_base, p.E, off, p.n2 * nS);
-      const int me = L.rt_base[e + 1] - L.rt_base[e];
-      const int loc = off - L.rt_base[e] * p.n2 * nS;
+      const int me = gp(L.rt_base)[e + 1] - gp(L.rt_base)[e];
+      const int loc = off - gp(L.rt_base)[e] * p.n2 * nS;
       t.kind = K_D; t.a = e; t.b = loc % me; t.c = (loc / me) % p.n2; t.d = loc / (me * p.n2);
       return true;
     }
     off -= nd;
     if (off < nf) { t.kind = K_F; t.a = off; return true; }
-    base = L.plan[PL_NEXTBASE];
+    base = gp(L.plan)[PL_NEXTBASE];
   }
   t.kind = K_NONE;
   return true;
 }
 
 // Dynamic: the next queue slot; slots below n_rt are the first layer's R tasks.
-ETC_DEV bool claim_dynamic(const Args& p, Task& t, uint64_t deadline) {
-  const int slot = atomicAdd(p.sched + W_QHEAD, 1);
+ETC_DEV bool claim_dynamic(KArgs& p, Task& t, uint64_t deadline) {
+  const int slot = ev_add_relaxed(p.sched + W_QHEAD, 1);
   if (slot < p.n_rt) {
     t.kind = K_R; t.layer = 0; t.a = slot;
     return true;
@@ -817,8 +842,8 @@ ETC_DEV bool claim_dynamic(const Args& p, Task& t, uint64_t deadline) {
 }
 
 // Static mode: wait until the task's inputs are complete (thread 0).
-ETC_DEV bool wait_deps(const Args& p, const Task& t, uint64_t deadline) {
-  const LayerArgs& L = p.layer[t.layer];
+ETC_DEV bool wait_deps(KArgs& p, const Task& t, uint64_t deadline) {
+  KLayer& L = p.layer[t.layer];
   switch (t.kind) {
     case K_R:
       if (t.layer == 0) return true;
@@ -830,13 +855,13 @@ ETC_DEV bool wait_deps(const Args& p, const Task& t, uint64_t deadline) {
     case K_GU:
       return spin_until_geq(L.ev_perm, p.n_rt, p.sched, deadline, 25);
     case K_D: {
-      const int gpc = L.plan[PL_GPC];
-      const int rt = L.rt_base[t.a] + t.b;
+      const int gpc = gp(L.plan)[PL_GPC];
+      const int rt = gp(L.rt_base)[t.a] + t.b;
       const int need = min(gpc, p.n1 - t.d * gpc);
       return spin_until_geq(L.ev_gu + rt * p.n1 + t.d, need, p.sched, deadline, 22);
     }
     case K_F: {
-      const int target = tile_rows(p, t.a) * p.K * p.n2 * L.plan[PL_NS];
+      const int target = tile_rows(p, t.a) * p.K * p.n2 * gp(L.plan)[PL_NS];
       return spin_until_geq(L.ev_comb + t.a, target, p.sched, deadline, 23);
     }
     default:
@@ -846,8 +871,8 @@ ETC_DEV bool wait_deps(const Args& p, const Task& t, uint64_t deadline) {
 
 // Enqueue n tasks (dynamic mode); every thread of the workgroup calls this.
 template <typename Gen>
-ETC_DEV void push_many(const Args& p, Smem& sm, int n, Gen gen) {
-  if (threadIdx.x == 0) sm.ibuf[0] = p.n_rt + atomicAdd(p.sched + W_QTAIL, n);
+ETC_DEV void push_many(KArgs& p, Smem& sm, int n, Gen gen) {
+  if (threadIdx.x == 0) sm.ibuf[0] = p.n_rt + ev_add_relaxed(p.sched + W_QTAIL, n);
   __syncthreads();
   const int base = sm.ibuf[0];
   // the results these tasks read were published (publish_shared) before the call
@@ -856,15 +881,15 @@ ETC_DEV void push_many(const Args& p, Smem& sm, int n, Gen gen) {
 }
 
 // The results the task reads were published (publish_shared) before the call.
-ETC_DEV void push_one(const Args& p, const Task& t) {
-  const int slot = p.n_rt + atomicAdd(p.sched + W_QTAIL, 1);
+ETC_DEV void push_one(KArgs& p, const Task& t) {
+  const int slot = p.n_rt + ev_add_relaxed(p.sched + W_QTAIL, 1);
   q_store_relaxed(p.queue + slot, enc(t));
 }
 
 // After S: static mode publishes ev_scan; dynamic mode enqueues every permutation task
 // and adds the layer's task count to the queue total.
-ETC_DEV void after_scan(const Args& p, int layer, Smem& sm) {
-  const LayerArgs& L = p.layer[layer];
+ETC_DEV void after_scan(KArgs& p, int layer, Smem& sm) {
+  KLayer& L = p.layer[layer];
   publish_shared();
   if (threadIdx.x == 0) ev_store_relaxed(L.ev_scan, 1);  // both modes: the event tensor is complete
   if (p.mode == ETC_SCHED_STATIC) return;
@@ -875,9 +900,9 @@ ETC_DEV void after_scan(const Args& p, int layer, Smem& sm) {
   });
   if (threadIdx.x == 0) {
     // the plan words are in global memory, written by this thread before publish_shared
-    const int added = p.n_rt + L.plan[PL_NGU] + L.plan[PL_ND] + L.plan[PL_NF] +
+    const int added = p.n_rt + gp(L.plan)[PL_NGU] + gp(L.plan)[PL_ND] + gp(L.plan)[PL_NF] +
                       (layer + 1 < p.L ? p.n_rt : 0) + (layer == 0 ? p.n_rt : 0);
-    atomicAdd(p.sched + W_QTOTAL, added);
+    ev_add_relaxed(p.sched + W_QTOTAL, added);
     ev_add(p.sched + W_PLANNED, 1);
   }
 }
@@ -885,7 +910,7 @@ ETC_DEV void after_scan(const Args& p, int layer, Smem& sm) {
 // One task of either scheduler: its body, then its signals (and, in dynamic mode, the
 // tasks its signal releases).  Every thread of the workgroup calls this.
 template <typename TE>
-ETC_DEV void run_task(const Args& p, const LayerArgs& L, const Task& t, Smem& sm) {
+ETC_DEV void run_task(KArgs& p, KLayer& L, const Task& t, Smem& sm) {
   const int tid = threadIdx.x;
   if (t.kind == K_R) {
     route_task<TE>(p, L, t.a, sm);
@@ -915,10 +940,10 @@ ETC_DEV void run_task(const Args& p, const LayerArgs& L, const Task& t, Smem& sm
     __syncthreads();
     if (sm.flag) {  // the permutation is complete: every gate/up task is ready
       const int layer = t.layer, n1 = p.n1, E = p.E;
-      push_many(p, sm, L.plan[PL_NGU], [&](int i) {
+      push_many(p, sm, gp(L.plan)[PL_NGU], [&](int i) {
         const int e = owner_expert(L.rt_base, E, i, n1);
-        const int me = L.rt_base[e + 1] - L.rt_base[e];
-        const int loc = i - L.rt_base[e] * n1;
+        const int me = gp(L.rt_base)[e + 1] - gp(L.rt_base)[e];
+        const int loc = i - gp(L.rt_base)[e] * n1;
         Task g;
         g.kind = K_GU; g.layer = layer; g.a = e; g.b = loc % me; g.c = loc / me; g.d = 0;
         return g;
@@ -927,10 +952,10 @@ ETC_DEV void run_task(const Args& p, const LayerArgs& L, const Task& t, Smem& sm
   } else if (t.kind == K_GU) {
     gateup_task<TE>(p, L, t.a, t.b, t.c, sm);
     publish_shared();
-    const int gpc = L.plan[PL_GPC];
+    const int gpc = gp(L.plan)[PL_GPC];
     const int s = t.c / gpc;
     if (tid == 0) {
-      const int rt = L.rt_base[t.a] + t.b;
+      const int rt = gp(L.rt_base)[t.a] + t.b;
       const int need = min(gpc, p.n1 - s * gpc);
       const int old = (p.mode == ETC_SCHED_DYNAMIC) ? ev_add_acquire(L.ev_gu + rt * p.n1 + s, 1)
                                                     : ev_add_relaxed(L.ev_gu + rt * p.n1 + s, 1);
@@ -946,13 +971,13 @@ ETC_DEV void run_task(const Args& p, const LayerArgs& L, const Task& t, Smem& sm
       });
     }
   } else if (t.kind == K_D) {
-    down_task<TE>(p, L, t.a, t.b, t.c, t.d, L.plan[PL_GPC], sm);
+    down_task<TE>(p, L, t.a, t.b, t.c, t.d, gp(L.plan)[PL_GPC], sm);
     // The results are published once for the whole task, then one signal goes out per
     // run of rows in the same routing tile (rows are token-sorted; a tile's rows can
     // span dozens of routing tiles).  In dynamic mode the signals acquire, for the last
     // arriver that enqueues the finalize task.
     publish_shared();
-    const int valid = min(BM, L.counts[t.a] - t.b * BM);
+    const int valid = min(BM, gp(L.counts)[t.a] - t.b * BM);
     if (tid < valid) {
       const int tau = sm.u.t.row_tok[tid] / BT;
       if (tid == 0 || sm.u.t.row_tok[tid - 1] / BT != tau) {
@@ -960,7 +985,7 @@ ETC_DEV void run_task(const Args& p, const LayerArgs& L, const Task& t, Smem& sm
         while (tid + len < valid && sm.u.t.row_tok[tid + len] / BT == tau) ++len;
         const int old = (p.mode == ETC_SCHED_DYNAMIC) ? ev_add_acquire(L.ev_comb + tau, len)
                                                       : ev_add_relaxed(L.ev_comb + tau, len);
-        const int target = tile_rows(p, tau) * p.K * p.n2 * L.plan[PL_NS];
+        const int target = tile_rows(p, tau) * p.K * p.n2 * gp(L.plan)[PL_NS];
         if (p.mode == ETC_SCHED_DYNAMIC && old + len == target) {
           Task f;
           f.kind = K_F; f.layer = t.layer; f.a = tau; f.b = f.c = f.d = 0;
@@ -999,7 +1024,7 @@ __global__ __launch_bounds__(MNT) void moe_kernel(Args pk) {
     for (int i = tid; i < (int)(sizeof(Args) / 4); i += MNT) dst[i] = src[i];
   }
   __syncthreads();
-  const Args& p = p_lds;
+  KArgs& p = *(KArgs*)&p_lds;
   const uint64_t deadline = now_ticks() + p.timeout_ticks;
 
   const bool tracing = (p.flags & ETC_FLAG_TRACE) != 0;
@@ -1021,13 +1046,13 @@ __global__ __launch_bounds__(MNT) void moe_kernel(Args pk) {
     const Task t = sm.task;
     __syncthreads();
     if (t.kind == K_NONE) break;
-    const LayerArgs& L = p.layer[t.layer];
+    KLayer& L = p.layer[t.layer];
     run_task<TE>(p, L, t, sm);
     if (tracing && tid == 0) {
       const uint64_t t_end = now_ticks();
-      const int i = atomicAdd(p.sched + W_TRACE, 1);
+      const int i = ev_add_relaxed(p.sched + W_TRACE, 1);
       if (i < p.trace_cap) {
-        unsigned long long* r = p.trace + 4 * (size_t)i;
+        ETC_GLOBAL unsigned long long* r = gp(p.trace) + 4 * (size_t)i;
         r[0] = (unsigned long long)enc(t);
         r[1] = t_claim;
         r[2] = (unsigned long long)blockIdx.x | ((unsigned long long)(uint32_t)(t_run - t_claim) << 32);
@@ -1038,11 +1063,11 @@ __global__ __launch_bounds__(MNT) void moe_kernel(Args pk) {
 
   // the last workgroup out clears the event counters and control words
   wg_publish();
-  if (tid == 0) sm.flag = (atomicAdd(p.sched + W_EXIT, 1) == (int)gridDim.x - 1) ? 1 : 0;
+  if (tid == 0) sm.flag = (ev_add_relaxed(p.sched + W_EXIT, 1) == (int)gridDim.x - 1) ? 1 : 0;
   __syncthreads();
   if (sm.flag && !(p.flags & ETC_FLAG_KEEP_COUNTERS)) {
     for (int l = 0; l < p.L; ++l) {
-      const LayerArgs& L = p.layer[l];
+      KLayer& L = p.layer[l];
       if (tid == 0) {
         ev_store_relaxed(L.ev_route, 0);
         ev_store_relaxed(L.ev_scan, 0);

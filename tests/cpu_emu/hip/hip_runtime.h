@@ -112,6 +112,24 @@ inline T max(T a, T b) { return a < b ? b : a; }
 
 inline float __uint_as_float(unsigned u) { float f; memcpy(&f, &u, 4); return f; }
 inline unsigned __float_as_uint(float f) { unsigned u; memcpy(&u, &f, 4); return u; }
+inline float __int_as_float(int u) { float f; memcpy(&f, &u, 4); return f; }
+inline int __float_as_int(float f) { int u; memcpy(&u, &f, 4); return u; }
+
+// DPP moves used by the kernels: quad permutations and the two row mirrors
+inline int emu_update_dpp(int old, int src, int ctrl, int row_mask, int bank_mask, bool bc) {
+  (void)old; (void)row_mask; (void)bank_mask; (void)bc;
+  const int lane = emu_lane();
+  int from;
+  if (ctrl < 0x100) from = (lane & ~3) | ((ctrl >> (2 * (lane & 3))) & 3);
+  else if (ctrl == 0x140) from = (lane & ~15) | (15 - (lane & 15));
+  else if (ctrl == 0x141) from = (lane & ~7) | (7 - (lane & 7));
+  else {
+    fprintf(stderr, "unsupported DPP control 0x%x\n", ctrl);
+    abort();
+  }
+  return emu_exchange(src, from);
+}
+#define __builtin_amdgcn_update_dpp(old, src, ctrl, rm, bm, bc) emu_update_dpp((old), (src), (ctrl), (rm), (bm), (bc))
 
 inline int atomicAdd(int* p, int v) { return __atomic_fetch_add(p, v, __ATOMIC_SEQ_CST); }
 inline float atomicAdd(float* p, float v) {
@@ -125,6 +143,9 @@ inline float atomicAdd(float* p, float v) {
 }
 
 #define __HIP_MEMORY_SCOPE_AGENT 3
+// host memory has one address space
+#define ETC_GLOBAL
+#define ETC_LDS
 #define __hip_atomic_load(p, order, scope) __atomic_load_n((p), (order))
 #define __hip_atomic_store(p, v, order, scope) __atomic_store_n((p), (v), (order))
 #define __hip_atomic_fetch_add(p, v, order, scope) __atomic_fetch_add((p), (v), (order))
