@@ -32,8 +32,12 @@ ETC_DEV float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 // float -> bfloat16 bits, round to nearest even (gfx950 converts in hardware, two values
 // per v_cvt_pk_bf16_f32)
 ETC_DEV uint32_t f32_to_bf16_bits(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+// two values in one v_cvt_pk_bf16_f32 (converting them one at a time costs a conversion
+// each plus the shifts and ORs that pack them)
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 ETC_DEV uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 template <typename TE>
@@ -160,12 +164,17 @@ ETC_DEV void st_shared(float* p, float v) { st_shared(reinterpret_cast<uint32_t*
 ETC_DEV void st_shared8(void* p, uint64_t v) {
   __hip_atomic_store(gp(static_cast<uint64_t*>(p)), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// 16 bytes at a 16-byte aligned address, as two 8-byte stores
-ETC_DEV void st_shared16(void* p, const uint4& v) {
-  uint64_t* q = static_cast<uint64_t*>(p);
-  st_shared8(q, (uint64_t)v.x | ((uint64_t)v.y << 32));
-  st_shared8(q + 1, (uint64_t)v.z | ((uint64_t)v.w << 32));
+// 16 bytes at byte offset off (16-byte aligned, per lane) from the wave-uniform base, as
+// one buffer_store_dwordx4 with the same device-scope policy (sc1).  Two 8-byte stores
+// would leave every 16-byte piece half written by each instruction: byte-masked partial
+// writes of the cache lines, which cost far more than whole 64-byte pieces.
+constexpr int BUF_DESC_WORD3 = 0x00020000;  // raw 32-bit buffer access (gfx9 family)
+constexpr int CPOL_SC1 = 16;
+ETC_DEV void st_shared16(void* base, uint32_t off, const u32x4& v) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, (short)0, 0x7fffffff, BUF_DESC_WORD3);
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, CPOL_SC1);
 }
+
 // Every thread's stores have completed (so every shared result of the workgroup has
 // reached the point of coherence), then the workgroup meets.
 ETC_DEV void publish_shared() {

@@ -16,10 +16,12 @@
 //   R(tau)         RMSNorm, router logits, top-k, softmax for 16 tokens; ranks of their
 //                  (token, slot) pairs inside the tile and the tile's expert histogram
 //                  -> ev_route[l] += 1.  For l > 0 it waits ev_done[l-1][tau] >= 1.
-//   S              waits ev_route[l] >= n_rt: counts, exclusive scan, row tiles per
-//                  expert, first sorted row of every (routing tile, expert) block;
-//                  sizes the down split (nS chunks of GPC gate/up tiles) from the actual
-//                  number of row tiles; -> ev_scan[l] = 1.
+//   S              run by the R task whose signal brings ev_route[l] to n_rt: counts,
+//                  exclusive scan, row tiles per expert, first sorted row of every
+//                  (routing tile, expert) block; sizes the down split (nS chunks of GPC
+//                  gate/up tiles) from the actual number of row tiles; -> ev_scan[l] = 1.
+//                  With at most PERM_INLINE_RT routing tiles it also scatters the
+//                  permutation (there are no P tasks) -> ev_perm[l] = n_rt.
 //   P(tau)         waits ev_scan[l] >= 1: places the (token, slot) pairs of routing
 //                  tile tau in the permutation -> ev_perm[l] += 1.
 //   GU(e, m, n)    waits ev_perm[l] >= n_rt: gate/up tile of expert e rows m*128.. and
@@ -29,11 +31,11 @@
 //                  ev_comb[l][tau] += its rows in tau, per routing tile tau it touches.
 //   F(tau)         waits ev_comb[l][tau] >= rows(tau) * k * n2 * nS; writes the layer
 //                  output rows -> ev_done[l][tau] = 1.
-// Static mode: workgroups draw tickets of the order [R.. S P.. GU.. D.. F..] per layer
+// Static mode: workgroups draw tickets of the order [R.. P.. GU.. D.. F..] per layer
 // and spin on each task's counter.  Dynamic mode: a queue of ready tasks; the R tasks of
-// the first layer are implicit in slots 0..n_rt-1, the last R runs S inline, S enqueues
-// the P tasks, the last P enqueues the GU tasks, and whichever signal completes a counter
-// enqueues the tasks it releases.
+// the first layer are implicit in slots 0..n_rt-1, S enqueues the P tasks (or the GU
+// tasks when it scattered the permutation itself), the last P enqueues the GU tasks,
+// and whichever signal completes a counter enqueues the tasks it releases.
 // The token count T is a kernel argument; nothing in the code depends on its value.
 #include <float.h>
 #include <stdlib.h>
@@ -56,6 +58,9 @@ constexpr int MNT = 512, NWAVE = MNT / 64;
 constexpr int H_ALIGN = 128, F_ALIGN = 64;
 constexpr int MAX_WORKERS = 2048;
 constexpr int MAX_TOKENS = 262143;  // task fields are 14 bits
+// Up to this many routing tiles (T <= 64) the scan task also scatters the permutation
+// (at most 64 * k pairs): separate P tasks would only add a hand-off to a short path.
+constexpr int PERM_INLINE_RT = 4;
 
 // Task bodies are separate functions: each gets its own register allocation instead of
 // sharing one with the scheduler loop and every other task (inlined together they spill
@@ -121,6 +126,7 @@ struct Args {
   int mode, combine;
   unsigned flags;
   int n_rt, n1, n2, workers, max_rt, n_rt_cap, queue_len;
+  int n_perm;  // P tasks per layer: n_rt, or 0 when S scatters the permutation itself
   uint64_t timeout_ticks;
   void* xq;        // [T][H] normalised input in storage precision
   void* hbuf;      // [T*k][F] SwiGLU output, rows in sorted order
@@ -139,14 +145,19 @@ typedef const ETC_LDS Args KArgs;
 typedef const ETC_LDS LayerArgs KLayer;
 
 struct RouteSmem {
+  static constexpr int GCHUNK = 16384;  // gamma values staged at a time
   float part[BT * 512];  // [KS][BT][E] partial logits, KS * E <= 512
   float lg[BT][MAXE];
+  alignas(16) float gam[GCHUNK];
   float rs[BT];
+  unsigned emask[MAXE];  // tokens of the tile that selected each expert
+  float bias[MAXE];
   int sel[BT][MAXK];
 };
 struct ScanSmem {
   int off[MAXE + 1];
   int rtb[MAXE + 1];
+  int toff[PERM_INLINE_RT * MAXE];  // tile_off when S scatters the permutation itself
   int tmp[NWAVE];
   int part[MNT];  // per-thread partial counts over a chunk of routing tiles
 };
@@ -168,17 +179,15 @@ struct Smem {
 };
 
 template <typename TE>
-ETC_DEV uint4 pack16(const float* v);
+ETC_DEV u32x4 pack16(const float* v);
 template <>
-ETC_DEV uint4 pack16<bf16>(const float* v) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = f32_to_bf16_bits(v[2 * i]) | (f32_to_bf16_bits(v[2 * i + 1]) << 16);
-  return make_uint4(w[0], w[1], w[2], w[3]);
+ETC_DEV u32x4 pack16<bf16>(const float* v) {
+  return u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+               pack_bf16x2(v[6], v[7])};
 }
 template <>
-ETC_DEV uint4 pack16<float>(const float* v) {
-  return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3]));
+ETC_DEV u32x4 pack16<float>(const float* v) {
+  return u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
 }
 
 ETC_DEV int tile_rows(KArgs& p, int tau) { return min(BT, p.T - tau * BT); }
@@ -199,12 +208,13 @@ ETC_DEV int owner_expert(const int* rt_base, int E, int idx, int mult) {
 // tile's per-expert ranks and histogram [P3 §5.5 Obstacle 1: the counts that set the
 // event targets come from here].
 //
-// Router precision.  logits[t][e] = sum_h xn[t][h] * W_r[e][h] (+ b[e]) with
-// xn = x * rs * gamma in float32.  On the matrix cores xn is split into three bfloat16
-// parts (hi = bf16(xn), mid = bf16(xn - hi), lo = bf16(xn - hi - mid)); the product of
-// each part with a bfloat16 weight is exact in float32 and the parts accumulate
-// separately, so the dot product keeps float32 accuracy.  Float32 layers use the float32
-// MFMA on xn directly.
+// Router precision.  logits[t][e] = rs_t * sum_h v[t][h] * W_r[e][h] (+ b[e]) with
+// v = x * gamma in float32 and rs_t = 1/sqrt(mean_h x[t][h]^2 + eps), which is
+// sum_h xn[t][h] W_r[e][h] for xn = x * rs * gamma up to float32 rounding.  On the matrix
+// cores v is split into three bfloat16 parts (hi = bf16(v), mid = bf16(v - hi),
+// lo = bf16(v - hi - mid)); the product of each part with a bfloat16 weight is exact in
+// float32 and the parts accumulate separately, so the dot product keeps float32 accuracy.
+// Float32 layers use the float32 MFMA on v directly.
 //
 // Work split.  NB = ceil(E/16) blocks of 16 experts; a wave owns NBW of them (the next
 // power of two >= NB, at most 4) over one of KS = 8 / ceil(NB/NBW) K slices, so every
@@ -238,68 +248,84 @@ struct RouterSplit<1> {  // float32 layers: the values themselves
   }
 };
 
-// Wave item: expert blocks g*NBW .. g*NBW+NBW-1 over K steps [s0, s1).  Writes the
-// partial logits of its K slice to R.part[ks][t][e].
+// Wave item: expert blocks g*NBW .. g*NBW+NBW-1 over the wave's share of every K chunk,
+// on v = x * gamma (the 1/rms factor of each token is applied to its logits).
+// gamma is staged in LDS one chunk of GCHUNK values at a time (every wave calls this with
+// the same NBW, so the barriers around the staging are reached by the whole workgroup).
+// Writes the partial logits of its K slice to R.part[ks][t][e].
 template <typename TE, int NBW>
-ETC_DEV void router_item(KArgs& p, KLayer& L, RouteSmem& R, int t0, int nt, int g,
-                         int ks, int KS) {
+ETC_DEV void router_item(KArgs& p, KLayer& L, RouteSmem& R, int t0, int nt, int g, int ks,
+                         int KS) {
   constexpr int EPC = 16 / (int)sizeof(TE);  // values per 16-byte chunk
   constexpr int KSTEP = 4 * EPC;              // K per MFMA step (four lane groups)
   constexpr int NSPLIT = sizeof(TE) == 2 ? 3 : 1;
-  constexpr int U = NBW <= 2 ? 4 : 2;         // K steps whose loads are in flight together
-  const int lane = threadIdx.x & 63, row = lane & 15, grp = lane >> 4;
+  constexpr int U = NBW <= 2 ? 8 : 4;         // K steps whose loads are in flight together
+  const int tid = threadIdx.x, lane = tid & 63, row = lane & 15, grp = lane >> 4;
   const int H = p.H, E = p.E;
-  const int nsteps = H / KSTEP;
-  const int s0 = ks * nsteps / KS, s1 = (ks + 1) * nsteps / KS;
   // rows past the tile's tokens repeat its last token and experts past E repeat the last
   // expert, so every load is unconditional; those results are never used
   const int tr = row < nt ? row : nt - 1;
   const TE* xrow = static_cast<const TE*>(L.in) + (size_t)(t0 + tr) * H + grp * EPC;
-  const float* grow = L.gamma + grp * EPC;
   const TE* wbase = static_cast<const TE*>(L.w_router) + grp * EPC;
+  // the first expert group also writes xn = v * rs in storage precision (xq); rows past
+  // the tile's tokens write their copy of the last token's values to its row
+  TE* xqtile = static_cast<TE*>(p.xq) + (size_t)t0 * H;
+  const uint32_t xqoff = (uint32_t)((tr * H + grp * EPC) * (int)sizeof(TE));
+  const bool put = g == 0;
+  const float rs = R.rs[tr];
   int woff[NBW];
 #pragma unroll
   for (int b = 0; b < NBW; ++b) woff[b] = min((g * NBW + b) * 16 + row, E - 1) * H;
-  TE* xqrow = static_cast<TE*>(p.xq) + (size_t)(t0 + row) * H + grp * EPC;
-  const bool put = g == 0 && row < nt;
-  const float rs = R.rs[tr];
   f32x4 acc[NBW][NSPLIT];
 #pragma unroll
   for (int b = 0; b < NBW; ++b)
 #pragma unroll
     for (int q = 0; q < NSPLIT; ++q) acc[b][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto steps = [&](int s, auto nst) ETC_INLINE {
-    constexpr int N = decltype(nst)::value;
-    u32x4 xv[N], wv[N][NBW];
-    f32x4 gv[N][EPC / 4];
-    static_for<N>([&](auto u) ETC_INLINE {
-      const int k = (s + u) * KSTEP;
-      xv[u] = gld<u32x4>(xrow + k);
-      static_for<EPC / 4>([&](auto q) ETC_INLINE { gv[u][q] = gld<f32x4>(grow + k + 4 * q); });
-      static_for<NBW>([&](auto b) ETC_INLINE { wv[u][b] = gld<u32x4>(wbase + woff[b] + k); });
-    });
-    static_for<N>([&](auto u) ETC_INLINE {
-      const int k = (s + u) * KSTEP;
-      float v[EPC];
-      expand16(xv[u], v, (const TE*)nullptr);
-      static_for<EPC / 4>([&](auto q) ETC_INLINE {
-        v[4 * q] = v[4 * q] * rs * gv[u][q].x;
-        v[4 * q + 1] = v[4 * q + 1] * rs * gv[u][q].y;
-        v[4 * q + 2] = v[4 * q + 2] * rs * gv[u][q].z;
-        v[4 * q + 3] = v[4 * q + 3] * rs * gv[u][q].w;
+  for (int kc = 0; kc < H; kc += RouteSmem::GCHUNK) {
+    const int len = min(RouteSmem::GCHUNK, H - kc);
+    __syncthreads();  // every wave is done with the previous chunk
+    for (int i = tid * 4; i < len; i += MNT * 4)
+      *reinterpret_cast<f32x4*>(&R.gam[i]) = gld<f32x4>(L.gamma + kc + i);
+    __syncthreads();
+    const int nsteps = len / KSTEP;
+    const int s0 = ks * nsteps / KS, s1 = (ks + 1) * nsteps / KS;
+    auto steps = [&](int s, auto nst) ETC_INLINE {
+      constexpr int N = decltype(nst)::value;
+      u32x4 xv[N], wv[N][NBW];
+      static_for<N>([&](auto u) ETC_INLINE {
+        const int k = kc + (s + u) * KSTEP;
+        xv[u] = gld<u32x4>(xrow + k);
+        static_for<NBW>([&](auto b) ETC_INLINE { wv[u][b] = gld<u32x4>(wbase + woff[b] + k); });
       });
-      if (put) st_shared16(xqrow + k, pack16<TE>(v));
-      u32x4 a[NSPLIT];
-      RouterSplit<NSPLIT>::run(v, a);
-      static_for<NBW>([&](auto b) ETC_INLINE {
-        static_for<NSPLIT>([&](auto q) ETC_INLINE { mma16(acc[b][q], a[q], wv[u][b], (const TE*)nullptr); });
+      static_for<N>([&](auto u) ETC_INLINE {
+        const int kl = (s + u) * KSTEP + grp * EPC;  // within the chunk
+        float v[EPC];
+        expand16(xv[u], v, (const TE*)nullptr);
+        static_for<EPC / 4>([&](auto q) ETC_INLINE {
+          const f32x4 gq = *reinterpret_cast<const f32x4*>(&R.gam[kl + 4 * q]);
+          v[4 * q] *= gq.x;
+          v[4 * q + 1] *= gq.y;
+          v[4 * q + 2] *= gq.z;
+          v[4 * q + 3] *= gq.w;
+        });
+        if (put) {
+          float xn[EPC];
+#pragma unroll
+          for (int i = 0; i < EPC; ++i) xn[i] = v[i] * rs;
+          st_shared16(xqtile, xqoff + (uint32_t)((kc + (s + u) * KSTEP) * (int)sizeof(TE)), pack16<TE>(xn));
+        }
+        u32x4 a[NSPLIT];
+        RouterSplit<NSPLIT>::run(v, a);
+        static_for<NBW>([&](auto b) ETC_INLINE {
+          static_for<NSPLIT>([&](auto q) ETC_INLINE { mma16(acc[b][q], a[q], wv[u][b], (const TE*)nullptr); });
+        });
       });
-    });
-  };
-  int s = s0;
-  for (; s + U <= s1; s += U) steps(s, std::integral_constant<int, U>{});
-  for (; s < s1; ++s) steps(s, std::integral_constant<int, 1>{});
+    };
+    int s = s0;
+    for (; s + U <= s1; s += U) steps(s, std::integral_constant<int, U>{});
+    for (; s < s1; ++s) steps(s, std::integral_constant<int, 1>{});
+  }
 
   // result element (token grp*4+i, expert block column row) of each block
 #pragma unroll
@@ -358,6 +384,7 @@ ETC_DEV void topk_row(KArgs& p, KLayer& L, RouteSmem& R, int t0, int nt) {
     st_shared(L.topk_idx + t * K + j, mine_e);
     st_shared(L.topk_w + t * K + j, z / zsum);
     R.sel[tt][j] = mine_e;
+    atomicOr(&R.emask[mine_e], 1u << tt);
   }
 }
 
@@ -369,6 +396,11 @@ ETC_TASK void route_task(KArgs& p, KLayer& L, int tau, Smem& sm) {
   const int H = p.H, E = p.E, K = p.K;
   const int t0 = tau * BT, nt = tile_rows(p, tau);
   RouteSmem& R = sm.u.r;
+
+  for (int e = tid; e < E; e += MNT) {
+    R.emask[e] = 0u;
+    R.bias[e] = L.bias ? gp(L.bias)[e] : 0.f;
+  }
 
   // 1. inverse RMS of each token: 32 lanes per token, each summing the squares of every
   //    32nd chunk of the row (eight chunks in flight), then a butterfly over the 32 lanes
@@ -402,7 +434,7 @@ ETC_TASK void route_task(KArgs& p, KLayer& L, int tau, Smem& sm) {
   }
   __syncthreads();
 
-  // 2. partial logits per (expert group, K slice), one item per wave; xq on the way
+  // 2. partial logits per (expert group, K slice), one item per wave
   const int NB = cdiv(E, 16);
   const int NBW = NB <= 1 ? 1 : (NB <= 2 ? 2 : 4);
   const int KS = NWAVE / cdiv(NB, NBW);
@@ -412,12 +444,18 @@ ETC_TASK void route_task(KArgs& p, KLayer& L, int tau, Smem& sm) {
     else if (NBW == 2) router_item<TE, 2>(p, L, R, t0, nt, g, ks, KS);
     else router_item<TE, 4>(p, L, R, t0, nt, g, ks, KS);
   }
+  // clear this tile's accumulator rows for the atomic combine: the last global loads of
+  // the task are done, so these stores drain while the rest of the task runs
+  if (p.combine == ETC_COMBINE_ATOMIC) {
+    uint64_t* acc = reinterpret_cast<uint64_t*>(p.out_acc + (size_t)t0 * H);
+    for (int i = tid; i < nt * H / 2; i += MNT) st_shared8(acc + i, 0);
+  }
   __syncthreads();
   for (int o = tid; o < nt * E; o += MNT) {
     const int tt = o / E, e = o - tt * E;
     float v = 0.f;
     for (int k = 0; k < KS; ++k) v += R.part[(k * BT + tt) * E + e];
-    R.lg[tt][e] = v + (L.bias ? gp(L.bias)[e] : 0.f);
+    R.lg[tt][e] = R.rs[tt] * v + R.bias[e];
   }
   __syncthreads();
 
@@ -432,25 +470,14 @@ ETC_TASK void route_task(KArgs& p, KLayer& L, int tau, Smem& sm) {
   }
   __syncthreads();
 
-  // 4. per expert: walk the tile's pairs in token order, giving each pair of the expert
-  //    its rank (tokens ascending; a token never holds one expert twice) and counting
-  //    them into the tile's histogram
-  for (int e = tid; e < E; e += MNT) {
-    int c = 0;
-    for (int u = 0; u < nt; ++u)
-      for (int jj = 0; jj < K; ++jj)
-        if (R.sel[u][jj] == e) {
-          st_shared(L.lrank + (t0 + u) * K + jj, c);
-          ++c;
-        }
-    st_shared(L.hist + tau * E + e, c);
+  // 4. rank of each pair among the tile's pairs of its expert (tokens ascending; a token
+  //    never holds one expert twice) and the tile's histogram, from the per-expert masks
+  //    of the tile's tokens that selected it
+  for (int a = tid; a < nt * K; a += MNT) {
+    const int tt = a / K, j = a - tt * K;
+    st_shared(L.lrank + t0 * K + a, __popc(R.emask[R.sel[tt][j]] & ((1u << tt) - 1u)));
   }
-
-  // 5. clear this tile's accumulator rows for the atomic combine
-  if (p.combine == ETC_COMBINE_ATOMIC) {
-    uint64_t* acc = reinterpret_cast<uint64_t*>(p.out_acc + (size_t)t0 * H);
-    for (int i = tid; i < nt * H / 2; i += MNT) st_shared8(acc + i, 0);
-  }
+  for (int e = tid; e < E; e += MNT) st_shared(L.hist + tau * E + e, __popc(R.emask[e]));
 }
 
 // ------------------------------------------------------------------ S: scan and permutation
@@ -531,6 +558,7 @@ ETC_TASK void scan_task(KArgs& p, KLayer& L, int layer, Smem& sm) {
       for (int u = 0; u < 8; ++u)
         if (tau + u < tau1) {
           st_shared(L.tile_off + (tau + u) * E + e_t, run);
+          if (p.n_perm == 0) S.toff[(tau + u) * E + e_t] = run;
           run += v[u];
         }
     }
@@ -553,7 +581,18 @@ ETC_TASK void scan_task(KArgs& p, KLayer& L, int layer, Smem& sm) {
     st_shared(L.plan + PL_NF, nf);
     st_shared(L.plan + PL_NS, nS);
     st_shared(L.plan + PL_GPC, gpc);
-    st_shared(L.plan + PL_NEXTBASE, base + n_rt + 1 + n_rt + ngu + nd + nf);
+    st_shared(L.plan + PL_NEXTBASE, base + n_rt + p.n_perm + ngu + nd + nf);
+  }
+  // few routing tiles: the permutation scatter of every tile here (what P(tau) does)
+  if (p.n_perm == 0) {
+    __syncthreads();
+    const int npairs = p.T * K;
+    for (int a = threadIdx.x; a < npairs; a += MNT) {
+      const int tau = a / (BT * K);
+      const int r = S.toff[tau * E + gp(L.topk_idx)[a]] + gp(L.lrank)[a];
+      st_shared(L.sorted_assign + r, a);
+      st_shared(L.pos + a, r);
+    }
   }
 }
 
@@ -638,8 +677,7 @@ ETC_TASK void gateup_task(KArgs& p, KLayer& L, int e, int m, int n, Smem& sm) {
       const float* src = hs + row * HSTR + c;
       uint64_t v;
       if constexpr (sizeof(TE) == 2) {
-        v = (uint64_t)(f32_to_bf16_bits(src[0]) | (f32_to_bf16_bits(src[1]) << 16)) |
-            ((uint64_t)(f32_to_bf16_bits(src[2]) | (f32_to_bf16_bits(src[3]) << 16)) << 32);
+        v = (uint64_t)pack_bf16x2(src[0], src[1]) | ((uint64_t)pack_bf16x2(src[2], src[3]) << 32);
       } else {
         v = (uint64_t)__float_as_uint(src[0]) | ((uint64_t)__float_as_uint(src[1]) << 32);
       }
@@ -758,14 +796,14 @@ ETC_TASK void finalize_task(KArgs& p, KLayer& L, int tau) {
         }
       }
     }
-    st_shared16(out + (size_t)t * H + h, pack16<TE>(v));
+    st_shared16(out + (size_t)t0 * H, (uint32_t)(c * 16), pack16<TE>(v));
   }
 }
 
 // ------------------------------------------------------------------ scheduling
 
 // Static: the ticket's task; waits for S of a layer before decoding past it.
-// Static mode: the fixed task order (per layer: all R, S, all GU, all D, all F) is cut
+// Static mode: the fixed task order (per layer: all R, all P, all GU, all D, all F) is cut
 // into chunks of G consecutive tasks, chunk c belonging to queue c mod Q; workgroup b
 // draws from queue b mod Q.  The dispatcher places workgroup b on XCD b mod 8, so with
 // Q = 8 each chunk runs on one XCD: the row tiles that share a weight tile and the
@@ -783,10 +821,9 @@ ETC_DEV bool claim_static(KArgs& p, Task& t, uint64_t deadline) {
     KLayer& L = p.layer[l];
     t.layer = l;
     if (ticket < base + p.n_rt) { t.kind = K_R; t.a = ticket - base; return true; }
-    if (ticket == base + p.n_rt) { t.kind = K_S; return true; }
-    int off = ticket - base - p.n_rt - 1;
-    if (off < p.n_rt) { t.kind = K_P; t.a = off; return true; }
-    off -= p.n_rt;
+    int off = ticket - base - p.n_rt;
+    if (off < p.n_perm) { t.kind = K_P; t.a = off; return true; }
+    off -= p.n_perm;
     if (!spin_until_geq(L.ev_scan, 1, p.sched, deadline, 10 + l)) return false;
     const int ngu = gp(L.plan)[PL_NGU], nd = gp(L.plan)[PL_ND], nf = gp(L.plan)[PL_NF], nS = gp(L.plan)[PL_NS];
     if (off < ngu) {
@@ -848,8 +885,6 @@ ETC_DEV bool wait_deps(KArgs& p, const Task& t, uint64_t deadline) {
     case K_R:
       if (t.layer == 0) return true;
       return spin_until_geq(p.layer[t.layer - 1].ev_done + t.a, 1, p.sched, deadline, 20);
-    case K_S:
-      return spin_until_geq(L.ev_route, p.n_rt, p.sched, deadline, 21);
     case K_P:
       return spin_until_geq(L.ev_scan, 1, p.sched, deadline, 24);
     case K_GU:
@@ -886,24 +921,59 @@ ETC_DEV void push_one(KArgs& p, const Task& t) {
   q_store_relaxed(p.queue + slot, enc(t));
 }
 
-// After S: static mode publishes ev_scan; dynamic mode enqueues every permutation task
-// and adds the layer's task count to the queue total.
+// Dynamic mode: every gate/up task of the layer is ready (the permutation is complete).
+ETC_DEV void push_gateup(KArgs& p, KLayer& L, int layer, Smem& sm) {
+  const int n1 = p.n1, E = p.E;
+  push_many(p, sm, gp(L.plan)[PL_NGU], [&](int i) {
+    const int e = owner_expert(L.rt_base, E, i, n1);
+    const int me = gp(L.rt_base)[e + 1] - gp(L.rt_base)[e];
+    const int loc = i - gp(L.rt_base)[e] * n1;
+    Task g;
+    g.kind = K_GU; g.layer = layer; g.a = e; g.b = loc % me; g.c = loc / me; g.d = 0;
+    return g;
+  });
+}
+
+// After S (run by the last routing task of the layer, in both modes): publish ev_scan,
+// and ev_perm as well when S scattered the permutation itself.  Dynamic mode then
+// enqueues the P tasks (or, without them, every gate/up task) and adds the layer's task
+// count to the queue total.
 ETC_DEV void after_scan(KArgs& p, int layer, Smem& sm) {
   KLayer& L = p.layer[layer];
   publish_shared();
-  if (threadIdx.x == 0) ev_store_relaxed(L.ev_scan, 1);  // both modes: the event tensor is complete
+  if (threadIdx.x == 0) {
+    ev_store_relaxed(L.ev_scan, 1);  // the event tensor is complete
+    if (p.n_perm == 0) ev_store_relaxed(L.ev_perm, p.n_rt);
+  }
   if (p.mode == ETC_SCHED_STATIC) return;
-  push_many(p, sm, p.n_rt, [&](int i) {
-    Task t;
-    t.kind = K_P; t.layer = layer; t.a = i; t.b = t.c = t.d = 0;
-    return t;
-  });
+  if (p.n_perm > 0) {
+    push_many(p, sm, p.n_perm, [&](int i) {
+      Task t;
+      t.kind = K_P; t.layer = layer; t.a = i; t.b = t.c = t.d = 0;
+      return t;
+    });
+  } else {
+    push_gateup(p, L, layer, sm);
+  }
   if (threadIdx.x == 0) {
     // the plan words are in global memory, written by this thread before publish_shared
-    const int added = p.n_rt + gp(L.plan)[PL_NGU] + gp(L.plan)[PL_ND] + gp(L.plan)[PL_NF] +
+    const int added = p.n_perm + gp(L.plan)[PL_NGU] + gp(L.plan)[PL_ND] + gp(L.plan)[PL_NF] +
                       (layer + 1 < p.L ? p.n_rt : 0) + (layer == 0 ? p.n_rt : 0);
     ev_add_relaxed(p.sched + W_QTOTAL, added);
     ev_add(p.sched + W_PLANNED, 1);
+  }
+}
+
+// One ETC_FLAG_TRACE record: task word, start of its claim, workgroup and ticks spent
+// claiming / waiting, ticks running.
+ETC_DEV void trace_record(KArgs& p, const Task& t, uint64_t t_claim, uint64_t t_run, uint64_t t_end) {
+  const int i = ev_add_relaxed(p.sched + W_TRACE, 1);
+  if (i < p.trace_cap) {
+    ETC_GLOBAL unsigned long long* r = gp(p.trace) + 4 * (size_t)i;
+    r[0] = (unsigned long long)enc(t);
+    r[1] = t_claim;
+    r[2] = (unsigned long long)blockIdx.x | ((unsigned long long)(uint32_t)(t_run - t_claim) << 32);
+    r[3] = (unsigned long long)(uint32_t)(t_end - t_run);
   }
 }
 
@@ -916,19 +986,21 @@ ETC_DEV void run_task(KArgs& p, KLayer& L, const Task& t, Smem& sm) {
     route_task<TE>(p, L, t.a, sm);
     publish_shared();
     if (tid == 0) {
-      // dynamic mode: the last arriver runs S, which reads every tile's results
-      const int old = (p.mode == ETC_SCHED_DYNAMIC) ? ev_add_acquire(L.ev_route, 1)
-                                                    : ev_add_relaxed(L.ev_route, 1);
-      sm.flag = (p.mode == ETC_SCHED_DYNAMIC && old + 1 == p.n_rt) ? 1 : 0;
+      // the last routing tile of the layer runs S, which reads every tile's results
+      // (acquire: they were published before the other tiles' signals)
+      sm.flag = (ev_add_acquire(L.ev_route, 1) + 1 == p.n_rt) ? 1 : 0;
     }
     __syncthreads();
-    if (sm.flag) {  // last routing tile of the layer: S runs here (dynamic mode)
+    if (sm.flag) {
+      const uint64_t t0 = now_ticks();
       scan_task(p, L, t.layer, sm);
       after_scan(p, t.layer, sm);
+      if (tid == 0 && (p.flags & ETC_FLAG_TRACE)) {  // S keeps a trace record of its own
+        Task st;
+        st.kind = K_S; st.layer = t.layer; st.a = st.b = st.c = st.d = 0;
+        trace_record(p, st, t0, t0, now_ticks());
+      }
     }
-  } else if (t.kind == K_S) {
-    scan_task(p, L, t.layer, sm);
-    after_scan(p, t.layer, sm);
   } else if (t.kind == K_P) {
     perm_task(p, L, t.a);
     publish_shared();
@@ -938,17 +1010,7 @@ ETC_DEV void run_task(KArgs& p, KLayer& L, const Task& t, Smem& sm) {
       sm.flag = (p.mode == ETC_SCHED_DYNAMIC && old + 1 == p.n_rt) ? 1 : 0;
     }
     __syncthreads();
-    if (sm.flag) {  // the permutation is complete: every gate/up task is ready
-      const int layer = t.layer, n1 = p.n1, E = p.E;
-      push_many(p, sm, gp(L.plan)[PL_NGU], [&](int i) {
-        const int e = owner_expert(L.rt_base, E, i, n1);
-        const int me = gp(L.rt_base)[e + 1] - gp(L.rt_base)[e];
-        const int loc = i - gp(L.rt_base)[e] * n1;
-        Task g;
-        g.kind = K_GU; g.layer = layer; g.a = e; g.b = loc % me; g.c = loc / me; g.d = 0;
-        return g;
-      });
-    }
+    if (sm.flag) push_gateup(p, L, t.layer, sm);  // the permutation is complete
   } else if (t.kind == K_GU) {
     gateup_task<TE>(p, L, t.a, t.b, t.c, sm);
     publish_shared();
@@ -1048,17 +1110,7 @@ __global__ __launch_bounds__(MNT) void moe_kernel(Args pk) {
     if (t.kind == K_NONE) break;
     KLayer& L = p.layer[t.layer];
     run_task<TE>(p, L, t, sm);
-    if (tracing && tid == 0) {
-      const uint64_t t_end = now_ticks();
-      const int i = ev_add_relaxed(p.sched + W_TRACE, 1);
-      if (i < p.trace_cap) {
-        ETC_GLOBAL unsigned long long* r = gp(p.trace) + 4 * (size_t)i;
-        r[0] = (unsigned long long)enc(t);
-        r[1] = t_claim;
-        r[2] = (unsigned long long)blockIdx.x | ((unsigned long long)(uint32_t)(t_run - t_claim) << 32);
-        r[3] = (unsigned long long)(uint32_t)(t_end - t_run);
-      }
-    }
+    if (tracing && tid == 0) trace_record(p, t, t_claim, t_run, now_ticks());
   }
 
   // the last workgroup out clears the event counters and control words
@@ -1264,6 +1316,7 @@ ETC_API etc_status etc_moe_layer(int32_t T, int32_t H, int32_t E, int32_t K, int
   p.combine = combine;
   p.flags = flags;
   p.n_rt = cdiv(T, moe::BT);
+  p.n_perm = p.n_rt <= moe::PERM_INLINE_RT ? 0 : p.n_rt;
   p.n1 = Y.n1;
   p.n2 = Y.n2;
   p.max_rt = Y.max_rt;

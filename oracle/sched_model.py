@@ -16,8 +16,10 @@ down projection split along ffn into chunks of GPC gate/up tiles:
 
   R(tau)          routing tile tau                      waits  done[l-1][tau] >= 1 (l > 0)
                                                         signals route[l] += 1
-  S               counts, scans, per-tile row offsets   waits  route[l] >= n_rt
-                                                        signals scan[l] = 1
+  S               counts, scans, per-tile row offsets   runs in the R task whose signal
+                                                        brings route[l] to n_rt
+                                                        signals scan[l] = 1 (and perm[l] = n_rt
+                                                        when it scatters the permutation)
   P(tau)          permutation scatter of tile tau       waits  scan[l] >= 1
                                                         signals perm[l] += 1
   GU(e, m, n)     gate/up tile                          waits  perm[l] >= n_rt
@@ -27,13 +29,18 @@ down projection split along ffn into chunks of GPC gate/up tiles:
   F(tau)          finalize the output rows of tau       waits  comb[l][tau] >= |tau| * k * n2 * nS
                                                         signals done[l][tau] += 1
 
-Static mode runs the tasks in one fixed ticket order (per layer: all R, S, all P, all
-GU, all D, all F) and each worker spins on the dependencies of the task it drew.
-Dynamic mode keeps a FIFO ready queue: the R tasks of the first layer are queued at
-the start; the worker whose signal completes a counter (the last arriver) makes the
-dependents ready -- S runs inline after the last R, S queues every P task, the last P
-queues every GU task, a full gu chunk queues its D tasks, a full comb tile queues its F, and F queues the next
-layer's R for the same tokens.
+reading (few routing tiles): with at most Plan.PI routing tiles S also scatters the
+permutation and there are no P tasks (a hand-off less on a short critical path).
+
+S is not a ticket of its own: in both modes the R task whose signal completes
+route[l] (the last arriver) runs it.  Static mode runs the other tasks in one fixed
+ticket order (per layer: all R, all P, all GU, all D, all F) and each worker spins on
+the dependencies of the task it drew.  Dynamic mode keeps a FIFO ready queue: the R
+tasks of the first layer are queued at the start; the worker whose signal completes a
+counter makes the dependents ready -- S queues every P task (or every GU task when it
+scattered the permutation), the last P queues every GU task, a full gu chunk queues its
+D tasks, a full comb tile queues its F, and F queues the next layer's R for the same
+tokens.
 """
 
 from dataclasses import dataclass, field
@@ -51,6 +58,7 @@ class Plan:
     BN1: int  # ffn columns per gate/up tile
     BN2: int  # hidden columns per down tile
     GPC: int  # gate/up tiles per down chunk (ffn split of the down projection)
+    PI: int = 0  # up to this many routing tiles S scatters the permutation (no P tasks)
 
 
 @dataclass
@@ -83,8 +91,12 @@ def build_layer(l, T, H, F, k, counts, plan, tokens_of_rows):
     for tau in range(n_rt):
         waits = [(("done", l - 1, tau), 1)] if l > 0 else []
         R.append(Task("R", l, (tau,), waits, [(("route", l), 1)]))
-    S = Task("S", l, (), [(("route", l), n_rt)], [(("scan", l), 1)])
-    P = [Task("P", l, (tau,), [(("scan", l), 1)], [(("perm", l), 1)]) for tau in range(n_rt)]
+    if n_rt <= plan.PI:
+        S = Task("S", l, (), [(("route", l), n_rt)], [(("scan", l), 1), (("perm", l), n_rt)])
+        P = []
+    else:
+        S = Task("S", l, (), [(("route", l), n_rt)], [(("scan", l), 1)])
+        P = [Task("P", l, (tau,), [(("scan", l), 1)], [(("perm", l), 1)]) for tau in range(n_rt)]
     for e, c in enumerate(counts):
         for m in range(cdiv(int(c), plan.BM)):
             for n in range(n1):
@@ -124,10 +136,46 @@ def expected_final_counters(graph):
 
 
 def static_order(graph):
+    """The ticket order (S runs inside the last R of its layer and has no ticket)."""
     order = []
     for R, S, P, GU, D, Fin in graph:
-        order += R + [S] + P + GU + D + Fin
+        order += R + P + GU + D + Fin
     return order
+
+
+def _scan_of(graph):
+    """S of each layer by the route counter its last R completes."""
+    return {("route", l): (g[1], len(g[0])) for l, g in enumerate(graph)}
+
+
+def _run_inline_scan(task, before, counters, scans, executed):
+    """If ``task`` (an R) completed its layer's route counter, S runs right after it in
+    the same worker.  Returns S or None."""
+    for ctr, _ in task.signals:
+        if ctr in scans:
+            S, n_rt = scans[ctr]
+            if before.get(ctr, 0) < n_rt <= counters[ctr]:
+                assert _ready(S, counters)
+                _signal(S, counters)
+                executed.append(S)
+                return S
+    return None
+
+
+def replay_static(graph):
+    """One worker taking the tickets in order and never waiting (S inline after the R
+    that completes its layer's route counter); raises if a ticket's task is not ready
+    when its turn comes.  Returns the execution order."""
+    scans = _scan_of(graph)
+    counters, executed = {}, []
+    for t in static_order(graph):
+        if not _ready(t, counters):
+            raise RuntimeError(f"ticket {t.kind}{t.key} of layer {t.layer} is not ready in order")
+        before = dict(counters)
+        _signal(t, counters)
+        executed.append(t)
+        _run_inline_scan(t, before, counters, scans, executed)
+    return executed
 
 
 def _ready(task, counters):
@@ -152,10 +200,12 @@ def simulate_static(graph, workers, rng=None, queues=1, chunk=1):
     raises RuntimeError on deadlock (no worker can move)."""
     rng = rng or random.Random(0)
     order = static_order(graph)
+    scans = _scan_of(graph)
     counters, executed = {}, []
     next_local = [0] * queues
     holding = [None] * workers  # task drawn by each worker
-    while len(executed) < len(order):
+    total = len(order) + len(graph)  # the tickets and one S per layer
+    while len(executed) < total:
         # every idle worker draws its queue's next ticket (an atomic increment); a
         # ticket past the end of the order means the queue is drained
         for w in range(workers):
@@ -172,8 +222,10 @@ def simulate_static(graph, workers, rng=None, queues=1, chunk=1):
             raise RuntimeError(f"static schedule deadlocked holding {[(t.kind, t.key) for t in stuck]}")
         w = rng.choice(movable)
         t = holding[w]
+        before = dict(counters)
         _signal(t, counters)
         executed.append(t)
+        _run_inline_scan(t, before, counters, scans, executed)
         holding[w] = None
     return executed, counters
 
@@ -218,12 +270,13 @@ def simulate_dynamic(graph, workers, rng=None):
             old, new = before.get(ctr, 0), counters[ctr]
             kind = ctr[0]
             if kind == "route" and new == len(R) and old < new:
-                # the last routing tile runs S inline
+                # the last routing tile runs S inline; S queues the P tasks, or the GU
+                # tasks when it scattered the permutation itself
                 assert _ready(S, counters)
                 _signal(S, counters)
                 executed.append(S)
-                queue.extend(p_by_layer[l])
-            elif kind == "perm" and new == len(P) and old < new:
+                queue.extend(p_by_layer[l] if p_by_layer[l] else gu_by_layer[l])
+            elif kind == "perm" and P and new == len(P) and old < new:
                 queue.extend(gu_by_layer[l])
             elif kind == "gu":
                 _, _, e, m, s = ctr

@@ -132,6 +132,8 @@ inline int emu_update_dpp(int old, int src, int ctrl, int row_mask, int bank_mas
 #define __builtin_amdgcn_update_dpp(old, src, ctrl, rm, bm, bc) emu_update_dpp((old), (src), (ctrl), (rm), (bm), (bc))
 
 inline int atomicAdd(int* p, int v) { return __atomic_fetch_add(p, v, __ATOMIC_SEQ_CST); }
+inline unsigned atomicOr(unsigned* p, unsigned v) { return __atomic_fetch_or(p, v, __ATOMIC_SEQ_CST); }
+inline int __popc(unsigned v) { return __builtin_popcount(v); }
 inline float atomicAdd(float* p, float v) {
   unsigned* u = reinterpret_cast<unsigned*>(p);
   unsigned old = __atomic_load_n(u, __ATOMIC_RELAXED);
@@ -162,6 +164,19 @@ inline void emu_global_load_lds(const void* src, void* lds_base, int size, int o
 #define __builtin_amdgcn_global_load_lds(src, dst, size, off, aux) \
   emu_global_load_lds((const void*)(src), (void*)(dst), (size), (off))
 #define __builtin_amdgcn_s_barrier() emu_syncthreads()
+// raw buffer stores: the resource is the base address; the 16 bytes go out as two
+// 8-byte atomic stores (device-scope stores are atomic in this stand-in as well)
+typedef char* __amdgpu_buffer_rsrc_t;
+#define __builtin_amdgcn_make_buffer_rsrc(p, stride, num, flags) ((char*)(p))
+template <typename V>
+inline void emu_buffer_store16(const V& v, char* base, int off, int soff) {
+  uint64_t w[2];
+  memcpy(w, &v, 16);
+  uint64_t* d = reinterpret_cast<uint64_t*>(base + off + soff);
+  __atomic_store_n(d, w[0], __ATOMIC_RELAXED);
+  __atomic_store_n(d + 1, w[1], __ATOMIC_RELAXED);
+}
+#define __builtin_amdgcn_raw_buffer_store_b128(v, r, off, soff, aux) emu_buffer_store16((v), (r), (off), (soff))
 #define __builtin_amdgcn_sched_barrier(mask) ((void)0)
 #define __builtin_amdgcn_sched_group_barrier(mask, n, id) ((void)0)
 

@@ -23,6 +23,10 @@ import numpy as np
 
 from oracle import moe as om
 
+# routing tiles up to which the library's scan task scatters the permutation itself
+# (no P tasks; PERM_INLINE_RT in csrc/moe.hip)
+PERM_INLINE_RT = 4
+
 TIE_FIRST = 1e-5
 TIE_LATER = 2e-3
 GATE_TOL = 1e-5
@@ -126,7 +130,7 @@ def check_event_tensor(read_i32, layout, T, H, F, k, E, gpu, layers):
         sa = gpu["sa"][l]
         off = np.concatenate([[0], np.cumsum(counts)])
         tors = [list(sa[off[e]:off[e + 1]] // k) for e in range(E)]
-        plan = sm.Plan(BT=BT, BM=BM, BN1=BN1, BN2=BN2, GPC=gpc)
+        plan = sm.Plan(BT=BT, BM=BM, BN1=BN1, BN2=BN2, GPC=gpc, PI=PERM_INLINE_RT)
         final = sm.expected_final_counters(sm.build_graph(T, H, F, k, [counts], [tors], plan))
         n_rt, n1m, n2, nSm = sm.layer_shape(T, H, F, plan)
         assert (n1m, nSm) == (n1, nS) and RT == sum(-(-int(c) // BM) for c in counts)

@@ -36,6 +36,10 @@ CASES = [
     (256, 2048, 768, 128, 8, 1, sm.Plan(BT=16, BM=64, BN1=128, BN2=256, GPC=6)),
     (300, 512, 384, 16, 6, 2, sm.Plan(BT=16, BM=64, BN1=64, BN2=128, GPC=6)),
     (33, 256, 192, 8, 3, 3, sm.Plan(BT=8, BM=16, BN1=32, BN2=64, GPC=2)),
+    # few routing tiles: S scatters the permutation, no P tasks
+    (1, 4096, 14336, 8, 2, 2, sm.Plan(BT=16, BM=128, BN1=128, BN2=256, GPC=7, PI=4)),
+    (64, 4096, 14336, 8, 2, 1, sm.Plan(BT=16, BM=128, BN1=128, BN2=256, GPC=4, PI=4)),
+    (33, 256, 192, 8, 3, 3, sm.Plan(BT=8, BM=16, BN1=32, BN2=64, GPC=2, PI=5)),
 ]
 
 
@@ -138,8 +142,25 @@ def test_static_ticket_order_is_topological():
     graph = _graph_from_routing(100, 256, 384, 2, 8, [_random_idx(rng, 100, 8, 2)] * 2, plan)
     # one worker executing the ticket order without ever waiting proves every task's
     # producers hold smaller tickets (deadlock freedom with co-resident workers)
-    order = sm.static_order(graph)
-    sm.check_execution(order, graph)
+    sm.check_execution(sm.replay_static(graph), graph)
+    # S has no ticket: it runs inside the routing task that completes route[l]
+    assert all(t.kind != "S" for t in sm.static_order(graph))
+
+
+def test_inline_permutation_replaces_p_tasks():
+    rng = np.random.default_rng(3)
+    idx = [_random_idx(rng, 40, 8, 2)] * 2
+    few = _graph_from_routing(40, 256, 384, 2, 8, idx, sm.Plan(BT=16, BM=64, BN1=64, BN2=128, GPC=3, PI=4))
+    many = _graph_from_routing(40, 256, 384, 2, 8, idx, sm.Plan(BT=16, BM=64, BN1=64, BN2=128, GPC=3, PI=2))
+    for R, S, P, GU, D, Fin in few:
+        assert P == [] and (("perm", S.layer), len(R)) in S.signals
+    for R, S, P, GU, D, Fin in many:
+        assert len(P) == len(R)
+    # both reach the same final counters, and both schedules complete
+    assert sm.expected_final_counters(few) == sm.expected_final_counters(many)
+    for g in (few, many):
+        sm.check_execution(sm.simulate_static(g, 3, queues=2, chunk=2)[0], g)
+        sm.check_execution(sm.simulate_dynamic(g, 3)[0], g)
 
 
 def test_splitk_graph():
