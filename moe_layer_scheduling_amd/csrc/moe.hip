@@ -66,6 +66,10 @@ constexpr int PERM_INLINE_RT = 4;
 // sharing one with the scheduler loop and every other task (inlined together they spill
 // inside the GEMM loop).  A call per task costs nothing next to the task itself.
 #define ETC_TASK __device__ __attribute__((noinline))
+// The short tasks (routing, scan, permutation, finalize) are inlined into the task loop:
+// as calls they would save and restore the callee-saved registers they use (about 90 per
+// lane) on every call, for a task that runs only once or twice per workgroup.
+#define ETC_SMALL_TASK __device__ __attribute__((always_inline))
 
 enum Kind { K_NONE = 0, K_R = 1, K_S = 2, K_GU = 3, K_D = 4, K_F = 5, K_P = 6 };
 enum PlanWord { PL_RT = 0, PL_NGU, PL_ND, PL_NF, PL_NS, PL_GPC, PL_NEXTBASE, PL_WORDS = 8 };
@@ -155,10 +159,10 @@ struct RouteSmem {
   int sel[BT][MAXK];
 };
 struct ScanSmem {
+  static constexpr int HIST_LDS = 16384;  // histogram entries staged in LDS
+  alignas(16) int hs[HIST_LDS];            // hist, then tile_off in place
   int off[MAXE + 1];
-  int rtb[MAXE + 1];
-  int toff[PERM_INLINE_RT * MAXE];  // tile_off when S scatters the permutation itself
-  int tmp[NWAVE];
+  int tmp[2 * NWAVE];
   int part[MNT];  // per-thread partial counts over a chunk of routing tiles
 };
 struct TileSmem {
@@ -166,6 +170,7 @@ struct TileSmem {
   int row_tok[BM];
   float row_gate[BM];
 };
+static_assert(PERM_INLINE_RT * MAXE <= ScanSmem::HIST_LDS, "the inline scatter reads staged offsets");
 union SmemU {
   RouteSmem r;
   ScanSmem s;
@@ -340,6 +345,77 @@ ETC_DEV void router_item(KArgs& p, KLayer& L, RouteSmem& R, int t0, int nt, int 
   }
 }
 
+// Router on the vector ALUs for a tile of at most NTOK (1 or 2) tokens and at most 16
+// experts (decode-sized batches), where the 16-row MFMA path would split 16 rows for one
+// or two real tokens.  Thread tid takes chunks tid, tid + MNT, ... of the rows; for every token
+// and expert it accumulates v . W_r[e] over its chunks in float32 (fused multiply-add),
+// then every wave sums its lanes and writes R.part[w][t][e] (KS = NWAVE slices).  It also
+// writes xq = dtype(v * rs) for the tile's tokens (16 bytes per lane, rows contiguous).
+template <typename TE, int NTOK>
+ETC_DEV void router_valu(KArgs& p, KLayer& L, RouteSmem& R, int t0, int nt) {
+  constexpr int EPC = 16 / (int)sizeof(TE);
+  constexpr int EMAX = 16;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int H = p.H, E = p.E, cpr = H / EPC;
+  const TE* x = static_cast<const TE*>(L.in) + (size_t)t0 * H;
+  const TE* wr = static_cast<const TE*>(L.w_router);
+  TE* xq = static_cast<TE*>(p.xq) + (size_t)t0 * H;
+  float acc[NTOK][EMAX];
+#pragma unroll
+  for (int t = 0; t < NTOK; ++t)
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) acc[t][e] = 0.f;
+  float rs[NTOK];
+#pragma unroll
+  for (int t = 0; t < NTOK; ++t) rs[t] = R.rs[min(t, nt - 1)];
+  for (int c = tid; c < cpr; c += MNT) {
+    // rows past the tile's tokens repeat its last token, experts past E the last expert
+    u32x4 xv[NTOK], wv[EMAX];
+    f32x4 gv[EPC / 4];
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t) xv[t] = gld<u32x4>(x + (size_t)min(t, nt - 1) * H + c * EPC);
+#pragma unroll
+    for (int q = 0; q < EPC / 4; ++q) gv[q] = gld<f32x4>(L.gamma + c * EPC + 4 * q);
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) wv[e] = gld<u32x4>(wr + (size_t)min(e, E - 1) * H + c * EPC);
+#pragma unroll
+    for (int t = 0; t < NTOK; ++t) {
+      float v[EPC];
+      expand16(xv[t], v, (const TE*)nullptr);
+#pragma unroll
+      for (int q = 0; q < EPC / 4; ++q) {
+        v[4 * q] *= gv[q].x;
+        v[4 * q + 1] *= gv[q].y;
+        v[4 * q + 2] *= gv[q].z;
+        v[4 * q + 3] *= gv[q].w;
+      }
+#pragma unroll
+      for (int e = 0; e < EMAX; ++e) {
+        float wf[EPC];
+        expand16(wv[e], wf, (const TE*)nullptr);
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) acc[t][e] = fmaf(v[i], wf[i], acc[t][e]);
+      }
+      if (t < nt) {
+        float xn[EPC];
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) xn[i] = v[i] * rs[t];
+        st_shared16(xq, (uint32_t)(((size_t)t * H + c * EPC) * sizeof(TE)), pack16<TE>(xn));
+      }
+    }
+  }
+  // every wave's sum of its lanes, per (token, expert)
+#pragma unroll
+  for (int t = 0; t < NTOK; ++t)
+#pragma unroll
+    for (int e = 0; e < EMAX; ++e) {
+      float v = row16_sum(acc[t][e]);
+      v += __shfl_xor(v, 16, WAVE);
+      v += __shfl_xor(v, 32, WAVE);
+      if (lane == 0 && t < nt && e < E) R.part[(w * BT + t) * E + e] = v;
+    }
+}
+
 // Top-k of one token per row of 16 lanes: lane j holds experts j, j+16, ...  k rounds of
 // an argmax by (logit desc, expert asc) across the row; lane j keeps the j-th winner.
 // Softmax over the k selected logits.  Rows past the tile's tokens compute on unused
@@ -389,7 +465,7 @@ ETC_DEV void topk_row(KArgs& p, KLayer& L, RouteSmem& R, int t0, int nt) {
 }
 
 template <typename TE>
-ETC_TASK void route_task(KArgs& p, KLayer& L, int tau, Smem& sm) {
+ETC_SMALL_TASK void route_task(KArgs& p, KLayer& L, int tau, Smem& sm) {
   constexpr int EPC = 16 / (int)sizeof(TE);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -434,11 +510,16 @@ ETC_TASK void route_task(KArgs& p, KLayer& L, int tau, Smem& sm) {
   }
   __syncthreads();
 
-  // 2. partial logits per (expert group, K slice), one item per wave
+  // 2. partial logits: on the vector ALUs for a few tokens and experts, else per
+  //    (expert group, K slice) on the matrix cores, one item per wave
   const int NB = cdiv(E, 16);
   const int NBW = NB <= 1 ? 1 : (NB <= 2 ? 2 : 4);
-  const int KS = NWAVE / cdiv(NB, NBW);
-  {
+  int KS = NWAVE / cdiv(NB, NBW);
+  if (E <= 16 && nt <= 2) {
+    KS = NWAVE;
+    if (nt == 1) router_valu<TE, 1>(p, L, R, t0, nt);
+    else router_valu<TE, 2>(p, L, R, t0, nt);
+  } else {
     const int g = w / KS, ks = w % KS;
     if (NBW == 1) router_item<TE, 1>(p, L, R, t0, nt, g, ks, KS);
     else if (NBW == 2) router_item<TE, 2>(p, L, R, t0, nt, g, ks, KS);
@@ -482,85 +563,104 @@ ETC_TASK void route_task(KArgs& p, KLayer& L, int tau, Smem& sm) {
 
 // ------------------------------------------------------------------ S: scan and permutation
 
-ETC_DEV int block_exclusive_scan(int v, int* tmp, int& total) {
+// Exclusive scans of two values at once over the workgroup (thread order): returns the
+// prefixes of a and b and their totals.  One exchange through LDS (tmp: 2 * NWAVE ints).
+ETC_DEV void block_exclusive_scan2(int a, int b, int* tmp, int& pa, int& pb, int& ta, int& tb) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  int x = v;
+  int x = a, y = b;
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
-    const int y = __shfl_up(x, off, WAVE);
-    if (lane >= off) x += y;
+    const int xs = __shfl_up(x, off, WAVE), ys = __shfl_up(y, off, WAVE);
+    if (lane >= off) { x += xs; y += ys; }
   }
-  if (lane == 63) tmp[w] = x;
+  if (lane == 63) { tmp[w] = x; tmp[NWAVE + w] = y; }
   __syncthreads();
-  int before = 0;
-  total = 0;
+  int bx = 0, by = 0;
+  ta = 0;
+  tb = 0;
 #pragma unroll
   for (int i = 0; i < NWAVE; ++i) {
-    before += (i < w) ? tmp[i] : 0;
-    total += tmp[i];
+    bx += (i < w) ? tmp[i] : 0;
+    by += (i < w) ? tmp[NWAVE + i] : 0;
+    ta += tmp[i];
+    tb += tmp[NWAVE + i];
   }
   __syncthreads();
-  return before + x - v;
+  pa = bx + x - a;
+  pb = by + y - b;
 }
 
-ETC_TASK void scan_task(KArgs& p, KLayer& L, int layer, Smem& sm) {
+ETC_SMALL_TASK void scan_task(KArgs& p, KLayer& L, int layer, Smem& sm) {
   const int tid = threadIdx.x;
   const int E = p.E, K = p.K, n_rt = p.n_rt;
   ScanSmem& S = sm.u.s;
-
-  // counts per expert: thread t sums the histogram of expert t / C over chunk t % C of
-  // the routing tiles (C = MNT / E chunks per expert, so every thread takes part)
-  const int C = MNT / E, e_t = tid / C, c_t = tid % C;
-  const int span = cdiv(n_rt, C), tau0 = c_t * span, tau1 = min(n_rt, tau0 + span);
-  const bool owner = e_t < E;
-  int part = 0;
-  if (owner) {
-    for (int tau = tau0; tau < tau1; tau += 8) {
-      int v[8];
+  const bool inline_perm = p.n_perm == 0;
+  // few routing tiles: the inputs of the pairs this thread places (at most 64 tokens, so
+  // at most two pairs per thread), loaded first so that their latency overlaps the scan
+  const int npairs = inline_perm ? p.T * K : 0;
+  int pe[2] = {0, 0}, pr[2] = {0, 0};
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = (tau + u < tau1) ? gp(L.hist)[(tau + u) * E + e_t] : 0;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) part += v[u];
+  for (int q = 0; q < 2; ++q) {
+    const int a = min(tid + q * MNT, max(npairs - 1, 0));
+    if (inline_perm) {
+      pe[q] = gp(L.topk_idx)[a];
+      pr[q] = gp(L.lrank)[a];
     }
   }
+
+  // The histogram [n_rt][E] comes into LDS in 16-byte pieces when it fits (the routing
+  // tiles' counts are then read from global memory once); larger ones are read in place.
+  const bool staged = n_rt * E <= ScanSmem::HIST_LDS;
+  if (staged) {
+    const int n = n_rt * E;
+    for (int i = tid * 4; i < n; i += MNT * 4) {
+      if (i + 4 <= n) {
+        *reinterpret_cast<u32x4*>(&S.hs[i]) = gld<u32x4>(L.hist + i);
+      } else {
+        for (int j = i; j < n; ++j) S.hs[j] = gp(L.hist)[j];
+      }
+    }
+    __syncthreads();
+  }
+  auto hist = [&](int tau, int e) ETC_INLINE { return staged ? S.hs[tau * E + e] : gp(L.hist)[tau * E + e]; };
+
+  // counts per expert: thread (c, e) = (tid / E, tid % E) sums the histogram of expert e
+  // over chunk c of the routing tiles (C = MNT / E chunks per expert)
+  const int C = MNT / E, e_t = tid % E, c_t = tid / E;
+  const bool owner = c_t < C;
+  const int span = cdiv(n_rt, C), tau0 = min(n_rt, c_t * span), tau1 = min(n_rt, tau0 + span);
+  int part = 0;
+  if (owner)
+    for (int tau = tau0; tau < tau1; ++tau) part += hist(tau, e_t);
   S.part[tid] = part;
   __syncthreads();
   int cnt = 0;
   if (tid < E)
-    for (int c = 0; c < C; ++c) cnt += S.part[tid * C + c];
-  int total_rows = 0, RT = 0;
-  const int off = block_exclusive_scan(cnt, S.tmp, total_rows);
-  const int rtb = block_exclusive_scan(cdiv(cnt, BM), S.tmp, RT);
+    for (int c = 0; c < C; ++c) cnt += S.part[c * E + tid];
+  int off = 0, rtb = 0, total_rows = 0, RT = 0;
+  block_exclusive_scan2(cnt, cdiv(cnt, BM), S.tmp, off, rtb, total_rows, RT);
   if (tid < E) {
     S.off[tid] = off;
-    S.rtb[tid] = rtb;
     st_shared(L.counts + tid, cnt);
     st_shared(L.offsets + tid, off);
     st_shared(L.rt_base + tid, rtb);
   }
   if (tid == 0) {
     S.off[E] = total_rows;
-    S.rtb[E] = RT;
     st_shared(L.offsets + E, total_rows);
     st_shared(L.rt_base + E, RT);
   }
   __syncthreads();
   // first sorted row of every (routing tile, expert) block: each thread continues the
-  // running offset of its expert through its chunk
+  // running offset of its expert through its chunk (in place in LDS when staged)
   if (owner) {
     int run = S.off[e_t];
-    for (int c = 0; c < c_t; ++c) run += S.part[e_t * C + c];
-    for (int tau = tau0; tau < tau1; tau += 8) {
-      int v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = (tau + u < tau1) ? gp(L.hist)[(tau + u) * E + e_t] : 0;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (tau + u < tau1) {
-          st_shared(L.tile_off + (tau + u) * E + e_t, run);
-          if (p.n_perm == 0) S.toff[(tau + u) * E + e_t] = run;
-          run += v[u];
-        }
+    for (int c = 0; c < c_t; ++c) run += S.part[c * E + e_t];
+    for (int tau = tau0; tau < tau1; ++tau) {
+      const int v = hist(tau, e_t);
+      if (staged) S.hs[tau * E + e_t] = run;
+      else st_shared(L.tile_off + tau * E + e_t, run);
+      run += v;
     }
   }
   // the down split: enough down tasks to feed every worker twice, when the combine
@@ -583,15 +683,28 @@ ETC_TASK void scan_task(KArgs& p, KLayer& L, int layer, Smem& sm) {
     st_shared(L.plan + PL_GPC, gpc);
     st_shared(L.plan + PL_NEXTBASE, base + n_rt + p.n_perm + ngu + nd + nf);
   }
-  // few routing tiles: the permutation scatter of every tile here (what P(tau) does)
-  if (p.n_perm == 0) {
+  if (staged) {
     __syncthreads();
-    const int npairs = p.T * K;
-    for (int a = threadIdx.x; a < npairs; a += MNT) {
-      const int tau = a / (BT * K);
-      const int r = S.toff[tau * E + gp(L.topk_idx)[a]] + gp(L.lrank)[a];
-      st_shared(L.sorted_assign + r, a);
-      st_shared(L.pos + a, r);
+    const int n = n_rt * E;
+    for (int i = tid * 4; i < n; i += MNT * 4) {
+      if (i + 4 <= n) {
+        st_shared16(L.tile_off, (uint32_t)(i * 4), *reinterpret_cast<const u32x4*>(&S.hs[i]));
+      } else {
+        for (int j = i; j < n; ++j) st_shared(L.tile_off + j, S.hs[j]);
+      }
+    }
+  }
+  // few routing tiles: the permutation scatter of every tile here (what P(tau) does),
+  // from the offsets in LDS (n_rt * E is small, so they are staged)
+  if (inline_perm) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int a = tid + q * MNT;
+      if (a < npairs) {
+        const int r = S.hs[(a / (BT * K)) * E + pe[q]] + pr[q];
+        st_shared(L.sorted_assign + r, a);
+        st_shared(L.pos + a, r);
+      }
     }
   }
 }
@@ -599,7 +712,7 @@ ETC_TASK void scan_task(KArgs& p, KLayer& L, int layer, Smem& sm) {
 // P(tau): the (token, slot) pairs of routing tile tau go to their rows of the
 // permutation: pair a = t*k + j of expert e lands at tile_off[tau][e] + its rank among
 // the tile's pairs of e (tokens ascending), so each expert's rows stay in token order.
-ETC_TASK void perm_task(KArgs& p, KLayer& L, int tau) {
+ETC_SMALL_TASK void perm_task(KArgs& p, KLayer& L, int tau) {
   const int K = p.K, E = p.E;
   const int a0 = tau * BT * K, npairs = tile_rows(p, tau) * K;
   for (int i = threadIdx.x; i < npairs; i += MNT) {
@@ -769,7 +882,7 @@ ETC_TASK void down_task(KArgs& p, KLayer& L, int e, int m, int n2i, int s, int g
 }
 
 template <typename TE>
-ETC_TASK void finalize_task(KArgs& p, KLayer& L, int tau) {
+ETC_SMALL_TASK void finalize_task(KArgs& p, KLayer& L, int tau) {
   constexpr int EPC = 16 / (int)sizeof(TE);
   const int tid = threadIdx.x, H = p.H, K = p.K;
   const int t0 = tau * BT, nt = tile_rows(p, tau);

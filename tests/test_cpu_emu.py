@@ -67,6 +67,18 @@ def test_ragged_hidden_and_ffn_tiles(lib, mode):
     _check(cfg, x, layers, driver.moe(lib, cfg, x, layers, mode=mode))
 
 
+WIDE = synth.MoEConfig("wide", (1040,), 128, 256, 2, 64, layers=1, zipf_s=0.8)
+
+
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
+def test_histogram_too_large_for_lds(lib, mode):
+    """65 routing tiles x 256 experts: the scan reads the histogram in place instead of
+    staging it in LDS."""
+    cfg = WIDE
+    layers, x = synth.make_layers(cfg), synth.make_x(cfg, 1040)
+    _check(cfg, x, layers, driver.moe(lib, cfg, x, layers, mode=mode))
+
+
 def test_mid_two_layers_dynamic(lib):
     cfg = MID
     layers, x = synth.make_layers(cfg), synth.make_x(cfg, 300)
