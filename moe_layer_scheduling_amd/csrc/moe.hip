@@ -176,11 +176,28 @@ union SmemU {
   ScanSmem s;
   TileSmem t;
 };
+// The plan, row-tile bases, counts and offsets of one layer, copied into LDS by the
+// whole workgroup before its first gate/up, down or finalize task of that layer: ticket
+// decoding (a binary search over the row-tile bases), dependency targets and the tiles'
+// row ranges then read LDS instead of making dependent global round trips per task.
+struct LayerCache {
+  int layer;  // -1: nothing cached
+  int plan[PL_WORDS];
+  int rtb[MAXE + 1];
+  int off[MAXE + 1];
+  int cnt[MAXE];
+};
+
 struct Smem {
   SmemU u;
   Task task;
   int flag;
+  int need_cache;
+  // layers whose ev_scan / ev_perm this workgroup has already acquired at their targets
+  // (bit l): later waits on them return at once (static mode, thread 0)
+  unsigned scan_seen, perm_seen;
   int ibuf[4];
+  LayerCache lc;
 };
 
 template <typename TE>
@@ -198,13 +215,17 @@ ETC_DEV u32x4 pack16<float>(const float* v) {
 ETC_DEV int tile_rows(KArgs& p, int tau) { return min(BT, p.T - tau * BT); }
 
 // Largest e in [0, E) with rt_base[e] * mult <= idx: the expert owning task idx.
-ETC_DEV int owner_expert(const int* rt_base, int E, int idx, int mult) {
+template <typename RtBase>
+ETC_DEV int owner_expert_by(RtBase rt_base, int E, int idx, int mult) {
   int lo = 0, hi = E;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if (gp(rt_base)[mid] * mult <= idx) lo = mid; else hi = mid;
+    if (rt_base(mid) * mult <= idx) lo = mid; else hi = mid;
   }
   return lo;
+}
+ETC_DEV int owner_expert(const int* rt_base, int E, int idx, int mult) {
+  return owner_expert_by([&](int i) ETC_INLINE { return gp(rt_base)[i]; }, E, idx, mult);
 }
 
 // ------------------------------------------------------------------ R: routing tile
@@ -732,8 +753,8 @@ ETC_TASK void gateup_task(KArgs& p, KLayer& L, int e, int m, int n, Smem& sm) {
   const int wm = w / Tile::WN, wn = w % Tile::WN;
   const int H = p.H, F = p.F, K = p.K;
   TileSmem& Ts = sm.u.t;
-  const int r0 = gp(L.offsets)[e] + m * BM;
-  const int valid = min(BM, gp(L.counts)[e] - m * BM);
+  const int r0 = sm.lc.off[e] + m * BM;
+  const int valid = min(BM, sm.lc.cnt[e] - m * BM);
   for (int i = tid; i < BM; i += MNT) Ts.row_tok[i] = (i < valid) ? gp(L.sorted_assign)[r0 + i] / K : -1;
   __syncthreads();
 
@@ -807,8 +828,8 @@ ETC_TASK void down_task(KArgs& p, KLayer& L, int e, int m, int n2i, int s, int g
   const int wm = w / Tile::WN, wn = w % Tile::WN;
   const int H = p.H, F = p.F, K = p.K;
   TileSmem& Ts = sm.u.t;
-  const int r0 = gp(L.offsets)[e] + m * BM;
-  const int valid = min(BM, gp(L.counts)[e] - m * BM);
+  const int r0 = sm.lc.off[e] + m * BM;
+  const int valid = min(BM, sm.lc.cnt[e] - m * BM);
   for (int i = tid; i < BM; i += MNT) {
     if (i < valid) {
       const int a = gp(L.sorted_assign)[r0 + i];
@@ -927,7 +948,7 @@ ETC_SMALL_TASK void finalize_task(KArgs& p, KLayer& L, int tau) {
 // workgroups that are not waiting on it: the order stays deadlock-free.
 ETC_DEV int static_ticket(KArgs& p) { return xcd_ticket(p.sched); }
 
-ETC_DEV bool claim_static(KArgs& p, Task& t, uint64_t deadline) {
+ETC_DEV bool claim_static(KArgs& p, Task& t, uint64_t deadline, Smem& sm) {
   const int ticket = static_ticket(p);
   int base = 0;
   for (int l = 0; l < p.L; ++l) {
@@ -937,26 +958,33 @@ ETC_DEV bool claim_static(KArgs& p, Task& t, uint64_t deadline) {
     int off = ticket - base - p.n_rt;
     if (off < p.n_perm) { t.kind = K_P; t.a = off; return true; }
     off -= p.n_perm;
-    if (!spin_until_geq(L.ev_scan, 1, p.sched, deadline, 10 + l)) return false;
-    const int ngu = gp(L.plan)[PL_NGU], nd = gp(L.plan)[PL_ND], nf = gp(L.plan)[PL_NF], nS = gp(L.plan)[PL_NS];
+    if (!(sm.scan_seen >> l & 1u)) {
+      if (!spin_until_geq(L.ev_scan, 1, p.sched, deadline, 10 + l)) return false;
+      sm.scan_seen |= 1u << l;
+    }
+    // the layer's plan from the workgroup's LDS copy when it holds this layer
+    const bool cached = sm.lc.layer == l;
+    auto plan = [&](int w) ETC_INLINE { return cached ? sm.lc.plan[w] : gp(L.plan)[w]; };
+    auto rtb = [&](int e) ETC_INLINE { return cached ? sm.lc.rtb[e] : gp(L.rt_base)[e]; };
+    const int ngu = plan(PL_NGU), nd = plan(PL_ND), nf = plan(PL_NF), nS = plan(PL_NS);
     if (off < ngu) {
-      const int e = owner_expert(L.rt_base, p.E, off, p.n1);
-      const int me = gp(L.rt_base)[e + 1] - gp(L.rt_base)[e];
-      const int loc = off - gp(L.rt_base)[e] * p.n1;
+      const int e = owner_expert_by(rtb, p.E, off, p.n1);
+      const int me = rtb(e + 1) - rtb(e);
+      const int loc = off - rtb(e) * p.n1;
       t.kind = K_GU; t.a = e; t.b = loc % me; t.c = loc / me;
       return true;
     }
     off -= ngu;
     if (off < nd) {
-      const int e = owner_expert(L.rt_base, p.E, off, p.n2 * nS);
-      const int me = gp(L.rt_base)[e + 1] - gp(L.rt_base)[e];
-      const int loc = off - gp(L.rt_base)[e] * p.n2 * nS;
+      const int e = owner_expert_by(rtb, p.E, off, p.n2 * nS);
+      const int me = rtb(e + 1) - rtb(e);
+      const int loc = off - rtb(e) * p.n2 * nS;
       t.kind = K_D; t.a = e; t.b = loc % me; t.c = (loc / me) % p.n2; t.d = loc / (me * p.n2);
       return true;
     }
     off -= nd;
     if (off < nf) { t.kind = K_F; t.a = off; return true; }
-    base = gp(L.plan)[PL_NEXTBASE];
+    base = plan(PL_NEXTBASE);
   }
   t.kind = K_NONE;
   return true;
@@ -992,7 +1020,7 @@ ETC_DEV bool claim_dynamic(KArgs& p, Task& t, uint64_t deadline) {
 }
 
 // Static mode: wait until the task's inputs are complete (thread 0).
-ETC_DEV bool wait_deps(KArgs& p, const Task& t, uint64_t deadline) {
+ETC_DEV bool wait_deps(KArgs& p, const Task& t, uint64_t deadline, Smem& sm) {
   KLayer& L = p.layer[t.layer];
   switch (t.kind) {
     case K_R:
@@ -1001,20 +1029,38 @@ ETC_DEV bool wait_deps(KArgs& p, const Task& t, uint64_t deadline) {
     case K_P:
       return spin_until_geq(L.ev_scan, 1, p.sched, deadline, 24);
     case K_GU:
-      return spin_until_geq(L.ev_perm, p.n_rt, p.sched, deadline, 25);
+      if (sm.perm_seen >> t.layer & 1u) return true;
+      if (!spin_until_geq(L.ev_perm, p.n_rt, p.sched, deadline, 25)) return false;
+      sm.perm_seen |= 1u << t.layer;
+      return true;
     case K_D: {
-      const int gpc = gp(L.plan)[PL_GPC];
-      const int rt = gp(L.rt_base)[t.a] + t.b;
+      const int gpc = sm.lc.plan[PL_GPC];
+      const int rt = sm.lc.rtb[t.a] + t.b;
       const int need = min(gpc, p.n1 - t.d * gpc);
       return spin_until_geq(L.ev_gu + rt * p.n1 + t.d, need, p.sched, deadline, 22);
     }
     case K_F: {
-      const int target = tile_rows(p, t.a) * p.K * p.n2 * gp(L.plan)[PL_NS];
+      const int target = tile_rows(p, t.a) * p.K * p.n2 * sm.lc.plan[PL_NS];
       return spin_until_geq(L.ev_comb + t.a, target, p.sched, deadline, 23);
     }
     default:
       return true;
   }
+}
+
+// Every thread of the workgroup: copy layer l's plan, row-tile bases, offsets and counts
+// into the LDS cache (the layer's S has completed: its results were acquired with the
+// task's claim).
+ETC_DEV void load_layer_cache(KArgs& p, int l, Smem& sm) {
+  KLayer& L = p.layer[l];
+  const int tid = threadIdx.x, E = p.E;
+  if (tid < PL_WORDS) sm.lc.plan[tid] = gp(L.plan)[tid];
+  for (int i = tid; i <= E; i += MNT) {
+    sm.lc.rtb[i] = gp(L.rt_base)[i];
+    sm.lc.off[i] = gp(L.offsets)[i];
+    if (i < E) sm.lc.cnt[i] = gp(L.counts)[i];
+  }
+  if (tid == 0) sm.lc.layer = l;
 }
 
 // Enqueue n tasks (dynamic mode); every thread of the workgroup calls this.
@@ -1127,10 +1173,10 @@ ETC_DEV void run_task(KArgs& p, KLayer& L, const Task& t, Smem& sm) {
   } else if (t.kind == K_GU) {
     gateup_task<TE>(p, L, t.a, t.b, t.c, sm);
     publish_shared();
-    const int gpc = gp(L.plan)[PL_GPC];
+    const int gpc = sm.lc.plan[PL_GPC];
     const int s = t.c / gpc;
     if (tid == 0) {
-      const int rt = gp(L.rt_base)[t.a] + t.b;
+      const int rt = sm.lc.rtb[t.a] + t.b;
       const int need = min(gpc, p.n1 - s * gpc);
       const int old = (p.mode == ETC_SCHED_DYNAMIC) ? ev_add_acquire(L.ev_gu + rt * p.n1 + s, 1)
                                                     : ev_add_relaxed(L.ev_gu + rt * p.n1 + s, 1);
@@ -1146,13 +1192,13 @@ ETC_DEV void run_task(KArgs& p, KLayer& L, const Task& t, Smem& sm) {
       });
     }
   } else if (t.kind == K_D) {
-    down_task<TE>(p, L, t.a, t.b, t.c, t.d, gp(L.plan)[PL_GPC], sm);
+    down_task<TE>(p, L, t.a, t.b, t.c, t.d, sm.lc.plan[PL_GPC], sm);
     // The results are published once for the whole task, then one signal goes out per
     // run of rows in the same routing tile (rows are token-sorted; a tile's rows can
     // span dozens of routing tiles).  In dynamic mode the signals acquire, for the last
     // arriver that enqueues the finalize task.
     publish_shared();
-    const int valid = min(BM, gp(L.counts)[t.a] - t.b * BM);
+    const int valid = min(BM, sm.lc.cnt[t.a] - t.b * BM);
     if (tid < valid) {
       const int tau = sm.u.t.row_tok[tid] / BT;
       if (tid == 0 || sm.u.t.row_tok[tid - 1] / BT != tau) {
@@ -1160,7 +1206,7 @@ ETC_DEV void run_task(KArgs& p, KLayer& L, const Task& t, Smem& sm) {
         while (tid + len < valid && sm.u.t.row_tok[tid + len] / BT == tau) ++len;
         const int old = (p.mode == ETC_SCHED_DYNAMIC) ? ev_add_acquire(L.ev_comb + tau, len)
                                                       : ev_add_relaxed(L.ev_comb + tau, len);
-        const int target = tile_rows(p, tau) * p.K * p.n2 * gp(L.plan)[PL_NS];
+        const int target = tile_rows(p, tau) * p.K * p.n2 * sm.lc.plan[PL_NS];
         if (p.mode == ETC_SCHED_DYNAMIC && old + len == target) {
           Task f;
           f.kind = K_F; f.layer = t.layer; f.a = tau; f.b = f.c = f.d = 0;
@@ -1204,22 +1250,45 @@ __global__ __launch_bounds__(MNT) void moe_kernel(Args pk) {
 
   const bool tracing = (p.flags & ETC_FLAG_TRACE) != 0;
   uint64_t t_claim = 0, t_run = 0;
+  if (tid == 0) {
+    sm.lc.layer = -1;
+    sm.scan_seen = 0u;
+    sm.perm_seen = 0u;
+  }
   while (true) {
+    // Thread 0 claims a task.  A gate/up, down or finalize task of a layer whose plan the
+    // workgroup has not cached yet first has the whole workgroup copy it into LDS; then
+    // (static mode) thread 0 waits for the task's inputs.
     if (tid == 0) {
       if (tracing) t_claim = now_ticks();
       Task t;
       t.kind = K_NONE; t.layer = 0; t.a = t.b = t.c = t.d = 0;
-      const bool ok = (p.mode == ETC_SCHED_STATIC) ? claim_static(p, t, deadline)
+      const bool ok = (p.mode == ETC_SCHED_STATIC) ? claim_static(p, t, deadline, sm)
                                                     : claim_dynamic(p, t, deadline);
       if (!ok) t.kind = K_NONE;
-      if (ok && t.kind != K_NONE && p.mode == ETC_SCHED_STATIC && !wait_deps(p, t, deadline))
+      const bool gemm_or_f = t.kind == K_GU || t.kind == K_D || t.kind == K_F;
+      sm.need_cache = (gemm_or_f && sm.lc.layer != t.layer) ? 1 : 0;
+      if (!sm.need_cache && t.kind != K_NONE && p.mode == ETC_SCHED_STATIC &&
+          !wait_deps(p, t, deadline, sm))
         t.kind = K_NONE;
       sm.task = t;
       if (tracing) t_run = now_ticks();
     }
     __syncthreads();
-    const Task t = sm.task;
+    Task t = sm.task;
+    const bool load_cache = sm.need_cache != 0;
     __syncthreads();
+    if (load_cache) {
+      load_layer_cache(p, t.layer, sm);
+      __syncthreads();
+      if (tid == 0) {
+        if (p.mode == ETC_SCHED_STATIC && !wait_deps(p, sm.task, deadline, sm)) sm.task.kind = K_NONE;
+        if (tracing) t_run = now_ticks();
+      }
+      __syncthreads();
+      t = sm.task;
+      __syncthreads();
+    }
     if (t.kind == K_NONE) break;
     KLayer& L = p.layer[t.layer];
     run_task<TE>(p, L, t, sm);
