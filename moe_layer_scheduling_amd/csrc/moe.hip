@@ -684,12 +684,14 @@ ETC_SMALL_TASK void scan_task(KArgs& p, KLayer& L, int layer, Smem& sm) {
       run += v;
     }
   }
-  // the down split: enough down tasks to feed every worker twice, when the combine
-  // is atomic (partial sums over ffn chunks add into the same accumulator)
+  // the down split: enough down tasks to give every worker one, when the combine is
+  // atomic (partial sums over ffn chunks add into the same accumulator).  One round of
+  // longer tasks beat two rounds of shorter ones on decode-sized batches (fewer
+  // pipeline fills and epilogues per byte of weights).
   if (tid == 0) {
     int nS = 1;
     if (p.combine == ETC_COMBINE_ATOMIC && RT > 0) {
-      const int want = 2 * p.workers;
+      const int want = p.workers;
       nS = (RT * p.n2 >= want) ? 1 : min(p.n1, cdiv(want, RT * p.n2));
     }
     const int gpc = cdiv(p.n1, nS);
