@@ -156,6 +156,8 @@ struct RouteSmem {
   float rs[BT];
   unsigned emask[MAXE];  // tokens of the tile that selected each expert
   float bias[MAXE];
+  int soff[MAXE + 1];    // single-tile scan: first sorted row of each expert
+  int stmp[2 * NWAVE];
   int sel[BT][MAXK];
 };
 struct ScanSmem {
@@ -611,6 +613,62 @@ ETC_DEV void block_exclusive_scan2(int a, int b, int* tmp, int& pa, int& pb, int
   pb = by + y - b;
 }
 
+// The layer's plan words (thread 0), from its number of row tiles RT.  The down split:
+// enough down tasks to give every worker one, when the combine is atomic (partial sums
+// over ffn chunks add into the same accumulator).  One round of longer tasks beat two
+// rounds of shorter ones on decode-sized batches (fewer pipeline fills and epilogues
+// per byte of weights).
+ETC_DEV void write_plan(KArgs& p, KLayer& L, int layer, int RT) {
+  const int n_rt = p.n_rt;
+  int nS = 1;
+  if (p.combine == ETC_COMBINE_ATOMIC && RT > 0) {
+    const int want = p.workers;
+    nS = (RT * p.n2 >= want) ? 1 : min(p.n1, cdiv(want, RT * p.n2));
+  }
+  const int gpc = cdiv(p.n1, nS);
+  nS = cdiv(p.n1, gpc);
+  const int ngu = RT * p.n1, nd = RT * p.n2 * nS, nf = n_rt;
+  const int base = (layer == 0) ? 0 : gp(p.layer[layer - 1].plan)[PL_NEXTBASE];
+  st_shared(L.plan + PL_RT, RT);
+  st_shared(L.plan + PL_NGU, ngu);
+  st_shared(L.plan + PL_ND, nd);
+  st_shared(L.plan + PL_NF, nf);
+  st_shared(L.plan + PL_NS, nS);
+  st_shared(L.plan + PL_GPC, gpc);
+  st_shared(L.plan + PL_NEXTBASE, base + n_rt + p.n_perm + ngu + nd + nf);
+}
+
+// S for a layer of a single routing tile, run by that tile's R task straight from its
+// LDS results (the tokens that selected each expert, the selections): counts, scans,
+// the tile's offsets, the plan and the permutation, with no global round trip between
+// routing and scan.  Every thread calls this.
+ETC_DEV void scan_single_tile(KArgs& p, KLayer& L, int layer, Smem& sm) {
+  const int tid = threadIdx.x, E = p.E, K = p.K, nt = p.T;
+  RouteSmem& R = sm.u.r;
+  const int cnt = tid < E ? __popc(R.emask[tid]) : 0;
+  int off = 0, rtb = 0, total_rows = 0, RT = 0;
+  block_exclusive_scan2(cnt, cdiv(cnt, BM), R.stmp, off, rtb, total_rows, RT);
+  if (tid < E) {
+    R.soff[tid] = off;
+    st_shared(L.counts + tid, cnt);
+    st_shared(L.offsets + tid, off);
+    st_shared(L.rt_base + tid, rtb);
+    st_shared(L.tile_off + tid, off);
+  }
+  if (tid == 0) {
+    st_shared(L.offsets + E, total_rows);
+    st_shared(L.rt_base + E, RT);
+    write_plan(p, L, layer, RT);
+  }
+  __syncthreads();
+  for (int a = tid; a < nt * K; a += MNT) {
+    const int t = a / K, j = a - t * K, e = R.sel[t][j];
+    const int r = R.soff[e] + __popc(R.emask[e] & ((1u << t) - 1u));
+    st_shared(L.sorted_assign + r, a);
+    st_shared(L.pos + a, r);
+  }
+}
+
 ETC_SMALL_TASK void scan_task(KArgs& p, KLayer& L, int layer, Smem& sm) {
   const int tid = threadIdx.x;
   const int E = p.E, K = p.K, n_rt = p.n_rt;
@@ -684,28 +742,7 @@ ETC_SMALL_TASK void scan_task(KArgs& p, KLayer& L, int layer, Smem& sm) {
       run += v;
     }
   }
-  // the down split: enough down tasks to give every worker one, when the combine is
-  // atomic (partial sums over ffn chunks add into the same accumulator).  One round of
-  // longer tasks beat two rounds of shorter ones on decode-sized batches (fewer
-  // pipeline fills and epilogues per byte of weights).
-  if (tid == 0) {
-    int nS = 1;
-    if (p.combine == ETC_COMBINE_ATOMIC && RT > 0) {
-      const int want = p.workers;
-      nS = (RT * p.n2 >= want) ? 1 : min(p.n1, cdiv(want, RT * p.n2));
-    }
-    const int gpc = cdiv(p.n1, nS);
-    nS = cdiv(p.n1, gpc);
-    const int ngu = RT * p.n1, nd = RT * p.n2 * nS, nf = n_rt;
-    const int base = (layer == 0) ? 0 : gp(p.layer[layer - 1].plan)[PL_NEXTBASE];
-    st_shared(L.plan + PL_RT, RT);
-    st_shared(L.plan + PL_NGU, ngu);
-    st_shared(L.plan + PL_ND, nd);
-    st_shared(L.plan + PL_NF, nf);
-    st_shared(L.plan + PL_NS, nS);
-    st_shared(L.plan + PL_GPC, gpc);
-    st_shared(L.plan + PL_NEXTBASE, base + n_rt + p.n_perm + ngu + nd + nf);
-  }
+  if (tid == 0) write_plan(p, L, layer, RT);
   if (staged) {
     __syncthreads();
     const int n = n_rt * E;
@@ -1143,7 +1180,21 @@ ETC_DEV void trace_record(KArgs& p, const Task& t, uint64_t t_claim, uint64_t t_
 template <typename TE>
 ETC_DEV void run_task(KArgs& p, KLayer& L, const Task& t, Smem& sm) {
   const int tid = threadIdx.x;
-  if (t.kind == K_R) {
+  if (t.kind == K_R && p.n_rt == 1) {
+    // the layer's only routing tile: S follows on the tile's LDS results, and one
+    // publish covers both
+    route_task<TE>(p, L, t.a, sm);
+    __syncthreads();
+    const uint64_t t0 = now_ticks();
+    scan_single_tile(p, L, t.layer, sm);
+    if (tid == 0) ev_add_relaxed(L.ev_route, 1);
+    after_scan(p, t.layer, sm);
+    if (tid == 0 && (p.flags & ETC_FLAG_TRACE)) {
+      Task st;
+      st.kind = K_S; st.layer = t.layer; st.a = st.b = st.c = st.d = 0;
+      trace_record(p, st, t0, t0, now_ticks());
+    }
+  } else if (t.kind == K_R) {
     route_task<TE>(p, L, t.a, sm);
     publish_shared();
     if (tid == 0) {
