@@ -198,6 +198,13 @@ struct Smem {
   // layers whose ev_scan / ev_perm this workgroup has already acquired at their targets
   // (bit l): later waits on them return at once (static mode, thread 0)
   unsigned scan_seen, perm_seen;
+  // static mode: the ticket a gate/up or down task drew for the workgroup's next claim
+  // while its epilogue ran (-1: none), so the claim's atomic round trip overlaps the
+  // task instead of sitting between tasks (thread 0)
+  int next_ticket;
+  // static mode: first ticket of layer l's successor once known (-1: not yet), so the
+  // claims of later layers skip earlier layers without reading their plans (thread 0)
+  int lbase[MAXL + 1];
   int ibuf[4];
   LayerCache lc;
 };
@@ -785,6 +792,9 @@ ETC_SMALL_TASK void perm_task(KArgs& p, KLayer& L, int tau) {
 
 // ------------------------------------------------------------------ GU / D / F
 
+// Static mode: the next ticket of this workgroup's XCD queue (see claim_static).
+ETC_DEV int static_ticket(KArgs& p) { return xcd_ticket(p.sched); }
+
 template <typename TE>
 ETC_TASK void gateup_task(KArgs& p, KLayer& L, int e, int m, int n, Smem& sm) {
   using Tile = KTile<TE, MNT>;
@@ -820,6 +830,11 @@ ETC_TASK void gateup_task(KArgs& p, KLayer& L, int e, int m, int n, Smem& sm) {
   }
   f32x4 acc[4][Tile::NJ];
   Tile::run(Ts.gemm, rowp, H, valid, acc);
+  // static mode: draw the next ticket now; its atomic round trip overlaps the epilogue
+  // (issued before the tile, it would hold up the tile's first wait for its copies)
+  const bool prefetch = p.mode == ETC_SCHED_STATIC;
+  int next = -1;
+  if (prefetch && tid == 0) next = static_ticket(p);
 
   // SwiGLU into LDS (float, row stride BN1 + 1 words), then whole rows out to hbuf:
   // column block j of this wave is gate (j even) or up (j odd) for ffn columns
@@ -857,6 +872,7 @@ ETC_TASK void gateup_task(KArgs& p, KLayer& L, int e, int m, int n, Smem& sm) {
       st_shared8(hb + (size_t)(r0 + row) * F + f0 + c, v);
     }
   }
+  if (prefetch && tid == 0) sm.next_ticket = next;
 }
 
 template <typename TE>
@@ -901,6 +917,9 @@ ETC_TASK void down_task(KArgs& p, KLayer& L, int e, int m, int n2i, int s, int g
   }
   f32x4 acc[4][Tile::NJ];
   Tile::run(Ts.gemm, rowp, klen, valid, acc);
+  const bool prefetch = p.mode == ETC_SCHED_STATIC;  // as in gateup_task
+  int next = -1;
+  if (prefetch && tid == 0) next = static_ticket(p);
 
   // The tile goes through LDS first (row stride BN2 + 1 words: both passes free of bank
   // conflicts; the LDS of the GEMM is free once Tile::run has returned), so that the
@@ -939,6 +958,7 @@ ETC_TASK void down_task(KArgs& p, KLayer& L, int e, int m, int n2i, int s, int g
       }
     }
   }
+  if (prefetch && tid == 0) sm.next_ticket = next;
 }
 
 template <typename TE>
@@ -975,7 +995,6 @@ ETC_SMALL_TASK void finalize_task(KArgs& p, KLayer& L, int tau) {
 
 // ------------------------------------------------------------------ scheduling
 
-// Static: the ticket's task; waits for S of a layer before decoding past it.
 // Static mode: the fixed task order (per layer: all R, all P, all GU, all D, all F) is cut
 // into chunks of G consecutive tasks, chunk c belonging to queue c mod Q; workgroup b
 // draws from queue b mod Q.  The dispatcher places workgroup b on XCD b mod 8, so with
@@ -984,13 +1003,22 @@ ETC_SMALL_TASK void finalize_task(KArgs& p, KLayer& L, int tau) {
 // instead of being fetched once per XCD.  G = workers / Q, one task per CU of the XCD.
 // Each queue hands out its tasks in the global order and has at least one workgroup
 // (Q <= workers), so the smallest waiting task always has its inputs claimed by
-// workgroups that are not waiting on it: the order stays deadlock-free.
-ETC_DEV int static_ticket(KArgs& p) { return xcd_ticket(p.sched); }
-
+// workgroups that are not waiting on it: the order stays deadlock-free.  A gate/up or
+// down task draws its workgroup's next ticket while it runs; that ticket is larger than
+// the running task's, so the smallest unfinished ticket is still the current task of
+// its workgroup and the argument holds.
+//
+// Static: the ticket's task (the one drawn during the previous task, if any); waits for
+// S of a layer before decoding past it.
 ETC_DEV bool claim_static(KArgs& p, Task& t, uint64_t deadline, Smem& sm) {
-  const int ticket = static_ticket(p);
+  const int ticket = sm.next_ticket >= 0 ? sm.next_ticket : static_ticket(p);
+  sm.next_ticket = -1;
   int base = 0;
   for (int l = 0; l < p.L; ++l) {
+    if (sm.lbase[l + 1] >= 0 && ticket >= sm.lbase[l + 1]) {
+      base = sm.lbase[l + 1];
+      continue;
+    }
     KLayer& L = p.layer[l];
     t.layer = l;
     if (ticket < base + p.n_rt) { t.kind = K_R; t.a = ticket - base; return true; }
@@ -1024,6 +1052,7 @@ ETC_DEV bool claim_static(KArgs& p, Task& t, uint64_t deadline, Smem& sm) {
     off -= nd;
     if (off < nf) { t.kind = K_F; t.a = off; return true; }
     base = plan(PL_NEXTBASE);
+    sm.lbase[l + 1] = base;
   }
   t.kind = K_NONE;
   return true;
@@ -1307,6 +1336,8 @@ __global__ __launch_bounds__(MNT) void moe_kernel(Args pk) {
     sm.lc.layer = -1;
     sm.scan_seen = 0u;
     sm.perm_seen = 0u;
+    sm.next_ticket = -1;
+    for (int l = 0; l <= MAXL; ++l) sm.lbase[l] = -1;
   }
   while (true) {
     // Thread 0 claims a task.  A gate/up, down or finalize task of a layer whose plan the

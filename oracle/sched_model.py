@@ -193,28 +193,40 @@ def queue_ticket(q, i, queues, chunk):
     return ((i // chunk) * queues + q) * chunk + i % chunk
 
 
-def simulate_static(graph, workers, rng=None, queues=1, chunk=1):
+def simulate_static(graph, workers, rng=None, queues=1, chunk=1, prefetch=False):
     """Workers draw tickets and spin on the drawn task's waits.  With queues > 1 the
     order is dealt to the queues in chunks (queue_ticket) and worker w draws only from
-    queue w mod queues, each queue in its own order.  Returns the execution order;
-    raises RuntimeError on deadlock (no worker can move)."""
+    queue w mod queues, each queue in its own order.  With prefetch, a worker that runs
+    a GU or D task draws its next ticket while running it (the kernel overlaps that
+    atomic with the task) and takes that ticket afterwards.  Returns the execution
+    order; raises RuntimeError on deadlock (no worker can move)."""
     rng = rng or random.Random(0)
     order = static_order(graph)
     scans = _scan_of(graph)
     counters, executed = {}, []
     next_local = [0] * queues
     holding = [None] * workers  # task drawn by each worker
+    pending = [None] * workers  # ticket drawn ahead (prefetch), False: queue drained
     total = len(order) + len(graph)  # the tickets and one S per layer
+
+    def draw(w):
+        q = w % queues
+        g = queue_ticket(q, next_local[q], queues, chunk)
+        if g >= len(order):
+            return False
+        next_local[q] += 1
+        return order[g]
+
     while len(executed) < total:
-        # every idle worker draws its queue's next ticket (an atomic increment); a
-        # ticket past the end of the order means the queue is drained
+        # every idle worker draws its queue's next ticket (an atomic increment), or takes
+        # the one it drew ahead; a ticket past the end of the order means the queue is
+        # drained
         for w in range(workers):
-            q = w % queues
             if holding[w] is None:
-                g = queue_ticket(q, next_local[q], queues, chunk)
-                if g < len(order):
-                    holding[w] = order[g]
-                    next_local[q] += 1
+                t = pending[w] if pending[w] is not None else draw(w)
+                pending[w] = None
+                if t is not False:
+                    holding[w] = t
         movable = [w for w in range(workers)
                    if holding[w] is not None and _ready(holding[w], counters)]
         if not movable:
@@ -222,6 +234,8 @@ def simulate_static(graph, workers, rng=None, queues=1, chunk=1):
             raise RuntimeError(f"static schedule deadlocked holding {[(t.kind, t.key) for t in stuck]}")
         w = rng.choice(movable)
         t = holding[w]
+        if prefetch and t.kind in ("GU", "D"):
+            pending[w] = draw(w)
         before = dict(counters)
         _signal(t, counters)
         executed.append(t)

@@ -63,7 +63,8 @@ def test_static_and_dynamic_complete(T, H, F, E, k, L, plan):
 def test_static_xcd_queues_complete(T, H, F, E, k, L, plan):
     """The static order dealt in chunks to up to 8 queues (one per XCD), each worker
     drawing only from its own queue: every task runs once and every counter ends at
-    its target, for worker counts that do and do not divide into the queues."""
+    its target, for worker counts that do and do not divide into the queues, with and
+    without gate/up and down tasks drawing their worker's next ticket ahead."""
     rng = np.random.default_rng(T + 3 * E)
     idx = [_random_idx(rng, T, E, k, skew=1.1 if E >= 64 else 0.0) for _ in range(L)]
     graph = _graph_from_routing(T, H, F, k, E, idx, plan)
@@ -71,10 +72,11 @@ def test_static_xcd_queues_complete(T, H, F, E, k, L, plan):
     for workers in (1, 2, 8, 17, 64):
         queues = min(8, workers)
         for seed in range(2):
-            ex, ctr = sm.simulate_static(graph, workers, random.Random(seed), queues=queues,
-                                         chunk=workers // queues)
-            assert sm.check_execution(ex, graph) == final
-            assert ctr == final
+            for prefetch in (False, True):
+                ex, ctr = sm.simulate_static(graph, workers, random.Random(seed), queues=queues,
+                                             chunk=workers // queues, prefetch=prefetch)
+                assert sm.check_execution(ex, graph) == final
+                assert ctr == final
 
 
 def test_queue_tickets_partition_the_order():
