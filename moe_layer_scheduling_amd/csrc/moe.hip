@@ -885,17 +885,11 @@ ETC_TASK void down_task(KArgs& p, KLayer& L, int e, int m, int n2i, int s, int g
   TileSmem& Ts = sm.u.t;
   const int r0 = sm.lc.off[e] + m * BM;
   const int valid = min(BM, sm.lc.cnt[e] - m * BM);
-  for (int i = tid; i < BM; i += MNT) {
-    if (i < valid) {
-      const int a = gp(L.sorted_assign)[r0 + i];
-      Ts.row_tok[i] = a / K;
-      Ts.row_gate[i] = gp(L.topk_w)[a];
-    } else {
-      Ts.row_tok[i] = -1;
-      Ts.row_gate[i] = 0.f;
-    }
-  }
-  __syncthreads();
+  // The operand rows are the tile's rows of the sorted activations, which do not depend
+  // on the tokens: the (token, slot) pair of each row is loaded now and used only by the
+  // epilogue, so its round trip overlaps the tile instead of preceding the first copy.
+  static_assert(BM <= MNT, "one row per thread");
+  const int pair = tid < valid ? gp(L.sorted_assign)[r0 + tid] : -1;
 
   const int kb = s * gpc * BN1;
   const int klen = min(F, kb + gpc * BN1) - kb;
@@ -920,6 +914,7 @@ ETC_TASK void down_task(KArgs& p, KLayer& L, int e, int m, int n2i, int s, int g
   const bool prefetch = p.mode == ETC_SCHED_STATIC;  // as in gateup_task
   int next = -1;
   if (prefetch && tid == 0) next = static_ticket(p);
+  const float gate = pair >= 0 ? gp(L.topk_w)[pair] : 0.f;  // arrives during the staging
 
   // The tile goes through LDS first (row stride BN2 + 1 words: both passes free of bank
   // conflicts; the LDS of the GEMM is free once Tile::run has returned), so that the
@@ -937,6 +932,10 @@ ETC_TASK void down_task(KArgs& p, KLayer& L, int e, int m, int n2i, int s, int g
       for (int r = 0; r < 4; ++r)
         ct[(wm * 64 + i * 16 + (lane >> 4) * 4 + r) * CSTR + wn * Tile::WCOLS + j * 16 + (lane & 15)] =
             acc[i][j][r];
+  if (tid < BM) {
+    Ts.row_tok[tid] = pair >= 0 ? pair / K : -1;
+    Ts.row_gate[tid] = gate;
+  }
   __syncthreads();
   const int c0 = n2i * BN2, ncols = min(BN2, H - c0);
   if (p.combine == ETC_COMBINE_ATOMIC) {
