@@ -55,6 +55,19 @@ def test_mid_ragged_one_layer(lib, mode):
     _check(cfg, x, layers, driver.moe(lib, cfg, x, layers, mode=mode, max_tokens=300))
 
 
+SMALL = synth.MoEConfig("small", (18,), 512, 8, 2, 256, layers=2)
+
+
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
+@pytest.mark.parametrize("T", [1, 2, 17, 18])
+def test_one_or_two_token_tiles(lib, mode, T):
+    """Routing tiles of one or two tokens (the whole batch, or the last tile after a full
+    one) take the vector-ALU router instead of the matrix cores; fp32 layers too."""
+    for cfg in (SMALL, SMALL.with_(dtype="f32", hidden=256)):
+        layers, x = synth.make_layers(cfg), synth.make_x(cfg, T, call=T)
+        _check(cfg, x, layers, driver.moe(lib, cfg, x, layers, mode=mode, max_tokens=18))
+
+
 EDGE = synth.MoEConfig("edge", (70,), 384, 6, 2, 320, layers=2, zipf_s=0.3)
 
 
