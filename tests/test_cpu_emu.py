@@ -92,6 +92,28 @@ def test_histogram_too_large_for_lds(lib, mode):
     _check(cfg, x, layers, driver.moe(lib, cfg, x, layers, mode=mode))
 
 
+LIMITS = synth.MoEConfig("limits", (200,), 256, 256, 16, 128, layers=1, zipf_s=0.5)
+DEEP = synth.MoEConfig("deep", (40,), 256, 8, 2, 128, layers=4)
+
+
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
+@pytest.mark.parametrize("T", [40, 200])
+def test_most_experts_and_top_k(lib, mode, T):
+    """256 experts and top-16 (the largest the library accepts), with the permutation
+    scattered inside the scan (3 routing tiles) and by P tasks (13)."""
+    cfg = LIMITS
+    layers, x = synth.make_layers(cfg), synth.make_x(cfg, T, call=T)
+    _check(cfg, x, layers, driver.moe(lib, cfg, x, layers, mode=mode, max_tokens=200))
+
+
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
+def test_four_chained_layers(lib, mode):
+    """Four layers (the most one call chains) of a small shape."""
+    cfg = DEEP
+    layers, x = synth.make_layers(cfg), synth.make_x(cfg, 40)
+    _check(cfg, x, layers, driver.moe(lib, cfg, x, layers, mode=mode))
+
+
 def test_mid_two_layers_dynamic(lib):
     cfg = MID
     layers, x = synth.make_layers(cfg), synth.make_x(cfg, 300)

@@ -148,6 +148,34 @@ def test_event_tensor_final_state(mode):
     ws.reset()
 
 
+LIMITS = synth.MoEConfig("limits", (200,), 256, 256, 16, 128, layers=1, zipf_s=0.5)
+DEEP = synth.MoEConfig("deep", (40,), 256, 8, 2, 128, layers=4)
+
+
+@pytest.mark.parametrize("combine", ["atomic", "ordered"])
+@pytest.mark.parametrize("T", [40, 200])
+def test_most_experts_and_top_k(T, combine):
+    """256 experts and top-16 (the largest the library accepts), with the permutation
+    scattered inside the scan (3 routing tiles) and by P tasks (13), through one
+    workspace sized for 200 tokens."""
+    cfg = LIMITS
+    x, layers, ld, lnp = _setup(cfg, T, call=T)
+    ws = binding.MoEWorkspace(200, cfg.hidden, cfg.experts, cfg.top_k, cfg.ffn, 1,
+                              torch.bfloat16, combine)
+    say(f"limits T={T} combine={combine}")
+    gpu = run_moe(x.cuda(), ld, cfg.top_k, mode="static", combine=combine, workspace=ws)
+    say(_compare(cfg, x, lnp, gpu))
+
+
+def test_four_chained_layers():
+    """Four layers (the most one call chains) of a small shape."""
+    cfg = DEEP
+    x, layers, ld, lnp = _setup(cfg, 40)
+    say("four layers")
+    gpu = run_moe(x.cuda(), ld, cfg.top_k, mode="static")
+    say(_compare(cfg, x, lnp, gpu))
+
+
 # ------------------------------------------------------------------ workload shapes
 
 
