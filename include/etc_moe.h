@@ -200,7 +200,7 @@ etc_status etc_splitk_gemm(int32_t M, int32_t N, int32_t K, int32_t split_k, con
 
 size_t etc_splitk_workspace_size(int32_t M, int32_t N, int32_t split_k);
 
-/* Clear a freshly allocated workspace (enqueues a memset of its control words on
+/* Clear a freshly allocated workspace (enqueues a memset of all workspace_bytes on
  * `stream`).  Needed once after allocation, and after a call that failed with a
  * device timeout or used ETC_FLAG_KEEP_COUNTERS. */
 etc_status etc_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
