@@ -152,3 +152,69 @@ def check_event_tensor(read_i32, layout, T, H, F, k, E, gpu, layers):
             assert comb[tau] == final[("comb", 0, tau)], (l, tau)
             assert done[tau] == 1
         assert not comb[n_rt:].any() and not done[n_rt:].any()
+
+
+TRACE_KIND = {"R": 1, "S": 2, "GU": 3, "D": 4, "F": 5, "P": 6}
+
+
+def check_trace_causality(records, T, H, F, k, E, gpu, layout, read_i32, layers,
+                          slack_ticks=200):
+    """The event tensor's dependencies, read off a trace of one call (ETC_FLAG_TRACE):
+    every task of the scheduler model (built from the GPU's own routing and down split)
+    has exactly one record, and no task began its body before every task whose signals
+    it waits for had signalled.
+
+    A record holds the task's claim start, the ticks spent claiming and waiting and the
+    ticks running, on the device's 100 MHz clock.  A producer's signal falls between
+    the start of its body and its end stamp, which is taken right after the signal, so
+    a consumer's body must start no earlier than the producer's end minus slack_ticks.
+    S runs inside the routing task whose signal completed ev_route; that task's record
+    ends after S, so S is only required to start after every routing task started."""
+    from oracle import sched_model as sm
+    from moe_layer_scheduling_amd import trace
+
+    d = trace.decode(records)
+    t_run = d["start"] + d["wait"]
+    t_end = t_run + d["run"]
+    index = {}
+    for i in range(len(d["kind"])):
+        key = (int(d["kind"][i]), int(d["layer"][i]), int(d["a"][i]), int(d["b"][i]),
+               int(d["c"][i]), int(d["d"][i]))
+        assert key not in index, f"task recorded twice: {key}"
+        index[key] = i
+
+    def rec(task):
+        f = list(task.key) + [0] * (4 - len(task.key))
+        return index[(TRACE_KIND[task.kind], task.layer, *f)]
+
+    tasks = []
+    for l in range(layers):
+        lay = layout(l)
+        _, _, _, BT, BM, BN1, BN2 = lay[6:13]
+        gpc = int(read_i32(lay[5], 8)[5])
+        counts = gpu["counts"][l]
+        sa = gpu["sa"][l]
+        off = np.concatenate([[0], np.cumsum(counts)])
+        tors = [list(sa[off[e]:off[e + 1]] // k) for e in range(E)]
+        plan = sm.Plan(BT=BT, BM=BM, BN1=BN1, BN2=BN2, GPC=gpc, PI=PERM_INLINE_RT)
+        R, S, P, GU, D, Fin = sm.build_layer(l, T, H, F, k, counts, plan, tors)
+        tasks += R + [S] + P + GU + D + Fin
+    assert len(tasks) == len(index), (len(tasks), len(index))
+    producers = {}
+    for t in tasks:
+        for ctr, _ in t.signals:
+            producers.setdefault(ctr, []).append(t)
+    checked = 0
+    for t in tasks:
+        i = rec(t)
+        for ctr, _ in t.waits:
+            for p in producers[ctr]:
+                j = rec(p)
+                if t.kind == "S":
+                    assert t_run[i] >= t_run[j], ("S before a routing task", t.layer, p.key)
+                else:
+                    assert t_run[i] >= t_end[j] - slack_ticks, (
+                        f"{t.kind}{t.key} (layer {t.layer}) began {int(t_end[j] - t_run[i])} ticks "
+                        f"before {p.kind}{p.key} signalled {ctr}")
+                checked += 1
+    return checked

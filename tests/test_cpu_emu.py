@@ -191,6 +191,35 @@ def test_trace_has_one_record_per_task(lib, mode, T):
     assert s["span_us"] > 0 and 0 < s["busy_fraction"] <= 1
 
 
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
+def test_trace_respects_every_dependency(lib, mode):
+    """Read off the trace of one call: no task began before its producers signalled."""
+    cfg = MID.with_(layers=2)
+    T = 100
+    layers, x = synth.make_layers(cfg), synth.make_x(cfg, T, call=11)
+    g = driver.moe(lib, cfg, x, layers, mode=mode, flags=binding.FLAG_TRACE)
+    _check(cfg, x, layers, g)
+    n = ctypes.c_int32.from_address(g["wptr"] + 4 * binding.W_TRACE_LAST).value
+    lay0 = lib_layout(lib, T, cfg, 0)
+    rec = np.frombuffer((ctypes.c_uint64 * (4 * n)).from_address(g["wptr"] + lay0[13]),
+                        dtype=np.uint64).reshape(n, 4)
+
+    def read(off, cnt):
+        return np.array((ctypes.c_int32 * cnt).from_address(g["wptr"] + off))
+
+    args = (T, cfg.hidden, cfg.ffn, cfg.top_k, cfg.experts, g, lambda l: lib_layout(lib, T, cfg, l),
+            read, cfg.layers)
+    checked = moe_check.check_trace_causality(rec, *args)
+    assert checked > 1000
+    # the check itself: a finalize task moved to begin at the call's first tick fails it
+    bad = rec.copy()
+    i = int(np.nonzero((bad[:, 0] & 15) == 5)[0][0])
+    bad[i, 1] = bad[:, 1].min()
+    bad[i, 2] &= np.uint64(0xFFFFFFFF)  # no claim or wait ticks
+    with pytest.raises(AssertionError, match="began"):
+        moe_check.check_trace_causality(bad, *args)
+
+
 def lib_layout(lib, T, cfg, l):
     out = (ctypes.c_int64 * binding.LAYOUT_WORDS)()
     assert lib.etc_moe_workspace_layout(T, cfg.hidden, cfg.experts, cfg.top_k, cfg.ffn,

@@ -148,6 +148,33 @@ def test_event_tensor_final_state(mode):
     ws.reset()
 
 
+def _trace_check(cfg, T, ws, gpu):
+    rec = ws.read_trace()
+
+    def read(off, cnt):
+        return ws.view(off, cnt, torch.int32).cpu().numpy()
+
+    return moe_check.check_trace_causality(rec, T, cfg.hidden, cfg.ffn, cfg.top_k, cfg.experts,
+                                           gpu, ws.layout, read, cfg.layers)
+
+
+@pytest.mark.parametrize("which", ["mid", "decode"])
+def test_trace_respects_every_dependency(which):
+    """On the device clock (a trace of one call): every task of the scheduler model ran
+    exactly once, and none began before every task whose signals it waits for had
+    signalled -- the event tensor's true dependencies hold on the hardware."""
+    cfg, T = (MID, 300) if which == "mid" else (synth.CONFIGS["decode"], 64)
+    x, layers, ld, lnp = _setup(cfg, T, call=13)
+    ws = binding.MoEWorkspace(T, cfg.hidden, cfg.experts, cfg.top_k, cfg.ffn, cfg.layers,
+                              torch.bfloat16)
+    say(f"trace {which} T={T}")
+    gpu = run_moe(x.cuda(), ld, cfg.top_k, mode="static", workspace=ws, flags=binding.FLAG_TRACE)
+    _compare(cfg, x, lnp, gpu)
+    checked = _trace_check(cfg, T, ws, gpu)
+    say(f"{checked} dependencies checked")
+    assert checked > 100
+
+
 LIMITS = synth.MoEConfig("limits", (200,), 256, 256, 16, 128, layers=1, zipf_s=0.5)
 DEEP = synth.MoEConfig("deep", (40,), 256, 8, 2, 128, layers=4)
 
