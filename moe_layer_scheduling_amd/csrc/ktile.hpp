@@ -128,11 +128,23 @@ struct KTile {
       static_for<NJ>([&](auto j) ETC_INLINE { boff[kk][j] = swz(BM + wn * WCOLS + j * 16 + (lane & 15), c); });
     });
 
-    auto issue = [&](int kt) ETC_INLINE {
+    // The copies of a stage: their sources and slot are formed first (prep, before the
+    // step's barrier), so that after the barrier only the copies themselves go out and
+    // the MFMAs resume at once.
+    auto prep = [&](int kt, const char* (&src)[LOADS], char*& slot) ETC_INLINE {
       const int st = min(kt, last);  // past the last stage: re-read it into an unread slot
       const size_t off = (size_t)st * 128;
-      char* slot = smem + (kt % NSTAGE) * STAGE_BYTES + w * 8 * 128;
-      static_for<LOADS>([&](auto i) ETC_INLINE { lds_dma16(rowp[i] + off, slot + i * RSTEP * 128); });
+      slot = smem + (kt % NSTAGE) * STAGE_BYTES + w * 8 * 128;
+      static_for<LOADS>([&](auto i) ETC_INLINE { src[i] = rowp[i] + off; });
+    };
+    auto go = [&](const char* const (&src)[LOADS], char* slot) ETC_INLINE {
+      static_for<LOADS>([&](auto i) ETC_INLINE { lds_dma16(src[i], slot + i * RSTEP * 128); });
+    };
+    auto issue = [&](int kt) ETC_INLINE {
+      const char* src[LOADS];
+      char* slot;
+      prep(kt, src, slot);
+      go(src, slot);
     };
     auto read = [&](Half& f, int kt, auto kk) ETC_INLINE {
       const char* base = smem + (kt % NSTAGE) * STAGE_BYTES;
@@ -180,8 +192,11 @@ struct KTile {
       interleave(std::integral_constant<int, 0>{});
       // stage kt+1 has landed everywhere, and every wave has finished reading slot
       // kt mod 3 (its reads completed before the barrier): stage kt+3 may overwrite it
+      const char* src[LOADS];
+      char* slot;
+      prep(kt + 3, src, slot);
       vm_wait_barrier<LOADS>();
-      issue(kt + 3);
+      go(src, slot);
       read(h0, kt + 1, K0);  // past the last stage: unused reads of an unused slot
       mma(h1);
       interleave(std::integral_constant<int, LOADS>{});
