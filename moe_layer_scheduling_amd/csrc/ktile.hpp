@@ -34,8 +34,9 @@
 // element r of acc[i][j] in lane l is row wm*64 + 16*i + 4*(l/16) + r, column
 // wn*WCOLS + 16*j + (l % 16).  Row blocks past `rows` (the valid row count) skip their
 // MFMAs: the count of live blocks is fixed per tile and selects one of five branch-free
-// instances of the loop.  Register arrays are indexed through static_for, so every
-// index is a compile-time constant.
+// instances of the loop; with at most 64 valid rows a second set of instances also
+// drops the copies of A rows 64..127.  Register arrays are indexed through static_for,
+// so every index is a compile-time constant.
 #pragma once
 
 #include <utility>
@@ -94,12 +95,24 @@ struct KTile {
     // scalar branches instead of exec-masked code
     const int wm = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) / WN;
     const int live = __builtin_amdgcn_readfirstlane(min(4, max(0, cdiv(rows - wm * 64, 16))));
-    switch (live) {
-      case 4: pipeline<4>(smem, rowp, klen, acc); break;
-      case 3: pipeline<3>(smem, rowp, klen, acc); break;
-      case 2: pipeline<2>(smem, rowp, klen, acc); break;
-      case 1: pipeline<1>(smem, rowp, klen, acc); break;
-      default: pipeline<0>(smem, rowp, klen, acc); break;
+    // At most 64 valid rows (decode batches, the last row tile of an expert): the copies
+    // of A rows 64..127 are dropped as well as their MFMAs; those LDS rows are never read.
+    if (rows <= 64) {
+      switch (live) {
+        case 4: pipeline<4, true>(smem, rowp, klen, acc); break;
+        case 3: pipeline<3, true>(smem, rowp, klen, acc); break;
+        case 2: pipeline<2, true>(smem, rowp, klen, acc); break;
+        case 1: pipeline<1, true>(smem, rowp, klen, acc); break;
+        default: pipeline<0, true>(smem, rowp, klen, acc); break;
+      }
+    } else {
+      switch (live) {
+        case 4: pipeline<4, false>(smem, rowp, klen, acc); break;
+        case 3: pipeline<3, false>(smem, rowp, klen, acc); break;
+        case 2: pipeline<2, false>(smem, rowp, klen, acc); break;
+        case 1: pipeline<1, false>(smem, rowp, klen, acc); break;
+        default: pipeline<0, false>(smem, rowp, klen, acc); break;
+      }
     }
     // the last copies (re-reads past the last stage) land before LDS is reused
     __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
@@ -112,9 +125,12 @@ struct KTile {
     u32x4 a[4], b[NJ];
   };
 
-  template <int LIVE>
+  template <int LIVE, bool HALF>
   ETC_DEV static void pipeline(char* smem, const char* const (&rowp)[LOADS], int klen,
                                f32x4 (&acc)[4][NJ]) {
+    // copies this thread issues per stage: with HALF, those of A rows 64..127 (copy
+    // indices ALOADS/2 .. ALOADS-1) are dropped, and every wait counts NL
+    constexpr int NL = LOADS - (HALF ? ALOADS / 2 : 0);
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = w / WN, wn = w % WN;
@@ -138,7 +154,10 @@ struct KTile {
       static_for<LOADS>([&](auto i) ETC_INLINE { src[i] = rowp[i] + off; });
     };
     auto go = [&](const char* const (&src)[LOADS], char* slot) ETC_INLINE {
-      static_for<LOADS>([&](auto i) ETC_INLINE { lds_dma16(src[i], slot + i * RSTEP * 128); });
+      static_for<LOADS>([&](auto i) ETC_INLINE {
+        constexpr int I = decltype(i)::value;
+        if constexpr (!(HALF && I >= ALOADS / 2 && I < ALOADS)) lds_dma16(src[i], slot + i * RSTEP * 128);
+      });
     };
     auto issue = [&](int kt) ETC_INLINE {
       const char* src[LOADS];
@@ -180,7 +199,7 @@ struct KTile {
     issue(0);
     issue(1);
     issue(2);
-    vm_wait_barrier<2 * LOADS>();  // stage 0 has landed
+    vm_wait_barrier<2 * NL>();  // stage 0 has landed
     read(h0, 0, K0);
     for (int kt = 0; kt < nk; ++kt) {
       // the first-half fragments were read before the previous MFMAs and have arrived;
@@ -195,11 +214,11 @@ struct KTile {
       const char* src[LOADS];
       char* slot;
       prep(kt + 3, src, slot);
-      vm_wait_barrier<LOADS>();
+      vm_wait_barrier<NL>();
       go(src, slot);
       read(h0, kt + 1, K0);  // past the last stage: unused reads of an unused slot
       mma(h1);
-      interleave(std::integral_constant<int, LOADS>{});
+      interleave(std::integral_constant<int, NL>{});
     }
   }
 };
