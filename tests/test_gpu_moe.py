@@ -223,6 +223,28 @@ def test_decode_sequence_one_kernel():
         say(_compare(cfg, x, lnp, gpu))
 
 
+@pytest.mark.timeout(400)
+def test_decode_32_calls_drawn_token_counts():
+    """The decode workload as defined: 32 calls whose token counts are drawn from
+    {1, 4, 16, 64} (seeded, every count at least once) through one workspace and the one
+    compiled kernel, each call checked against the oracle."""
+    cfg = synth.CONFIGS["decode"]
+    layers = synth.make_layers(cfg)
+    ld = layers_to_device(layers)
+    lnp = synth.layers_as_numpy(layers)
+    ws = binding.MoEWorkspace(64, cfg.hidden, cfg.experts, cfg.top_k, cfg.ffn, 1, torch.bfloat16)
+    rng = np.random.default_rng(0)
+    seq = [int(t) for t in rng.choice([1, 4, 16, 64], size=32)]
+    for i, T in enumerate((1, 4, 16, 64)):  # every count at least once
+        if T not in seq:
+            seq[i] = T
+    for i, T in enumerate(seq):
+        x = synth.make_x(cfg, T, call=100 + i)
+        say(f"decode call {i}: T={T}")
+        gpu = run_moe(x.cuda(), ld, cfg.top_k, mode="static", workspace=ws)
+        _compare(cfg, x, lnp, gpu)
+
+
 def test_finegrained_zipf():
     cfg = synth.CONFIGS["finegrained"]
     x, layers, ld, lnp = _setup(cfg, 256)
