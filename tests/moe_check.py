@@ -218,3 +218,57 @@ def check_trace_causality(records, T, H, F, k, E, gpu, layout, read_i32, layers,
                         f"before {p.kind}{p.key} signalled {ctr}")
                 checked += 1
     return checked
+
+
+def check_identical_experts(x, layers, eps, out):
+    """Every expert holds the same weights: whatever the routing, each token's output is
+    the single FFN of its normalised input (the gates sum to 1), rounded to bfloat16.
+    Returns (max error, max |reference|)."""
+    from oracle.numerics import round_bf16
+
+    lay = layers[0]
+    xn = om.rmsnorm(x, lay["gamma"], eps)
+    ffn = om.expert_ffn(round_bf16(xn), lay["w_gate"][0], lay["w_up"][0], lay["w_down"][0], "bf16")
+    ref = round_bf16(ffn)
+    err = float(np.max(np.abs(out - ref)))
+    ref_max = float(np.max(np.abs(ref)))
+    assert err <= OUT_TOL["bf16"] * ref_max, (err, ref_max)
+    return err, ref_max
+
+
+DEGENERATE = {
+    # one expert, top-1: every gate is 1
+    "one_expert": dict(name="one", tokens=(40,), hidden=256, experts=1, top_k=1, ffn=128, layers=2),
+    # top-k = E: every expert for every token, the gates are the full softmax
+    "all_experts": dict(name="all", tokens=(40,), hidden=256, experts=4, top_k=4, ffn=128, layers=1),
+    # every expert with the same weights: the output does not depend on the routing
+    "identical_experts": dict(name="same", tokens=(40,), hidden=256, experts=8, top_k=2, ffn=128,
+                              layers=1),
+}
+
+
+def degenerate_case(which):
+    """(config, layers, x) of a degenerate case of the method (see DEGENERATE)."""
+    from moe_layer_scheduling_amd import synth
+
+    cfg = synth.MoEConfig(**DEGENERATE[which])
+    layers = synth.make_layers(cfg)
+    if which == "identical_experts":
+        for lay in layers:
+            for key in ("w_gate", "w_up", "w_down"):
+                lay[key][:] = lay[key][0:1]
+    return cfg, layers, synth.make_x(cfg, 40)
+
+
+def check_degenerate(which, cfg, x, layers, gpu):
+    from moe_layer_scheduling_amd import synth
+
+    st = compare(synth.as_numpy(x), synth.layers_as_numpy(layers), cfg.top_k, cfg.eps, cfg.dtype, gpu)
+    if which == "one_expert":
+        assert np.all(gpu["w"] == 1.0) and np.all(gpu["idx"] == 0)
+    if which == "all_experts":
+        for l in range(cfg.layers):
+            assert np.array_equal(np.sort(gpu["idx"][l], axis=1), np.tile(np.arange(cfg.experts), (x.shape[0], 1)))
+    if which == "identical_experts":
+        check_identical_experts(synth.as_numpy(x), synth.layers_as_numpy(layers), cfg.eps, gpu["outs"][0])
+    return st

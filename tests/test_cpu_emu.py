@@ -107,6 +107,16 @@ def test_most_experts_and_top_k(lib, mode, T):
 
 
 @pytest.mark.parametrize("mode", ["static", "dynamic"])
+@pytest.mark.parametrize("which", sorted(moe_check.DEGENERATE))
+def test_degenerate_cases(lib, mode, which):
+    """One expert with top-1, top-k equal to the expert count, identical experts."""
+    cfg, layers, x = moe_check.degenerate_case(which)
+    g = driver.moe(lib, cfg, x, layers, mode=mode)
+    assert g["status"] == 0
+    moe_check.check_degenerate(which, cfg, x, layers, g)
+
+
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
 def test_four_chained_layers(lib, mode):
     """Four layers (the most one call chains) of a small shape."""
     cfg = DEEP

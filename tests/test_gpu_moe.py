@@ -194,6 +194,16 @@ def test_most_experts_and_top_k(T, combine):
     say(_compare(cfg, x, lnp, gpu))
 
 
+@pytest.mark.parametrize("which", sorted(moe_check.DEGENERATE))
+def test_degenerate_cases(which):
+    """One expert with top-1, top-k equal to the expert count, identical experts (the
+    output must not depend on the routing)."""
+    cfg, layers, x = moe_check.degenerate_case(which)
+    say(f"degenerate {which}")
+    gpu = run_moe(x.cuda(), layers_to_device(layers), cfg.top_k, mode="static")
+    say(moe_check.check_degenerate(which, cfg, x, layers, gpu))
+
+
 def test_four_chained_layers():
     """Four layers (the most one call chains) of a small shape."""
     cfg = DEEP
