@@ -86,6 +86,22 @@ def expert_bytes(cfg):
     return 3 * cfg.hidden * cfg.ffn * es
 
 
+def algorithmic_work(cfg, T, counts):
+    """Algorithmic work of one call (no padded rows, no re-reads): expert flops (every
+    (token, slot) pair costs the gate, up and down products, 2*H*F flops each), router
+    flops, and the bytes that must move: the weights of every expert that receives a
+    token in some layer, the router weights, and x in / out per layer.  counts: the
+    per-layer expert counts of the call's routing.  Returns (flops_expert, flops_router,
+    bytes, expert-layers touched)."""
+    es = 2 if cfg.dtype == "bf16" else 4
+    touched = int(sum((np.asarray(c) > 0).sum() for c in counts))
+    flops = cfg.layers * T * cfg.top_k * 6 * cfg.hidden * cfg.ffn
+    flops_router = cfg.layers * 2 * T * cfg.hidden * cfg.experts
+    nbytes = (touched * expert_bytes(cfg) + cfg.layers * cfg.experts * cfg.hidden * es +
+              2 * T * cfg.hidden * es * cfg.layers)
+    return flops, flops_router, nbytes, touched
+
+
 def bench_moe(cfg, T, steps, warmup, mode, combine, with_cpu=False, trace_out=None):
     log(f"[bench] {cfg.name}: drawing inputs T={T}")
     layers, x, ld = moe_inputs(cfg, T)
@@ -117,12 +133,7 @@ def bench_moe(cfg, T, steps, warmup, mode, combine, with_cpu=False, trace_out=No
         trace.chrome_trace(rec, trace_out)
         with open(trace_out + ".summary.json", "w") as f:
             json.dump(trace_summary, f, indent=1)
-    es = 2 if cfg.dtype == "bf16" else 4
-    touched = int(sum((c > 0).sum() for c in counts))  # expert-layers with work
-    flops_bf16 = cfg.layers * T * cfg.top_k * 6 * cfg.hidden * cfg.ffn
-    flops_router = cfg.layers * 2 * T * cfg.hidden * cfg.experts
-    bytes_alg = (touched * expert_bytes(cfg) + cfg.layers * cfg.experts * cfg.hidden * es +
-                 2 * T * cfg.hidden * es * cfg.layers)
+    flops_bf16, flops_router, bytes_alg, touched = algorithmic_work(cfg, T, counts)
     res = {
         "tokens": T, "ms_per_step": ms, "launch_ms": launch_ms,
         "launch_ms_p10": float(np.percentile(per, 10)), "launch_ms_p90": float(np.percentile(per, 90)),
