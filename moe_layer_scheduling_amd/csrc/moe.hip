@@ -963,32 +963,58 @@ ETC_TASK void down_task(KArgs& p, KLayer& L, int e, int m, int n2i, int s, int g
 template <typename TE>
 ETC_SMALL_TASK void finalize_task(KArgs& p, KLayer& L, int tau) {
   constexpr int EPC = 16 / (int)sizeof(TE);
+  // chunks per thread whose loads are in flight together: the stores of one group are
+  // not waited for before the next group's loads go out
+  constexpr int U = 4;
   const int tid = threadIdx.x, H = p.H, K = p.K;
   const int t0 = tau * BT, nt = tile_rows(p, tau);
+  const int nch = nt * H / EPC;
   TE* out = static_cast<TE*>(L.out);
-  for (int c = tid; c < nt * H / EPC; c += MNT) {
-    const int t = t0 + (c * EPC) / H, h = (c * EPC) % H;
-    float v[EPC];
+  for (int cb = tid; cb < nch; cb += U * MNT) {
+    float v[U][EPC];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < EPC; ++i) v[u][i] = 0.f;
     if (p.combine == ETC_COMBINE_ATOMIC) {
+      f32x4 a[U][EPC / 4];
 #pragma unroll
-      for (int i = 0; i < EPC; i += 4) {
-        const f32x4 a = gld<f32x4>(p.out_acc + (size_t)t * H + h + i);
-        v[i] = a[0]; v[i + 1] = a[1]; v[i + 2] = a[2]; v[i + 3] = a[3];
+      for (int u = 0; u < U; ++u) {
+        const int c = min(cb + u * MNT, nch - 1);  // past the end: a repeat, never stored
+        const int t = t0 + (c * EPC) / H, h = (c * EPC) % H;
+#pragma unroll
+        for (int i = 0; i < EPC / 4; ++i) a[u][i] = gld<f32x4>(p.out_acc + (size_t)t * H + h + 4 * i);
       }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) v[u][i] = a[u][i / 4][i % 4];
     } else {
-#pragma unroll
-      for (int i = 0; i < EPC; ++i) v[i] = 0.f;
       for (int j = 0; j < K; ++j) {  // slot order
-        const float g = gp(L.topk_w)[t * K + j];
-        const float* y = p.ybuf + (size_t)gp(L.pos)[t * K + j] * H + h;
+        float g[U];
+        const float* y[U];
 #pragma unroll
-        for (int i = 0; i < EPC; i += 4) {
-          const f32x4 a = gld<f32x4>(y + i);
-          v[i] += g * a[0]; v[i + 1] += g * a[1]; v[i + 2] += g * a[2]; v[i + 3] += g * a[3];
+        for (int u = 0; u < U; ++u) {
+          const int c = min(cb + u * MNT, nch - 1);
+          const int t = t0 + (c * EPC) / H, h = (c * EPC) % H;
+          g[u] = gp(L.topk_w)[t * K + j];
+          y[u] = p.ybuf + (size_t)gp(L.pos)[t * K + j] * H + h;
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int i = 0; i < EPC; i += 4) {
+            const f32x4 a = gld<f32x4>(y[u] + i);
+            v[u][i] += g[u] * a[0]; v[u][i + 1] += g[u] * a[1];
+            v[u][i + 2] += g[u] * a[2]; v[u][i + 3] += g[u] * a[3];
+          }
       }
     }
-    st_shared16(out + (size_t)t0 * H, (uint32_t)(c * 16), pack16<TE>(v));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = cb + u * MNT;
+      if (c < nch) st_shared16(out + (size_t)t0 * H, (uint32_t)(c * 16), pack16<TE>(v[u]));
+    }
   }
 }
 
