@@ -8,6 +8,7 @@ import subprocess
 import sys
 
 import numpy as np
+import pytest
 
 import bench
 from moe_layer_scheduling_amd import synth
@@ -70,3 +71,25 @@ def test_source_hash_covers_the_kernel_sources(tmp_path, monkeypatch):
     (d / "moe.hip").write_text("// empty\n")
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     assert bench.source_hash() != h
+
+
+@pytest.mark.gpu
+def test_bench_line_on_the_gpu():
+    """One short bench.py run of the tiny workload prints the one JSON line with the
+    fields the contract names, a positive throughput and a roofline object."""
+    import json
+
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--workload", "tiny",
+                        "--steps", "3", "--warmup", "1", "--no-secondary", "--no-cpu-baseline"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr[-2000:]
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "cpu_baseline"):
+        assert key in line, key
+    assert line["n_gpus"] == 1 and line["steps"] == 3 and line["value"] > 0
+    roof = line["roofline"]
+    assert roof["bound"] == "mfma" and roof["unit"] == "TFLOP/s" and roof["peak"] == 2500.0
+    assert roof["achieved"] > 0 and abs(roof["frac"] - roof["achieved"] / roof["peak"]) < 1e-9
+    assert line["config"]["workload"].startswith("tiny")
