@@ -42,7 +42,8 @@ typedef enum {
   ETC_ERR_UNSUPPORTED = 2, /* valid shape this build does not handle (see each call) */
   ETC_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or too small */
   ETC_ERR_HIP = 4,         /* a HIP runtime call failed (device state unknown) */
-  ETC_ERR_TIMEOUT = 5,     /* device status: a wait exceeded its time limit, the kernel
+  ETC_ERR_TIMEOUT = 5,     /* device status: a wait saw no progress for 5 s (its limit
+                              restarts whenever what it watches changes), the kernel
                               stopped early and its outputs are not valid */
   ETC_ERR_NO_DEVICE = 6    /* no usable gfx950 device is current */
 } etc_status;
@@ -75,6 +76,12 @@ typedef enum { ETC_COMBINE_ATOMIC = 0, ETC_COMBINE_ORDERED = 1 } etc_combine;
                                uint32 ticks spent claiming and waiting, uint32 ticks
                                running, uint32 zero.  The number of records is int32 word
                                10 of the workspace after the call. */
+#define ETC_FLAG_ALLOW_DYNAMIC 0x4u /* etc_moe_layer: accept mode ETC_SCHED_DYNAMIC.  Without
+                                       this bit the mode returns ETC_ERR_UNSUPPORTED: an early
+                                       run of the dynamic MoE scheduler on MI355X did not
+                                       terminate and the cause has not been identified, so
+                                       the mode runs only where the caller asks for it (the
+                                       CPU execution harness).  Split-K ignores the bit. */
 
 /* Weights of one MoE layer (all device pointers).  dtype is the call's dtype except
  * gamma and router_bias, which are always float32.  Layouts follow nn.Linear
@@ -135,10 +142,8 @@ typedef struct {
  *   stream       hipStream_t
  * Errors: ETC_ERR_INVALID_ARG (null pointer, size or enum out of range, unaligned
  * pointer -- every tensor pointer must be 16-byte aligned), ETC_ERR_UNSUPPORTED
- * (H % 128, F % 64, E > 256, k > 16, L > 4; and mode ETC_SCHED_DYNAMIC unless the
- * process environment has ETC_ENABLE_DYNAMIC_SCHED=1 -- the dynamic scheduler is
- * disabled by default while a non-terminating run of it on MI355X is investigated),
- * ETC_ERR_WORKSPACE, ETC_ERR_HIP, ETC_ERR_NO_DEVICE.  Device-side timeouts are
+ * (H % 128, F % 64, E > 256, k > 16, L > 4; and mode ETC_SCHED_DYNAMIC unless flags
+ * has ETC_FLAG_ALLOW_DYNAMIC), ETC_ERR_WORKSPACE, ETC_ERR_HIP, ETC_ERR_NO_DEVICE.  Device-side timeouts are
  * reported by etc_query_device_status.
  */
 etc_status etc_moe_layer(int32_t tokens, int32_t hidden, int32_t experts, int32_t top_k,

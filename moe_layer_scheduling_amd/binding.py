@@ -22,6 +22,7 @@ MODES = {"static": 0, "dynamic": 1}
 COMBINES = {"atomic": 0, "ordered": 1}
 FLAG_KEEP_COUNTERS = 0x1
 FLAG_TRACE = 0x2
+FLAG_ALLOW_DYNAMIC = 0x4
 LAYOUT_WORDS = 16
 W_TRACE_LAST = 10  # control word holding the last traced call's record count
 
@@ -190,12 +191,16 @@ class SplitKWorkspace(Workspace):
 
 def moe_layer(x, layers, top_k, *, eps=1e-6, mode="static", combine="atomic", workspace=None,
               max_tokens=None, return_routing=False, return_layer_outputs=False, workers=0,
-              flags=0):
+              flags=0, check=False):
     """Run len(layers) chained MoE layers on x [T][H] (float32 or bfloat16 device tensor).
 
     layers: list of dicts of device tensors gamma [H] f32, w_router [E][H], optional
     router_bias [E] f32, w_gate [E][F][H], w_up [E][F][H], w_down [E][H][F] (x's dtype).
     Returns out, or (out, info) when routing or layer outputs are requested.
+
+    Device-side timeouts: when the binding allocates the workspace itself (workspace is
+    None) or check is True, it synchronises the stream after the call and raises
+    EtcError on a device timeout; otherwise the caller reads workspace.status().
     """
     lib = load_library()
     if x.dim() != 2:
@@ -206,7 +211,8 @@ def moe_layer(x, layers, top_k, *, eps=1e-6, mode="static", combine="atomic", wo
         raise ValueError(f"unsupported dtype {dtype}")
     L = len(layers)
     E, F = layers[0]["w_gate"].shape[0], layers[0]["w_gate"].shape[1]
-    if workspace is None:
+    own = workspace is None
+    if own:
         workspace = MoEWorkspace(max_tokens or max(T, 1), H, E, top_k, F, L, dtype, combine,
                                  device=x.device)
     if workspace.shape[1:] != (H, E, top_k, F, L) or workspace.dtype != dtype:
@@ -245,6 +251,8 @@ def moe_layer(x, layers, top_k, *, eps=1e-6, mode="static", combine="atomic", wo
                            workspace.ptr, workspace.nbytes, ws_max, MODES[mode],
                            COMBINES[combine], int(flags), int(workers), _stream())
     _check(st, "etc_moe_layer")
+    if (own or check) and T > 0:
+        _check(workspace.status(), "etc_moe_layer (device)")
     if layer_out is not None:
         info["layer_outputs"] = layer_out
     if return_routing or return_layer_outputs:
@@ -252,20 +260,25 @@ def moe_layer(x, layers, top_k, *, eps=1e-6, mode="static", combine="atomic", wo
     return out
 
 
-def splitk_gemm(A, B, split_k=8, *, mode="static", workspace=None, workers=0, flags=0):
-    """C = A @ B (bfloat16 in, float32 out) through split_k event-counted partials."""
+def splitk_gemm(A, B, split_k=8, *, mode="static", workspace=None, workers=0, flags=0,
+                check=False):
+    """C = A @ B (bfloat16 in, float32 out) through split_k event-counted partials.
+    Device-side timeouts are raised as for moe_layer."""
     lib = load_library()
     M, K = A.shape
     K2, N = B.shape
     if K != K2:
         raise ValueError("inner dimensions differ")
-    if workspace is None:
+    own = workspace is None
+    if own:
         workspace = SplitKWorkspace(M, N, split_k, device=A.device)
     C = torch.empty(M, N, dtype=torch.float32, device=A.device)
     st = lib.etc_splitk_gemm(M, N, K, split_k, _dev_ptr(A, "A", torch.bfloat16),
                              _dev_ptr(B, "B", torch.bfloat16), C.data_ptr(), workspace.ptr,
                              workspace.nbytes, MODES[mode], int(flags), int(workers), _stream())
     _check(st, "etc_splitk_gemm")
+    if own or check:
+        _check(workspace.status(), "etc_splitk_gemm (device)")
     return C
 
 

@@ -1,7 +1,6 @@
 // Device-side building blocks shared by the persistent kernels: storage types,
 // bfloat16 conversion, the event-counter primitives (signal / wait with a watchdog)
-// and wave-level reductions.  gfx950 (CDNA4), wave64, one 256-thread workgroup per
-// persistent worker.
+// and wave-level reductions.  gfx950 (CDNA4), wave64.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -12,7 +11,7 @@
 
 namespace etc {
 
-constexpr int NT = 256;  // threads per persistent workgroup (4 waves)
+constexpr int NT = 256;  // default threads per workgroup of a persistent kernel (4 waves)
 constexpr int WAVE = 64;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -264,33 +263,58 @@ ETC_DEV int xcd_ticket(int* sched) {
 // Waits poll with relaxed loads (no cache invalidation per poll: an agent-scope acquire
 // invalidates this CU's L1 and the XCD's L2 lines, which would keep evicting the operands
 // of the tiles running beside the waiter) and, once the condition holds, take one
-// acquire load of the same location, which synchronises with the producers.  Every wait
-// is bounded twice: by the 100 MHz real-time clock and by an iteration count, so a wait
-// ends even if the clock did not advance.
+// acquire load of the same location, which synchronises with the producers.
+//
+// Watchdog.  A wait gives up when what it watches has made no progress for `patience`
+// ticks of the 100 MHz real-time clock: the limit starts when the wait begins and starts
+// again whenever the polled value changes, so a long call whose counters keep moving is
+// never cut short.  It also gives up after SPIN_MAX_ITERS polls without progress, so a
+// wait ends even if the clock did not advance.  Giving up records ETC_ERR_TIMEOUT and
+// the wait's site in the control words and raises the abort flag; every other wait
+// sees the flag at its next check and returns false as well, so every workgroup leaves.
 constexpr int SPIN_MAX_ITERS = 1 << 24;
+constexpr int WATCH_EVERY = 16;  // polls between two checks of the clock and the abort flag
 
-ETC_DEV bool wait_give_up(int* sched, uint64_t deadline, int it, int where) {
-  if ((it & 15) != 0) return false;
-  if (ev_load_relaxed(sched + W_ABORT)) return true;
-  if (now_ticks() > deadline || it >= SPIN_MAX_ITERS) {
-    ev_store_relaxed(sched + W_STATUS, 5 /* ETC_ERR_TIMEOUT */);
-    ev_store_relaxed(sched + W_AUX, where);
-    ev_store(sched + W_ABORT, 1);
-    return true;
+struct Watchdog {
+  uint64_t limit;
+  int seen, quiet;
+  ETC_DEV void start(uint64_t patience, int value) {
+    limit = now_ticks() + patience;
+    seen = value;
+    quiet = 0;
   }
-  return false;
-}
+  // Called every WATCH_EVERY polls with the value the wait currently sees.  True when
+  // the call is aborted (by this wait or by another workgroup).
+  ETC_DEV bool expired(int* sched, uint64_t patience, int value, int where) {
+    if (ev_load_relaxed(sched + W_ABORT)) return true;
+    if (value != seen) {
+      start(patience, value);
+      return false;
+    }
+    quiet += WATCH_EVERY;
+    if (now_ticks() > limit || quiet >= SPIN_MAX_ITERS) {
+      ev_store_relaxed(sched + W_STATUS, 5 /* ETC_ERR_TIMEOUT */);
+      ev_store_relaxed(sched + W_AUX, where);
+      ev_store(sched + W_ABORT, 1);
+      return true;
+    }
+    return false;
+  }
+};
 
 // Spin (one lane) until *ctr >= target.  Returns false if the call was aborted, by
-// this wait timing out or by another workgroup.
-ETC_DEV bool spin_until_geq(const int* ctr, int target, int* sched, uint64_t deadline,
+// this wait giving up or by another workgroup.
+ETC_DEV bool spin_until_geq(const int* ctr, int target, int* sched, uint64_t patience,
                             int where) {
-  for (int it = 1;; ++it) {
-    if (ev_load_relaxed(ctr) >= target) {
+  Watchdog wd;
+  for (int it = 0;; ++it) {
+    const int v = ev_load_relaxed(ctr);
+    if (v >= target) {
       (void)ev_load(ctr);  // acquire: everything released before the counter reached it
       return true;
     }
-    if (wait_give_up(sched, deadline, it, where)) return false;
+    if (it == 0) wd.start(patience, v);
+    else if (it % WATCH_EVERY == 0 && wd.expired(sched, patience, v, where)) return false;
     __builtin_amdgcn_s_sleep(2);
   }
 }

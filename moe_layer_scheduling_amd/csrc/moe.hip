@@ -38,7 +38,6 @@
 // and whichever signal completes a counter enqueues the tasks it releases.
 // The token count T is a kernel argument; nothing in the code depends on its value.
 #include <float.h>
-#include <stdlib.h>
 #include <string.h>
 
 #include "common.hpp"
@@ -131,7 +130,7 @@ struct Args {
   unsigned flags;
   int n_rt, n1, n2, workers, max_rt, n_rt_cap, queue_len;
   int n_perm;  // P tasks per layer: n_rt, or 0 when S scatters the permutation itself
-  uint64_t timeout_ticks;
+  uint64_t timeout_ticks;  // watchdog: a wait without progress for this long gives up
   void* xq;        // [T][H] normalised input in storage precision
   void* hbuf;      // [T*k][F] SwiGLU output, rows in sorted order
   float* out_acc;  // [T][H] atomic-combine accumulator
@@ -240,8 +239,8 @@ ETC_DEV int owner_expert(const int* rt_base, int E, int idx, int mult) {
 // ------------------------------------------------------------------ R: routing tile
 //
 // One task routes a tile of BT tokens: RMSNorm, router logits, top-k with softmax, the
-// tile's per-expert ranks and histogram [P3 §5.5 Obstacle 1: the counts that set the
-// event targets come from here].
+// tile's per-expert ranks and histogram (the counts that set the event targets come from
+// here: tutorial chapter "5 · Event Tensor et le dynamisme", §5.5 Obstacle 1).
 //
 // Router precision.  logits[t][e] = rs_t * sum_h v[t][h] * W_r[e][h] (+ b[e]) with
 // v = x * gamma in float32 and rs_t = 1/sqrt(mean_h x[t][h]^2 + eps), which is
@@ -1035,7 +1034,7 @@ ETC_SMALL_TASK void finalize_task(KArgs& p, KLayer& L, int tau) {
 //
 // Static: the ticket's task (the one drawn during the previous task, if any); waits for
 // S of a layer before decoding past it.
-ETC_DEV bool claim_static(KArgs& p, Task& t, uint64_t deadline, Smem& sm) {
+ETC_DEV bool claim_static(KArgs& p, Task& t, Smem& sm) {
   const int ticket = sm.next_ticket >= 0 ? sm.next_ticket : static_ticket(p);
   sm.next_ticket = -1;
   int base = 0;
@@ -1051,7 +1050,7 @@ ETC_DEV bool claim_static(KArgs& p, Task& t, uint64_t deadline, Smem& sm) {
     if (off < p.n_perm) { t.kind = K_P; t.a = off; return true; }
     off -= p.n_perm;
     if (!(sm.scan_seen >> l & 1u)) {
-      if (!spin_until_geq(L.ev_scan, 1, p.sched, deadline, 10 + l)) return false;
+      if (!spin_until_geq(L.ev_scan, 1, p.sched, p.timeout_ticks, 10 + l)) return false;
       sm.scan_seen |= 1u << l;
     }
     // the layer's plan from the workgroup's LDS copy when it holds this layer
@@ -1083,8 +1082,9 @@ ETC_DEV bool claim_static(KArgs& p, Task& t, uint64_t deadline, Smem& sm) {
   return true;
 }
 
-// Dynamic: the next queue slot; slots below n_rt are the first layer's R tasks.
-ETC_DEV bool claim_dynamic(KArgs& p, Task& t, uint64_t deadline) {
+// Dynamic: the next queue slot; slots below n_rt are the first layer's R tasks.  The
+// watchdog counts progress as tasks being pushed anywhere (the queue tail moving).
+ETC_DEV bool claim_dynamic(KArgs& p, Task& t) {
   const int slot = ev_add_relaxed(p.sched + W_QHEAD, 1);
   if (slot < p.n_rt) {
     t.kind = K_R; t.layer = 0; t.a = slot;
@@ -1093,7 +1093,8 @@ ETC_DEV bool claim_dynamic(KArgs& p, Task& t, uint64_t deadline) {
   // every slot below the final queue total is filled exactly once; a workgroup that
   // drew a slot past the end of the array only waits for the total to be known
   const bool in_array = slot < p.queue_len;
-  for (int it = 1;; ++it) {
+  Watchdog wd;
+  for (int it = 0;; ++it) {
     if (in_array && q_load_relaxed(p.queue + slot) != 0) {
       const long long v = q_load(p.queue + slot);  // acquire: the task's inputs are ready
       q_store_relaxed(p.queue + slot, 0);           // the slot is clean for the next call
@@ -1107,34 +1108,37 @@ ETC_DEV bool claim_dynamic(KArgs& p, Task& t, uint64_t deadline) {
       t.kind = K_NONE;
       return true;
     }
-    if (wait_give_up(p.sched, deadline, it, 2)) return false;
+    if (it == 0) wd.start(p.timeout_ticks, ev_load_relaxed(p.sched + W_QTAIL));
+    else if (it % WATCH_EVERY == 0 &&
+             wd.expired(p.sched, p.timeout_ticks, ev_load_relaxed(p.sched + W_QTAIL), 2))
+      return false;
     __builtin_amdgcn_s_sleep(2);
   }
 }
 
 // Static mode: wait until the task's inputs are complete (thread 0).
-ETC_DEV bool wait_deps(KArgs& p, const Task& t, uint64_t deadline, Smem& sm) {
+ETC_DEV bool wait_deps(KArgs& p, const Task& t, Smem& sm) {
   KLayer& L = p.layer[t.layer];
   switch (t.kind) {
     case K_R:
       if (t.layer == 0) return true;
-      return spin_until_geq(p.layer[t.layer - 1].ev_done + t.a, 1, p.sched, deadline, 20);
+      return spin_until_geq(p.layer[t.layer - 1].ev_done + t.a, 1, p.sched, p.timeout_ticks, 20);
     case K_P:
-      return spin_until_geq(L.ev_scan, 1, p.sched, deadline, 24);
+      return spin_until_geq(L.ev_scan, 1, p.sched, p.timeout_ticks, 24);
     case K_GU:
       if (sm.perm_seen >> t.layer & 1u) return true;
-      if (!spin_until_geq(L.ev_perm, p.n_rt, p.sched, deadline, 25)) return false;
+      if (!spin_until_geq(L.ev_perm, p.n_rt, p.sched, p.timeout_ticks, 25)) return false;
       sm.perm_seen |= 1u << t.layer;
       return true;
     case K_D: {
       const int gpc = sm.lc.plan[PL_GPC];
       const int rt = sm.lc.rtb[t.a] + t.b;
       const int need = min(gpc, p.n1 - t.d * gpc);
-      return spin_until_geq(L.ev_gu + rt * p.n1 + t.d, need, p.sched, deadline, 22);
+      return spin_until_geq(L.ev_gu + rt * p.n1 + t.d, need, p.sched, p.timeout_ticks, 22);
     }
     case K_F: {
       const int target = tile_rows(p, t.a) * p.K * p.n2 * sm.lc.plan[PL_NS];
-      return spin_until_geq(L.ev_comb + t.a, target, p.sched, deadline, 23);
+      return spin_until_geq(L.ev_comb + t.a, target, p.sched, p.timeout_ticks, 23);
     }
     default:
       return true;
@@ -1353,7 +1357,6 @@ __global__ __launch_bounds__(MNT) void moe_kernel(Args pk) {
   }
   __syncthreads();
   KArgs& p = *(KArgs*)&p_lds;
-  const uint64_t deadline = now_ticks() + p.timeout_ticks;
 
   const bool tracing = (p.flags & ETC_FLAG_TRACE) != 0;
   uint64_t t_claim = 0, t_run = 0;
@@ -1372,13 +1375,13 @@ __global__ __launch_bounds__(MNT) void moe_kernel(Args pk) {
       if (tracing) t_claim = now_ticks();
       Task t;
       t.kind = K_NONE; t.layer = 0; t.a = t.b = t.c = t.d = 0;
-      const bool ok = (p.mode == ETC_SCHED_STATIC) ? claim_static(p, t, deadline, sm)
-                                                    : claim_dynamic(p, t, deadline);
+      const bool ok = (p.mode == ETC_SCHED_STATIC) ? claim_static(p, t, sm)
+                                                    : claim_dynamic(p, t);
       if (!ok) t.kind = K_NONE;
       const bool gemm_or_f = t.kind == K_GU || t.kind == K_D || t.kind == K_F;
       sm.need_cache = (gemm_or_f && sm.lc.layer != t.layer) ? 1 : 0;
       if (!sm.need_cache && t.kind != K_NONE && p.mode == ETC_SCHED_STATIC &&
-          !wait_deps(p, t, deadline, sm))
+          !wait_deps(p, t, sm))
         t.kind = K_NONE;
       sm.task = t;
       if (tracing) t_run = now_ticks();
@@ -1391,7 +1394,7 @@ __global__ __launch_bounds__(MNT) void moe_kernel(Args pk) {
       load_layer_cache(p, t.layer, sm);
       __syncthreads();
       if (tid == 0) {
-        if (p.mode == ETC_SCHED_STATIC && !wait_deps(p, sm.task, deadline, sm)) sm.task.kind = K_NONE;
+        if (p.mode == ETC_SCHED_STATIC && !wait_deps(p, sm.task, sm)) sm.task.kind = K_NONE;
         if (tracing) t_run = now_ticks();
       }
       __syncthreads();
@@ -1554,15 +1557,6 @@ ETC_API etc_status etc_moe_workspace_layout(int32_t max_tokens, int32_t hidden, 
 
 ETC_API int32_t etc_default_workers(int32_t kind, etc_dtype dtype);
 
-// The dynamic (ready-queue) scheduler of the MoE kernel is refused unless the process
-// sets ETC_ENABLE_DYNAMIC_SCHED=1: a run of it on MI355X did not terminate and the cause
-// is not identified yet (the same code completes and matches the oracle in the CPU
-// execution harness under every interleaving tried).  Static scheduling is unaffected.
-static bool dynamic_sched_enabled() {
-  const char* v = getenv("ETC_ENABLE_DYNAMIC_SCHED");
-  return v != nullptr && v[0] == '1';
-}
-
 ETC_API etc_status etc_moe_layer(int32_t T, int32_t H, int32_t E, int32_t K, int32_t F, int32_t nl,
                                  etc_dtype dtype, float eps, const etc_moe_weights* weights, const void* x,
                                  void* out, void* layer_out, const etc_moe_routing* routing, void* workspace,
@@ -1572,7 +1566,9 @@ ETC_API etc_status etc_moe_layer(int32_t T, int32_t H, int32_t E, int32_t K, int
   if (st != ETC_OK) return st;
   if (T < 0 || T > max_tokens || !(eps >= 0.f)) return ETC_ERR_INVALID_ARG;
   if (mode != ETC_SCHED_STATIC && mode != ETC_SCHED_DYNAMIC) return ETC_ERR_INVALID_ARG;
-  if (mode == ETC_SCHED_DYNAMIC && !dynamic_sched_enabled()) return ETC_ERR_UNSUPPORTED;
+  // The dynamic (ready-queue) scheduler runs only when the caller opts in: a run of it on
+  // MI355X did not terminate and its cause has not been identified.
+  if (mode == ETC_SCHED_DYNAMIC && !(flags & ETC_FLAG_ALLOW_DYNAMIC)) return ETC_ERR_UNSUPPORTED;
   if (combine != ETC_COMBINE_ATOMIC && combine != ETC_COMBINE_ORDERED) return ETC_ERR_INVALID_ARG;
   if (T == 0) return ETC_OK;  // nothing to compute; empty tensors may have null pointers
   if (!weights || !x || !out) return ETC_ERR_INVALID_ARG;
@@ -1613,7 +1609,7 @@ ETC_API etc_status etc_moe_layer(int32_t T, int32_t H, int32_t E, int32_t K, int
   p.max_rt = Y.max_rt;
   p.queue_len = Y.queue_len;
   p.n_rt_cap = Y.n_rt;
-  p.timeout_ticks = 500000000ull;  // 5 s of the 100 MHz real-time clock
+  p.timeout_ticks = 500000000ull;  // 5 s without progress, on the 100 MHz real-time clock
   int grid = host::grid_size(workers, host::device_cus(dev), moe_occupancy(dev, dtype));
   if (grid > moe::MAX_WORKERS) grid = moe::MAX_WORKERS;
   p.workers = grid;

@@ -186,7 +186,6 @@ ETC_DEV void reduce_task(const Args& p, int tile, int rc) {
 __global__ __launch_bounds__(NT) void splitk_kernel(Args p) {
   __shared__ Smem sm;
   const int tid = threadIdx.x;
-  const uint64_t deadline = now_ticks() + p.timeout_ticks;
   const int nparts = p.tiles * p.S;
   // static: the partials, then RCHUNKS reduction tickets per tile
   const int total = (p.mode == ETC_SCHED_STATIC) ? nparts + p.tiles * RCHUNKS : nparts;
@@ -220,7 +219,7 @@ __global__ __launch_bounds__(NT) void splitk_kernel(Args p) {
       __syncthreads();
     } else {
       const int tile = (t - nparts) / RCHUNKS, rc = (t - nparts) % RCHUNKS;
-      if (tid == 0) sm.flag = spin_until_geq(p.ev + tile, p.S, p.sched, deadline, 1) ? 1 : 0;
+      if (tid == 0) sm.flag = spin_until_geq(p.ev + tile, p.S, p.sched, p.timeout_ticks, 1) ? 1 : 0;
       __syncthreads();
       if (sm.flag) reduce_task(p, tile, rc);
       __syncthreads();
@@ -312,7 +311,7 @@ ETC_API etc_status etc_splitk_gemm(int32_t M, int32_t N, int32_t K, int32_t spli
   p.sched = reinterpret_cast<int*>(ws + L.sched);
   p.ev = reinterpret_cast<int*>(ws + L.ev);
   p.part = reinterpret_cast<float*>(ws + L.part);
-  p.timeout_ticks = 500000000ull;  // 5 s at the 100 MHz real-time clock
+  p.timeout_ticks = 500000000ull;  // 5 s without progress, on the 100 MHz real-time clock
 
   const int grid = host::grid_size(workers, host::device_cus(dev), splitk_occupancy(dev));
   hipLaunchKernelGGL(splitk::splitk_kernel, dim3(grid), dim3(NT), 0, static_cast<hipStream_t>(stream), p);

@@ -39,6 +39,8 @@ def moe(lib, cfg, x, layers, *, mode="dynamic", combine="atomic", workers=0, fla
     cnt = torch.zeros(L, E, dtype=torch.int32)
     sa = torch.zeros(L, T * k, dtype=torch.int32)
     r = binding.MoeRouting(idx.data_ptr(), gw.data_ptr(), cnt.data_ptr(), sa.data_ptr())
+    if mode == "dynamic":  # the harness runs the dynamic scheduler, which needs the opt-in
+        flags |= binding.FLAG_ALLOW_DYNAMIC
     st = lib.etc_moe_layer(T, H, E, k, F, L, DT[cfg.dtype], cfg.eps, warr, x.contiguous().data_ptr(),
                            out.data_ptr(), lay.data_ptr() if L > 1 else None, ctypes.byref(r), wptr,
                            nbytes, maxT, binding.MODES[mode], binding.COMBINES[combine], flags,

@@ -167,6 +167,7 @@ void run_workgroup(unsigned b, unsigned grid, unsigned block, const std::functio
 EmuDim emu_thread_idx() { return EmuDim{g_wg->f[g_wg->cur].tid, 0, 0}; }
 EmuDim emu_block_idx() { return EmuDim{g_wg->block, 0, 0}; }
 EmuDim emu_grid_dim() { return EmuDim{g_wg->grid, 1, 1}; }
+EmuDim emu_block_dim() { return EmuDim{(unsigned)g_wg->f.size(), 1, 1}; }
 int emu_lane() { return g_wg->f[g_wg->cur].tid % LANES; }
 
 void emu_syncthreads() {

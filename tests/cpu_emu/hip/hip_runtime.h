@@ -56,10 +56,11 @@ struct EmuDim { unsigned x, y, z; };
 EmuDim emu_thread_idx();
 EmuDim emu_block_idx();
 EmuDim emu_grid_dim();
+EmuDim emu_block_dim();
 #define threadIdx emu_thread_idx()
 #define blockIdx emu_block_idx()
 #define gridDim emu_grid_dim()
-#define blockDim (EmuDim{256, 1, 1})
+#define blockDim emu_block_dim()
 
 void emu_syncthreads();
 void emu_wave_barrier();

@@ -33,7 +33,7 @@ def run_moe(x_dev, layers_dev, k, *, mode, combine="atomic", workspace=None, eps
                                   workspace=workspace, return_routing=True,
                                   return_layer_outputs=True, workers=workers, flags=flags)
     torch.cuda.synchronize()
-    if workspace is not None:
+    if workspace is not None:  # (without one, the binding checked the status itself)
         st = workspace.status()
         assert st == 0, f"device status {st}"
     outs = [info["layer_outputs"][l] for l in range(L - 1)] + [out]

@@ -121,11 +121,13 @@ def test_moe_argument_errors_before_any_hip_call(lib):
     assert _call_moe(lib, wsb=1024) == WS
 
 
-def test_dynamic_moe_refused_by_default(lib, monkeypatch):
-    """The dynamic MoE scheduler is off unless ETC_ENABLE_DYNAMIC_SCHED=1 (host check,
-    before any HIP call)."""
-    monkeypatch.delenv("ETC_ENABLE_DYNAMIC_SCHED", raising=False)
+def test_dynamic_moe_refused_without_the_flag(lib):
+    """The dynamic MoE scheduler is refused unless the call sets ETC_FLAG_ALLOW_DYNAMIC
+    (host check, before any HIP call); the library reads no environment variables."""
     assert _call_moe(lib, mode=1) == 2
+    import subprocess
+    strings = subprocess.run(["strings", binding.library_path()], capture_output=True, text=True).stdout
+    assert "getenv" not in strings and "ETC_ENABLE" not in strings
 
 
 def test_splitk_argument_errors_before_any_hip_call(lib):

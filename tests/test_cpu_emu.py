@@ -29,11 +29,6 @@ def lib():
     return binding.open_library(path)
 
 
-@pytest.fixture(autouse=True)
-def _dynamic_on(monkeypatch):
-    monkeypatch.setenv("ETC_ENABLE_DYNAMIC_SCHED", "1")
-
-
 def _check(cfg, x, layers, g):
     assert g["status"] == 0
     return moe_check.compare(synth.as_numpy(x), synth.layers_as_numpy(layers), cfg.top_k, cfg.eps,
@@ -228,6 +223,35 @@ def test_trace_respects_every_dependency(lib, mode):
     bad[i, 2] &= np.uint64(0xFFFFFFFF)  # no claim or wait ticks
     with pytest.raises(AssertionError, match="began"):
         moe_check.check_trace_causality(bad, *args)
+
+
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
+def test_watchdog_ends_a_call_with_a_dropped_signal(lib, mode):
+    """A counter that can never reach its target (planted in the workspace, on the CPU):
+    the wait on it gives up after its patience (5 s without progress), the call reports
+    ETC_ERR_TIMEOUT through the status word, and every workgroup leaves -- the call
+    returns.  A cleared workspace then serves the same call correctly.  Own process, with
+    the harness clock in real time."""
+    import json
+    import subprocess
+    import sys
+
+    env = dict(os.environ, ETC_EMU_CLOCK_DIV="1")
+    path = os.path.join(HERE, "cpu_emu", "libetc_moe_emu.so")
+    script = os.path.join(HERE, "cpu_emu", "watchdog_case.py")
+    res = subprocess.run([sys.executable, script, path, mode], env=env, capture_output=True,
+                         text=True, timeout=240)
+    assert res.returncode == 0, res.stderr[-2000:]
+    r = json.loads(res.stdout.strip().splitlines()[-1])
+    assert r["status"] == 5, r  # ETC_ERR_TIMEOUT
+    # static: the finalize task's wait on ev_comb (site 23); dynamic: a queue-slot wait (2)
+    assert r["where"] == (23 if mode == "static" else 2), r
+    assert 4.0 < r["seconds"] < 120, r
+    assert r["status_after_init"] == 0
+    cfg = synth.CONFIGS["tiny"]
+    layers, x = synth.make_layers(cfg), synth.make_x(cfg, 16)
+    ref = driver.moe(lib, cfg, x, layers, mode=mode)["outs"][-1]
+    assert np.array_equal(np.asarray(r["out_after_init"]), ref)
 
 
 def lib_layout(lib, T, cfg, l):

@@ -33,9 +33,8 @@ def _setup(cfg, T, call=0):
     return x, layers, layers_to_device(layers), synth.layers_as_numpy(layers)
 
 
-def _compare(cfg, x, layers_np, gpu, tokens=None):
-    return moe_check.compare(synth.as_numpy(x), layers_np, cfg.top_k, cfg.eps, cfg.dtype, gpu,
-                             tokens)
+def _compare(cfg, x, layers_np, gpu):
+    return moe_check.compare(synth.as_numpy(x), layers_np, cfg.top_k, cfg.eps, cfg.dtype, gpu)
 
 
 MID = synth.MoEConfig("mid", (300,), 512, 16, 6, 384, layers=2, zipf_s=0.5)
@@ -266,16 +265,15 @@ def test_finegrained_zipf():
     assert counts[0] == counts.max() and (counts > 0).sum() < cfg.experts  # skewed
 
 
-def test_prefill_two_layers_sampled():
-    """Full prefill shape (T=4096, H=4096, E=64, k=6, F=1408, two layers): routing of
-    every first-layer token, grouping of both layers, and outputs of 40 sampled tokens
-    through both layers."""
+@pytest.mark.timeout(300)
+def test_prefill_two_layers():
+    """Full prefill shape (T=4096, H=4096, E=64, k=6, F=1408, two layers): routing,
+    gates, counts, permutation and outputs of every token in both layers, each layer on
+    the GPU's own input, plus the end-to-end chain."""
     cfg = synth.CONFIGS["prefill"]
     say("prefill: drawing inputs")
     x, layers, ld, lnp = _setup(cfg, 4096)
-    rng = np.random.default_rng(0)
-    sample = sorted(set(rng.choice(4096, 38, replace=False).tolist()) | {0, 4095})
     for mode in STATIC_ONLY:
         say(f"prefill mode={mode}")
         gpu = run_moe(x.cuda(), ld, cfg.top_k, mode=mode)
-        say(_compare(cfg, x, lnp, gpu, tokens=sample))
+        say(_compare(cfg, x, lnp, gpu))
