@@ -1,4 +1,5 @@
-"""CPU oracle for the event-tensor MoE layer and the split-K GEMM.
+"""CPU oracle for the event-tensor MoE layer, the split-K GEMM and split-KV decode
+attention.
 
 TEST INFRASTRUCTURE, NOT PRODUCT CODE.  Only ``tests/``, ``__graft_entry__.smoke()``
 and the ``cpu_baseline`` leg of ``bench.py`` may import anything from this package.
@@ -19,9 +20,10 @@ Sources.  The pages this follows are
     event counters computed from router outputs, and static versus dynamic scheduling;
   * the OpenAlex record of "Event Tensor: A Unified Abstraction for Compiling Dynamic
     Megakernel" (abstract: event tensors encode dependencies between tiled tasks);
-  * the tutorial chapter "5 · Event Tensor et le dynamisme", §5.3 (parameterised
-    dependency structure, one compilation) and §5.5 (counter targets computed at run
-    time on the GPU before waiting; online load balancing with atomics).
+  * the tutorial chapter "5 · Event Tensor et le dynamisme", §5.1 (variable context
+    length as a source of shape dynamism), §5.3 (parameterised dependency structure,
+    one compilation) and §5.5 (counter targets computed at run time on the GPU before
+    waiting; online load balancing with atomics).
 The pages give no formula for RMSNorm, the router, top-k, SwiGLU or the combine.
 Each function states the plain reading it takes ("reading: ...").
 
@@ -30,4 +32,4 @@ closed forms, hand-worked cases (``tests/golden/``), invariants, library routine
 and brute force.  No function is "parity unpinned".
 """
 
-from . import numerics, moe, splitk, sched_model  # noqa: F401
+from . import numerics, moe, splitk, sched_model, attention  # noqa: F401
