@@ -205,13 +205,71 @@ etc_status etc_splitk_gemm(int32_t M, int32_t N, int32_t K, int32_t split_k, con
 
 size_t etc_splitk_workspace_size(int32_t M, int32_t N, int32_t split_k);
 
+/*
+ * etc_decode_attention -- decode attention (one query token per request) over key/value
+ * caches of per-request length, in one persistent kernel.
+ *
+ * For request b with context length L_b, KV head g and query head h = g*group + i:
+ * s_t = scale * q[b,h] . K[kv_start[b] + t, g] for t < L_b, out[b,h] = softmax(s) V.  The
+ * cache of each request is cut into chunks of 256 tokens; every (request, KV head,
+ * chunk) task writes a partial (largest score, sum of exp(s - max), exp-weighted value
+ * sum) and adds 1 to the (request, KV head) counter; the head's output is merged once
+ * the counter reaches ceil(L_b / 256), a target the kernel computes from the device array
+ * of lengths before anyone waits (tutorial chapter "5 · Event Tensor et le dynamisme",
+ * §5.1: context length as a source of shape dynamism; §5.5 Obstacle 1: targets computed
+ * at run time on the GPU; podcast episode page "Prompt Boundary-Aware Scheduling with
+ * Event Tensors for Dynamic Kernels", summary: the split-K summation example).  One
+ * compiled kernel serves any mix of lengths.
+ *
+ *   batch        requests B, 1 <= B <= max_batch
+ *   kv_heads     H_kv >= 1
+ *   group        query heads per KV head, 1..8 (1: multi-head attention)
+ *   head_dim     must be 128
+ *   context_lens device int32 [B]: L_b >= 1
+ *   kv_start     device int32 [B]: cache row of request b's first token; rows
+ *                kv_start[b] .. kv_start[b] + L_b - 1 must lie in [0, kv_rows)
+ *   kv_rows      rows of each cache
+ *   scale        score scale (typically 1/sqrt(head_dim))
+ *   q            device bfloat16 [B][H_kv*group][128]
+ *   k_cache, v_cache  device bfloat16 [kv_rows][H_kv][128]
+ *   out          device float32 [B][H_kv*group][128]
+ *   workspace    device, 256-byte aligned, >= etc_decode_attention_workspace_size(
+ *                max_batch, kv_heads, group, head_dim, max_total_tokens)
+ *   max_batch, max_total_tokens  the capacity the workspace was sized for: at most
+ *                max_batch requests whose lengths sum to at most max_total_tokens
+ *   mode         static: partial tickets, then one merge ticket per (request, KV head)
+ *                that waits on its counter; dynamic: the partial whose signal completes
+ *                the counter merges (last arriver)
+ *   flags, workers, stream  as for etc_moe_layer (ETC_FLAG_KEEP_COUNTERS applies)
+ * Errors: ETC_ERR_INVALID_ARG (null or misaligned pointer -- q, the caches and out must
+ * be 16-byte aligned, the int32 arrays 4-byte aligned --, batch out of range, kv_rows < 1,
+ * NaN scale, bad enum), ETC_ERR_UNSUPPORTED (head_dim != 128, group > 8, max_batch >
+ * 2048), ETC_ERR_WORKSPACE, ETC_ERR_HIP, ETC_ERR_NO_DEVICE.  The lengths and start rows
+ * are device data: a length below 1 or rows outside the cache make the kernel skip all
+ * work and leave ETC_ERR_INVALID_ARG in the device status, and lengths summing to more
+ * than max_total_tokens leave ETC_ERR_WORKSPACE (etc_query_device_status); out is then
+ * not written.
+ */
+etc_status etc_decode_attention(int32_t batch, int32_t kv_heads, int32_t group, int32_t head_dim,
+                                const int32_t* context_lens, const int32_t* kv_start,
+                                int32_t kv_rows, float scale, const void* q, const void* k_cache,
+                                const void* v_cache, float* out, void* workspace,
+                                size_t workspace_bytes, int32_t max_batch, int64_t max_total_tokens,
+                                etc_sched_mode mode, uint32_t flags, int32_t workers, void* stream);
+
+/* Bytes of workspace etc_decode_attention needs (0 on invalid arguments). */
+size_t etc_decode_attention_workspace_size(int32_t max_batch, int32_t kv_heads, int32_t group,
+                                           int32_t head_dim, int64_t max_total_tokens);
+
 /* Clear a freshly allocated workspace (enqueues a memset of all workspace_bytes on
  * `stream`).  Needed once after allocation, and after a call that failed with a
  * device timeout or used ETC_FLAG_KEEP_COUNTERS. */
 etc_status etc_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /* Synchronises `stream`, then returns the device status left in the workspace by the
- * last call: ETC_OK or ETC_ERR_TIMEOUT.  ETC_ERR_HIP if the copy fails. */
+ * last call: ETC_OK, ETC_ERR_TIMEOUT, or (etc_decode_attention) ETC_ERR_INVALID_ARG or
+ * ETC_ERR_WORKSPACE for device-side lengths out of range.  ETC_ERR_HIP if the copy
+ * fails.  The status word persists until etc_workspace_init. */
 etc_status etc_query_device_status(const void* workspace, void* stream);
 
 /* Human-readable name of a status code (static storage). */

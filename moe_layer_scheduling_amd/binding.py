@@ -88,6 +88,12 @@ def open_library(path):
     lib.etc_workspace_init.argtypes = [c_p, c_sz, c_p]
     lib.etc_query_device_status.restype = ctypes.c_int
     lib.etc_query_device_status.argtypes = [c_p, c_p]
+    lib.etc_decode_attention.restype = ctypes.c_int
+    lib.etc_decode_attention.argtypes = [c_i32] * 4 + [c_p, c_p, c_i32, ctypes.c_float, c_p, c_p, c_p,
+                                                       c_p, c_p, c_sz, c_i32, ctypes.c_int64,
+                                                       ctypes.c_int, c_u32, c_i32, c_p]
+    lib.etc_decode_attention_workspace_size.restype = c_sz
+    lib.etc_decode_attention_workspace_size.argtypes = [c_i32] * 4 + [ctypes.c_int64]
     lib.etc_default_workers.restype = c_i32
     lib.etc_default_workers.argtypes = [c_i32, ctypes.c_int]
     if lib.etc_abi_version() != ABI_VERSION:
@@ -280,6 +286,56 @@ def splitk_gemm(A, B, split_k=8, *, mode="static", workspace=None, workers=0, fl
     if own or check:
         _check(workspace.status(), "etc_splitk_gemm (device)")
     return C
+
+
+class AttnWorkspace(Workspace):
+    """Workspace of etc_decode_attention for up to max_batch requests whose context
+    lengths sum to at most max_total_tokens."""
+
+    def __init__(self, max_batch, kv_heads, group, max_total_tokens, head_dim=128, device=None):
+        n = load_library().etc_decode_attention_workspace_size(max_batch, kv_heads, group, head_dim,
+                                                               int(max_total_tokens))
+        if n == 0:
+            raise EtcError(2, "etc_decode_attention_workspace_size")
+        self.shape = (int(max_batch), kv_heads, group, head_dim, int(max_total_tokens))
+        super().__init__(n, device)
+
+
+def decode_attention(q, k_cache, v_cache, context_lens, kv_start, *, scale=None, mode="static",
+                     workspace=None, max_total_tokens=None, workers=0, flags=0, check=False):
+    """out[b, h] = softmax(scale * q[b,h] K_b^T) V_b for one query token per request.
+
+    q [B][H_kv*G][128] bfloat16; k_cache, v_cache [rows][H_kv][128] bfloat16; context_lens
+    and kv_start device int32 [B] (request b's tokens are cache rows kv_start[b] ..
+    kv_start[b] + L_b - 1).  Returns out [B][H_kv*G][128] float32.  Device-side errors
+    (lengths out of range, too little workspace, timeouts) are raised as for moe_layer
+    when the binding owns the workspace or check is True.
+    """
+    lib = load_library()
+    B, HQ, D = q.shape
+    rows, HKV, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != (rows, HKV, D) or HQ % HKV:
+        raise ValueError("q, k_cache and v_cache shapes disagree")
+    G = HQ // HKV
+    if scale is None:
+        scale = 1.0 / float(D) ** 0.5
+    own = workspace is None
+    if own:
+        workspace = AttnWorkspace(B, HKV, G, max_total_tokens or rows, D, device=q.device)
+    mb, whkv, wg, wd, mt = workspace.shape
+    if (whkv, wg, wd) != (HKV, G, D) or B > mb:
+        raise ValueError("workspace was sized for another shape")
+    out = torch.empty(B, HQ, D, dtype=torch.float32, device=q.device)
+    st = lib.etc_decode_attention(B, HKV, G, D, _dev_ptr(context_lens, "context_lens", torch.int32),
+                                  _dev_ptr(kv_start, "kv_start", torch.int32), rows, float(scale),
+                                  _dev_ptr(q, "q", torch.bfloat16), _dev_ptr(k_cache, "k_cache", torch.bfloat16),
+                                  _dev_ptr(v_cache, "v_cache", torch.bfloat16), out.data_ptr(),
+                                  workspace.ptr, workspace.nbytes, mb, mt, MODES[mode], int(flags),
+                                  int(workers), _stream())
+    _check(st, "etc_decode_attention")
+    if own or check:
+        _check(workspace.status(), "etc_decode_attention (device)")
+    return out
 
 
 def default_workers(kind="moe", dtype=torch.bfloat16):

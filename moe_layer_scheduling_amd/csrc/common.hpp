@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 #define ETC_DEV __device__ __forceinline__
 #define ETC_INLINE __attribute__((always_inline))  // for lambdas
 
@@ -353,5 +355,16 @@ ETC_DEV float wave_sum(float v) {
 }
 
 __host__ __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled: register arrays indexed
+// inside stay indexed by compile-time constants
+template <typename F, int... I>
+ETC_DEV void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+ETC_DEV void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 }  // namespace etc

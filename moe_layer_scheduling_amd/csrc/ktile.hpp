@@ -39,21 +39,10 @@
 // so every index is a compile-time constant.
 #pragma once
 
-#include <utility>
-
 #include "common.hpp"
 #include "mfma.hpp"
 
 namespace etc {
-
-template <typename F, int... I>
-ETC_DEV void static_for_impl(F& f, std::integer_sequence<int, I...>) {
-  (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-ETC_DEV void static_for(F&& f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 template <typename TE, int NTH = NT>
 struct KTile {

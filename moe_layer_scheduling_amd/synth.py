@@ -138,3 +138,36 @@ def as_numpy(t):
 
 def layers_as_numpy(layers):
     return [{k: as_numpy(v) for k, v in layer.items()} for layer in layers]
+
+
+# ------------------------------------------------------------------ decode attention
+
+# The decode-attention workload: a batch of 32 requests, 32 query heads sharing 8 KV
+# heads (4 per KV head), head dimension 128, bfloat16 caches; context lengths per request
+# drawn log-uniformly from [64, 32768] (the pages name no model or trace; the mix of
+# short and long contexts stands in for a serving batch).  q, K and V ~ N(0, 1).
+ATTN = dict(batch=32, kv_heads=8, group=4, head_dim=128, min_len=64, max_len=32768, seed=0)
+
+
+def draw_context_lens(batch, lo, hi, seed=0):
+    """Per-request context lengths, log-uniform in [lo, hi] (int32 CPU tensor)."""
+    gen = torch.Generator().manual_seed(7_919 * seed + 29)
+    u = torch.rand(batch, generator=gen, dtype=torch.float64)
+    lens = torch.exp(math.log(lo) + u * (math.log(hi) - math.log(lo))).round().to(torch.int64)
+    return lens.clamp(lo, hi).to(torch.int32)
+
+
+def make_attention(lens, kv_heads, group, head_dim=128, seed=0):
+    """(q, k_cache, v_cache, kv_start) for requests of the given context lengths: the
+    caches hold the requests' rows one after another (kv_start = exclusive scan of the
+    lengths), [rows][kv_heads][head_dim]; q is [B][kv_heads*group][head_dim]; all
+    bfloat16 CPU tensors ~N(0, 1) (kv_start int32)."""
+    lens = torch.as_tensor(lens, dtype=torch.int64)
+    B = lens.numel()
+    rows = int(lens.sum())
+    gen = torch.Generator().manual_seed(104_729 * seed + 31)
+    q = _normal(gen, (B, kv_heads * group, head_dim), 1.0, torch.bfloat16)
+    k = _normal(gen, (rows, kv_heads, head_dim), 1.0, torch.bfloat16)
+    v = _normal(gen, (rows, kv_heads, head_dim), 1.0, torch.bfloat16)
+    start = torch.cumsum(lens, 0) - lens
+    return q, k, v, start.to(torch.int32)

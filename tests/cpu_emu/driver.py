@@ -51,3 +51,27 @@ def moe(lib, cfg, x, layers, *, mode="dynamic", combine="atomic", workers=0, fla
     return {"idx": idx.numpy().astype(np.int64), "w": gw.numpy().astype(np.float64),
             "counts": cnt.numpy().astype(np.int64), "sa": sa.numpy().astype(np.int64),
             "outs": [synth.as_numpy(o) for o in outs], "status": status, "ws": ws, "wptr": wptr}
+
+
+def attention(lib, q, k, v, lens, kv_start, *, scale, mode="static", max_total=None, max_batch=None,
+              workers=0, flags=0):
+    """etc_decode_attention on host tensors.  Returns (out float64 array, status)."""
+    B, HQ, D = q.shape
+    rows, HKV, _ = k.shape
+    G = HQ // HKV
+    mb = max_batch or B
+    mt = max_total or max(rows, 1)
+    n = lib.etc_decode_attention_workspace_size(mb, HKV, G, D, mt)
+    assert n > 0
+    ws = torch.zeros(n + 256, dtype=torch.uint8)
+    wptr = ws.data_ptr() + (-ws.data_ptr()) % 256
+    out = torch.zeros(B, HQ, D, dtype=torch.float32)
+    lens = torch.as_tensor(lens, dtype=torch.int32).contiguous()
+    kv_start = torch.as_tensor(kv_start, dtype=torch.int32).contiguous()
+    st = lib.etc_decode_attention(B, HKV, G, D, lens.data_ptr(), kv_start.data_ptr(), rows, scale,
+                                  q.contiguous().data_ptr(), k.contiguous().data_ptr(),
+                                  v.contiguous().data_ptr(), out.data_ptr(), wptr, n, mb, mt,
+                                  binding.MODES[mode], flags, workers, None)
+    assert st == 0, st
+    status = ctypes.c_int32.from_address(wptr + 7 * 4).value
+    return out.numpy().astype(np.float64), status

@@ -69,6 +69,7 @@ struct Workgroup {
   unsigned block = 0, grid = 0;
   const std::function<void()>* fn = nullptr;
   unsigned spins = 0;
+  int or_flag = 0;
 };
 
 thread_local Workgroup* g_wg = nullptr;
@@ -181,6 +182,19 @@ void emu_syncthreads() {
     to_sched(w, me);
   }
   TSAN_ACQUIRE(&w.block_sync);
+}
+
+// OR of v over the workgroup, returned to every thread (a flag in the workgroup,
+// cleared by the last thread through a second barrier)
+int emu_syncthreads_or(int v) {
+  Workgroup& w = *g_wg;
+  emu_syncthreads();
+  if (v) w.or_flag = 1;
+  emu_syncthreads();
+  const int r = w.or_flag;
+  emu_syncthreads();
+  w.or_flag = 0;
+  return r;
 }
 
 void emu_wave_barrier() {

@@ -69,6 +69,9 @@ void* emu_wave_scratch(int bytes_per_lane);  // this wave's exchange buffer (64 
 int emu_lane();
 uint64_t emu_realtime();
 #define __syncthreads() emu_syncthreads()
+int emu_syncthreads_or(int v);
+#define __syncthreads_or(v) emu_syncthreads_or(v)
+#define __expf(x) expf(x)
 
 template <typename T>
 inline T emu_exchange(T v, int src) {

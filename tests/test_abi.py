@@ -152,3 +152,39 @@ def test_no_cpu_fallback_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(binding, "_lib", None)
     with pytest.raises(binding.EtcLibraryError):
         binding.load_library(str(tmp_path / "missing.so"))
+
+
+def test_decode_attention_arguments_before_any_hip_call(lib):
+    """Host-side validation of etc_decode_attention: sizes, pointers, alignment and the
+    workspace, all before any HIP call (no GPU needed)."""
+    f = lib.etc_decode_attention
+    ws_n = lib.etc_decode_attention_workspace_size(32, 8, 4, 128, 200000)
+    assert ws_n > 0
+    assert lib.etc_decode_attention_workspace_size(32, 8, 4, 64, 200000) == 0  # head_dim != 128
+    assert lib.etc_decode_attention_workspace_size(32, 8, 9, 128, 200000) == 0  # group > 8
+    assert lib.etc_decode_attention_workspace_size(4096, 8, 4, 128, 200000) == 0  # batch > 2048
+    assert lib.etc_decode_attention_workspace_size(0, 8, 4, 128, 200000) == 0
+    # more tokens need more partial records
+    assert lib.etc_decode_attention_workspace_size(32, 8, 4, 128, 400000) > ws_n
+    ok = dict(B=32, HKV=8, G=4, D=128, lens=1 << 20, start=2 << 20, rows=200000, scale=0.088,
+              q=3 << 20, k=4 << 20, v=5 << 20, out=6 << 20, ws=1 << 30, wsb=ws_n, mb=32, mt=200000,
+              mode=0, flags=0, workers=0)
+
+    def call(**over):
+        a = dict(ok, **over)
+        return f(a["B"], a["HKV"], a["G"], a["D"], a["lens"], a["start"], a["rows"], a["scale"],
+                 a["q"], a["k"], a["v"], a["out"], a["ws"], a["wsb"], a["mb"], a["mt"], a["mode"],
+                 a["flags"], a["workers"], None)
+
+    assert call(B=0) == 1
+    assert call(B=33) == 1  # more requests than the workspace holds
+    assert call(D=64) == 2
+    assert call(G=9) == 2
+    assert call(lens=None) == 1
+    assert call(lens=(1 << 20) + 2) == 1  # int32 array misaligned
+    assert call(q=(3 << 20) + 8) == 1
+    assert call(rows=0) == 1
+    assert call(scale=float("nan")) == 1
+    assert call(mode=3) == 1
+    assert call(ws=None) == 3
+    assert call(wsb=ws_n - 1) == 3

@@ -259,3 +259,51 @@ def lib_layout(lib, T, cfg, l):
     assert lib.etc_moe_workspace_layout(T, cfg.hidden, cfg.experts, cfg.top_k, cfg.ffn,
                                         cfg.layers, 1, 0, l, out) == 0
     return list(out)
+
+
+# ------------------------------------------------------------------ decode attention
+
+
+def _attn_case(lens, HKV=2, G=4, seed=3):
+    from oracle import attention as oa
+
+    q, k, v, start = synth.make_attention(lens, HKV, G, seed=seed)
+    scale = 1.0 / np.sqrt(128.0)
+    ref = oa.decode_attention(synth.as_numpy(q), synth.as_numpy(k), synth.as_numpy(v),
+                              start.numpy(), np.asarray(lens), G, scale)
+    return q, k, v, start, scale, ref
+
+
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
+def test_decode_attention_ragged_lengths(lib, mode):
+    """Context lengths of 1, 255, 256, 257 and 600 tokens (one chunk, a chunk +-1, three
+    chunks) in one call, against the oracle's plain definition."""
+    lens = [1, 255, 256, 257, 600]
+    q, k, v, start, scale, ref = _attn_case(lens)
+    out, st = driver.attention(lib, q, k, v, lens, start, scale=scale, mode=mode)
+    assert st == 0
+    err = float(np.max(np.abs(out - ref)))
+    assert err <= 1e-3 * float(np.max(np.abs(ref))), err
+
+
+@pytest.mark.parametrize("G", [1, 3, 8])
+def test_decode_attention_group_sizes(lib, G):
+    lens = [130, 40]
+    q, k, v, start, scale, ref = _attn_case(lens, HKV=3, G=G, seed=G)
+    out, st = driver.attention(lib, q, k, v, lens, start, scale=scale, mode="dynamic")
+    assert st == 0
+    assert float(np.max(np.abs(out - ref))) <= 1e-3 * float(np.max(np.abs(ref)))
+
+
+def test_decode_attention_device_checks(lib):
+    """Lengths are device data: a zero length, rows past the cache, and lengths beyond
+    the workspace's token capacity are reported through the status word, and nothing is
+    written."""
+    lens = [40, 60]
+    q, k, v, start, scale, ref = _attn_case(lens)
+    out, st = driver.attention(lib, q, k, v, [40, 0], start, scale=scale)
+    assert st == 1 and not out.any()
+    out, st = driver.attention(lib, q, k, v, [40, 61], start, scale=scale)
+    assert st == 1 and not out.any()
+    out, st = driver.attention(lib, q, k, v, lens, start, scale=scale, max_total=20)
+    assert st == 3 and not out.any()
