@@ -203,6 +203,37 @@ def bench_splitk(steps, warmup, mode="static", copies=4):
             "mode": mode}
 
 
+def bench_attention(steps, warmup, mode, lens, label):
+    """Variable-context decode attention on one call's worth of synthetic cache: batch,
+    heads and lengths from synth.ATTN (or the given lengths).  Algorithmic bytes: every
+    request's K and V rows once (L_b * H_kv * 128 * 2 bytes each), q in, out (float32)."""
+    cfg = synth.ATTN
+    HKV, G, D = cfg["kv_heads"], cfg["group"], cfg["head_dim"]
+    lens = torch.as_tensor(lens, dtype=torch.int32)
+    B = lens.numel()
+    q, k, v, start = synth.make_attention(lens, HKV, G, head_dim=D, seed=cfg["seed"])
+    qd, kd, vd, sd, ld = q.cuda(), k.cuda(), v.cuda(), start.cuda(), lens.cuda()
+    ws = binding.AttnWorkspace(B, HKV, G, int(lens.sum()), D)
+    out = torch.empty(0)
+
+    def step():
+        nonlocal out
+        out = binding.decode_attention(qd, kd, vd, ld, sd, mode=mode, workspace=ws)
+
+    log(f"[bench] attention {label}: timing {steps} steps")
+    ms, launch_ms, _ = time_steps(step, steps, warmup)
+    st = ws.status()
+    if st != 0:
+        raise RuntimeError(f"device status {st}")
+    total = int(lens.sum())
+    nbytes = total * HKV * D * 2 * 2 + B * HKV * G * D * 2 + B * HKV * G * D * 4
+    del qd, kd, vd, ws
+    torch.cuda.empty_cache()
+    return {"requests": B, "tokens": total, "launch_ms": launch_ms, "gbs_alg": nbytes / (launch_ms / 1e3) / 1e9,
+            "hbm_frac": nbytes / (launch_ms / 1e3) / 1e9 / PEAK_HBM_GBS, "bytes_alg": nbytes,
+            "requests_per_s": B / (ms / 1e3), "mode": mode}
+
+
 def source_hash():
     """sha256 over the HIP sources of the library (names and contents, sorted): the
     identity of the kernels that counter measurements belong to."""
@@ -248,6 +279,20 @@ def copy_calibration(nbytes=1 << 30, reps=3):
             "launch_ms": launch_ms, "gbs": 2 * nbytes / (launch_ms / 1e3) / 1e9}
 
 
+def attention_lines(steps):
+    """Decode-attention lines: the serving batch (mixed lengths, both schedulers) and
+    batches of one fixed length, all through the one compiled kernel."""
+    cfg = synth.ATTN
+    mixed = synth.draw_context_lens(cfg["batch"], cfg["min_len"], cfg["max_len"], cfg["seed"])
+    lines = {}
+    for m in ("static", "dynamic"):
+        lines[f"attention_mixed_{m}"] = bench_attention(steps, 2, m, mixed, f"mixed {m}")
+    for L in (1024, 8192, 32768):
+        lines[f"attention_L{L}"] = bench_attention(steps, 2, "dynamic", [L] * cfg["batch"], f"L={L}")
+    keep = ("requests", "tokens", "launch_ms", "gbs_alg", "hbm_frac")
+    return {k: {f: v[f] for f in keep} for k, v in lines.items()}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,6 +311,8 @@ def main():
                     help="only run a plain 1 GiB elementwise copy (counter calibration)")
     ap.add_argument("--splitk-only", action="store_true",
                     help="only time the split-K GEMM (for per-kernel profiles)")
+    ap.add_argument("--attention-only", action="store_true",
+                    help="only time the decode-attention lines (for per-kernel profiles)")
     ap.add_argument("--splitk-copies", type=int, default=4,
                     help="copies of B rotated between split-K calls (4: B streams from HBM)")
     ap.add_argument("--source-hash", action="store_true",
@@ -286,6 +333,9 @@ def main():
         print(json.dumps(copy_calibration()), flush=True)
         return
     binding.load_library()
+    if args.attention_only:
+        print(json.dumps({"attention": attention_lines(args.steps)}), flush=True)
+        return
     if args.splitk_only:
         res = {m: bench_splitk(args.steps, args.warmup, m, args.splitk_copies) for m in ("static", "dynamic")}
         print(json.dumps({"splitk": res}), flush=True)
@@ -321,6 +371,7 @@ def main():
         for m in ("static", "dynamic"):  # split-K's dynamic mode is a last-arriver reduction
             sk = bench_splitk(max(5, args.steps // 2), 2, m)
             secondary[f"splitk_{m}"] = {k: sk[k] for k in ("launch_ms", "gbs_alg", "hbm_frac")}
+        secondary.update(attention_lines(max(5, args.steps // 2)))
 
     line = {
         "metric": METRIC,

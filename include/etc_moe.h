@@ -210,7 +210,7 @@ size_t etc_splitk_workspace_size(int32_t M, int32_t N, int32_t split_k);
  * caches of per-request length, in one persistent kernel.
  *
  * For request b with context length L_b, KV head g and query head h = g*group + i:
- * s_t = scale * q[b,h] . K[kv_start[b] + t, g] for t < L_b, out[b,h] = softmax(s) V.  The
+ * s_t = scale * q[b,h] . K[g][kv_start[b] + t] for t < L_b, out[b,h] = softmax(s) V.  The
  * cache of each request is cut into chunks of 256 tokens; every (request, KV head,
  * chunk) task writes a partial (largest score, sum of exp(s - max), exp-weighted value
  * sum) and adds 1 to the (request, KV head) counter; the head's output is merged once
@@ -231,7 +231,8 @@ size_t etc_splitk_workspace_size(int32_t M, int32_t N, int32_t split_k);
  *   kv_rows      rows of each cache
  *   scale        score scale (typically 1/sqrt(head_dim))
  *   q            device bfloat16 [B][H_kv*group][128]
- *   k_cache, v_cache  device bfloat16 [kv_rows][H_kv][128]
+ *   k_cache, v_cache  device bfloat16 [H_kv][kv_rows][128] (head-major: the rows of one
+ *                KV head are contiguous, so a chunk of one request is one contiguous run)
  *   out          device float32 [B][H_kv*group][128]
  *   workspace    device, 256-byte aligned, >= etc_decode_attention_workspace_size(
  *                max_batch, kv_heads, group, head_dim, max_total_tokens)

@@ -305,7 +305,7 @@ def decode_attention(q, k_cache, v_cache, context_lens, kv_start, *, scale=None,
                      workspace=None, max_total_tokens=None, workers=0, flags=0, check=False):
     """out[b, h] = softmax(scale * q[b,h] K_b^T) V_b for one query token per request.
 
-    q [B][H_kv*G][128] bfloat16; k_cache, v_cache [rows][H_kv][128] bfloat16; context_lens
+    q [B][H_kv*G][128] bfloat16; k_cache, v_cache [H_kv][rows][128] bfloat16; context_lens
     and kv_start device int32 [B] (request b's tokens are cache rows kv_start[b] ..
     kv_start[b] + L_b - 1).  Returns out [B][H_kv*G][128] float32.  Device-side errors
     (lengths out of range, too little workspace, timeouts) are raised as for moe_layer
@@ -313,8 +313,8 @@ def decode_attention(q, k_cache, v_cache, context_lens, kv_start, *, scale=None,
     """
     lib = load_library()
     B, HQ, D = q.shape
-    rows, HKV, D2 = k_cache.shape
-    if D2 != D or tuple(v_cache.shape) != (rows, HKV, D) or HQ % HKV:
+    HKV, rows, D2 = k_cache.shape
+    if D2 != D or tuple(v_cache.shape) != (HKV, rows, D) or HQ % HKV:
         raise ValueError("q, k_cache and v_cache shapes disagree")
     G = HQ // HKV
     if scale is None:

@@ -19,7 +19,8 @@
 //   merge:               M = max m_c, L = sum l_c exp(m_c - M), out = sum o_c exp(m_c - M) / L
 //
 // Tasks (256 threads, four waves):
-//   P(b, g, c)  the chunk's 256 tokens: wave w takes tokens 64w .. 64w+63.  Scores come
+//   P(b, g, c)  the chunk's 256 tokens (contiguous rows of head g's cache, which is
+//               stored head-major: [H_kv][rows][128]): wave w takes tokens 64w .. 64w+63.  Scores come
 //               from bf16 MFMA 16x16x32 (the G query heads padded to 16 rows as the A
 //               operand, 16 tokens per block as the B operand, K read straight into
 //               registers in the MFMA layout); the chunk's max and weight sum per head
@@ -56,8 +57,8 @@ struct Args {
   const int* kv_start;  // [B] first cache row of each request (device)
   int kv_rows;
   const bf16* q;        // [B][HKV*G][HD]
-  const bf16* k;        // [kv_rows][HKV][HD]
-  const bf16* v;        // [kv_rows][HKV][HD]
+  const bf16* k;        // [HKV][kv_rows][HD]
+  const bf16* v;        // [HKV][kv_rows][HD]
   float* out;           // [B][HKV*G][HD]
   float* part;          // [cap][G][REC]
   int cap;              // partial records the workspace holds
@@ -70,6 +71,8 @@ struct Args {
 struct Smem {
   int pbase[MAXB + 1];  // first partial ticket of each request (exclusive scan of HKV * n_b)
   int nsplit[MAXB];
+  int len[MAXB];        // the requests' lengths and first cache rows, read once per call
+  int start[MAXB];
   int tmp[8];
   long long ltmp[4];
   float s[MAXG][CH];        // scores, then weights exp(s - m)
@@ -77,6 +80,7 @@ struct Smem {
   float o[4][MAXG][HD];     // per wave partial weighted value sums
   int task;
   int flag;
+  int next;  // a ticket drawn during the previous partial task (-1: none), thread 0
 };
 
 // Every thread: the call's plan from the device arrays: n_b = ceil(L_b / CH), the
@@ -93,6 +97,8 @@ ETC_DEV int make_plan(const Args& p, Smem& sm) {
     bad |= ok ? 0 : 1;
     lsum += ok ? L : 0;
     sm.nsplit[b] = ok ? cdiv(L, CH) : 0;
+    sm.len[b] = L;
+    sm.start[b] = st;
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) lsum += __shfl_xor(lsum, off, WAVE);
@@ -138,12 +144,13 @@ ETC_DEV void partial_task(const Args& p, Smem& sm, int b, int g, int c, int rec)
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = p.G, HQ = p.HKV * G;
-  const int L = gp(p.lens)[b];
+  const int L = sm.len[b];
   const int t0 = c * CH, n = min(CH, L - t0);
-  const size_t row0 = (size_t)gp(p.kv_start)[b] + t0;
-  const size_t rstride = (size_t)p.HKV * HD;  // elements between consecutive cache rows
-  const bf16* kb = p.k + row0 * rstride + (size_t)g * HD;
-  const bf16* vb = p.v + row0 * rstride + (size_t)g * HD;
+  // head g's rows of the chunk are contiguous: [g][kv_start[b] + t0 + t][HD]
+  const size_t row0 = (size_t)g * p.kv_rows + (size_t)sm.start[b] + t0;
+  constexpr int rstride = HD;
+  const bf16* kb = p.k + row0 * rstride;
+  const bf16* vb = p.v + row0 * rstride;
   const int q16 = lane & 15, grp = lane >> 4;
 
   // every load of this lane goes out first: q (A operand, head q16, dims 32kk + 8grp),
@@ -160,6 +167,10 @@ ETC_DEV void partial_task(const Args& p, Smem& sm, int b, int g, int c, int rec)
     const int t = min(w * TPW + 4 * i + grp, n - 1);
     vr[i] = gld<u32x4>(vb + t * rstride + 8 * q16);
   });
+  // the workgroup's next ticket, drawn while this chunk's loads are in flight (a later
+  // ticket than the running one, so the order stays deadlock-free: every partial ticket
+  // precedes every merge ticket, and a partial never waits)
+  if (tid == 0) sm.next = atomicAdd(p.sched + W_TICKET, 1);
 
   // scores of the wave's 64 tokens: block j holds heads 4*grp + r (rows) x tokens
   // 16j + q16 (columns)
@@ -299,9 +310,11 @@ __global__ __launch_bounds__(NT) void attn_kernel(Args p) {
   const int nmerge = p.B * p.HKV;
   const int total = !valid ? 0 : (p.mode == ETC_SCHED_STATIC ? np + nmerge : np);
 
+  if (tid == 0) sm.next = -1;
   while (true) {
     if (tid == 0) {
-      int t = atomicAdd(p.sched + W_TICKET, 1);
+      int t = sm.next >= 0 ? sm.next : atomicAdd(p.sched + W_TICKET, 1);
+      sm.next = -1;
       if (ev_load_relaxed(p.sched + W_ABORT)) t = total;
       sm.task = t;
     }

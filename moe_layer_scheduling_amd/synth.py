@@ -160,14 +160,14 @@ def draw_context_lens(batch, lo, hi, seed=0):
 def make_attention(lens, kv_heads, group, head_dim=128, seed=0):
     """(q, k_cache, v_cache, kv_start) for requests of the given context lengths: the
     caches hold the requests' rows one after another (kv_start = exclusive scan of the
-    lengths), [rows][kv_heads][head_dim]; q is [B][kv_heads*group][head_dim]; all
-    bfloat16 CPU tensors ~N(0, 1) (kv_start int32)."""
+    lengths), head-major [kv_heads][rows][head_dim]; q is [B][kv_heads*group][head_dim];
+    all bfloat16 CPU tensors ~N(0, 1) (kv_start int32)."""
     lens = torch.as_tensor(lens, dtype=torch.int64)
     B = lens.numel()
     rows = int(lens.sum())
     gen = torch.Generator().manual_seed(104_729 * seed + 31)
     q = _normal(gen, (B, kv_heads * group, head_dim), 1.0, torch.bfloat16)
-    k = _normal(gen, (rows, kv_heads, head_dim), 1.0, torch.bfloat16)
-    v = _normal(gen, (rows, kv_heads, head_dim), 1.0, torch.bfloat16)
+    k = _normal(gen, (kv_heads, rows, head_dim), 1.0, torch.bfloat16)
+    v = _normal(gen, (kv_heads, rows, head_dim), 1.0, torch.bfloat16)
     start = torch.cumsum(lens, 0) - lens
     return q, k, v, start.to(torch.int32)

@@ -57,7 +57,7 @@ def attention(lib, q, k, v, lens, kv_start, *, scale, mode="static", max_total=N
               workers=0, flags=0):
     """etc_decode_attention on host tensors.  Returns (out float64 array, status)."""
     B, HQ, D = q.shape
-    rows, HKV, _ = k.shape
+    HKV, rows, _ = k.shape
     G = HQ // HKV
     mb = max_batch or B
     mt = max_total or max(rows, 1)

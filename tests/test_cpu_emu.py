@@ -269,8 +269,10 @@ def _attn_case(lens, HKV=2, G=4, seed=3):
 
     q, k, v, start = synth.make_attention(lens, HKV, G, seed=seed)
     scale = 1.0 / np.sqrt(128.0)
-    ref = oa.decode_attention(synth.as_numpy(q), synth.as_numpy(k), synth.as_numpy(v),
-                              start.numpy(), np.asarray(lens), G, scale)
+    # the library's caches are head-major [H_kv][rows][D]; the oracle takes [rows][H_kv][D]
+    ref = oa.decode_attention(synth.as_numpy(q), synth.as_numpy(k).transpose(1, 0, 2),
+                              synth.as_numpy(v).transpose(1, 0, 2), start.numpy(), np.asarray(lens),
+                              G, scale)
     return q, k, v, start, scale, ref
 
 

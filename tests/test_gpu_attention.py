@@ -30,8 +30,10 @@ def _case(lens, HKV, G, seed):
 
 
 def _ref(q, k, v, start, lens, G, scale):
-    return oa.decode_attention(synth.as_numpy(q), synth.as_numpy(k), synth.as_numpy(v),
-                               start.numpy(), np.asarray(lens), G, scale)
+    # the library's caches are head-major [H_kv][rows][D]; the oracle takes [rows][H_kv][D]
+    kt = synth.as_numpy(k).transpose(1, 0, 2)
+    vt = synth.as_numpy(v).transpose(1, 0, 2)
+    return oa.decode_attention(synth.as_numpy(q), kt, vt, start.numpy(), np.asarray(lens), G, scale)
 
 
 def _run(q, k, v, lens, start, mode, ws=None, workers=0, flags=0):
