@@ -262,6 +262,30 @@ etc_status etc_decode_attention(int32_t batch, int32_t kv_heads, int32_t group, 
 size_t etc_decode_attention_workspace_size(int32_t max_batch, int32_t kv_heads, int32_t group,
                                            int32_t head_dim, int64_t max_total_tokens);
 
+/*
+ * etc_splitk_gemm_noalloc -- etc_splitk_gemm without a caller workspace and without any
+ * allocation, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * The partials and counters live in a 16 MiB array in the library's device memory, one
+ * per GPU, held until the process ends; calls whose workspace would exceed it
+ * (etc_splitk_workspace_size(M, N, split_k) > 16 MiB) return ETC_ERR_WORKSPACE before
+ * any HIP call.  Each call first clears the array's control words and counters with a
+ * small fill kernel on `stream` (no memset), then runs the same kernel as
+ * etc_splitk_gemm, so results are identical.  Every call on one GPU shares that GPU's
+ * array: calls that overlap on one GPU (different streams without ordering) race and
+ * must not be made.  The first call on a device looks up the array's device address
+ * (hipGetSymbolAddress); no call allocates.
+ *
+ *   M, N, K, split_k, A, B, C, mode, flags, workers, stream  as for etc_splitk_gemm
+ *   status   device int32 [1] or NULL: the kernel writes its device status there (0, or
+ *            ETC_ERR_TIMEOUT); with NULL a device timeout goes unreported
+ * Errors: as etc_splitk_gemm, with ETC_ERR_WORKSPACE for shapes beyond the array.
+ */
+etc_status etc_splitk_gemm_noalloc(int32_t M, int32_t N, int32_t K, int32_t split_k, const void* A,
+                                   const void* B, float* C, int32_t* status, etc_sched_mode mode,
+                                   uint32_t flags, int32_t workers, void* stream);
+
 /* Clear a freshly allocated workspace (enqueues a memset of all workspace_bytes on
  * `stream`).  Needed once after allocation, and after a call that failed with a
  * device timeout or used ETC_FLAG_KEEP_COUNTERS. */

@@ -82,6 +82,8 @@ def open_library(path):
     lib.etc_splitk_gemm.restype = ctypes.c_int
     lib.etc_splitk_gemm.argtypes = [c_i32] * 4 + [c_p, c_p, c_p, c_p, c_sz, ctypes.c_int, c_u32,
                                                   c_i32, c_p]
+    lib.etc_splitk_gemm_noalloc.restype = ctypes.c_int
+    lib.etc_splitk_gemm_noalloc.argtypes = [c_i32] * 4 + [c_p, c_p, c_p, c_p, ctypes.c_int, c_u32, c_i32, c_p]
     lib.etc_splitk_workspace_size.restype = c_sz
     lib.etc_splitk_workspace_size.argtypes = [c_i32] * 3
     lib.etc_workspace_init.restype = ctypes.c_int
@@ -336,6 +338,25 @@ def decode_attention(q, k_cache, v_cache, context_lens, kv_start, *, scale=None,
     if own or check:
         _check(workspace.status(), "etc_decode_attention (device)")
     return out
+
+
+def splitk_gemm_noalloc(A, B, split_k=8, *, mode="static", out=None, status=None, workers=0, flags=0):
+    """C = A @ B like splitk_gemm, through the library's allocation-free entry point (its
+    partials live in a static device array; no workspace is passed).  out: optional
+    preallocated float32 [M][N]; status: optional device int32 [1] that receives the
+    kernel's device status."""
+    lib = load_library()
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    C = out if out is not None else torch.empty(M, N, dtype=torch.float32, device=A.device)
+    st = lib.etc_splitk_gemm_noalloc(M, N, K, split_k, _dev_ptr(A, "A", torch.bfloat16),
+                                     _dev_ptr(B, "B", torch.bfloat16), _dev_ptr(C, "out", torch.float32),
+                                     _dev_ptr(status, "status", torch.int32), MODES[mode], int(flags),
+                                     int(workers), _stream())
+    _check(st, "etc_splitk_gemm_noalloc")
+    return C
 
 
 def default_workers(kind="moe", dtype=torch.bfloat16):

@@ -26,6 +26,8 @@
 // consecutive k per lane, so each lane gathers its 8 values with 2-byte LDS reads; the
 // 16-byte chunk c of B row r sits at position c ^ ((r / 8) % 16), which puts the four
 // k groups of a quarter-wave in different banks.
+#include <mutex>
+
 #include "common.hpp"
 #include "host.hpp"
 #include "mfma.hpp"
@@ -55,6 +57,7 @@ struct Args {
   float* part;   // [tiles][S][TM][TN]
   int* sched;    // control words
   int* ev;       // [tiles]
+  int* status;   // or null: the last workgroup out copies the status word here
   uint64_t timeout_ticks;
 };
 
@@ -230,10 +233,18 @@ __global__ __launch_bounds__(NT) void splitk_kernel(Args p) {
   wg_publish();
   if (tid == 0) sm.flag = (atomicAdd(p.sched + W_EXIT, 1) == (int)gridDim.x - 1) ? 1 : 0;
   __syncthreads();
+  if (sm.flag && tid == 0 && p.status) gp(p.status)[0] = ev_load_relaxed(p.sched + W_STATUS);
   if (sm.flag && !(p.flags & ETC_FLAG_KEEP_COUNTERS)) {
     for (int i = tid; i < p.tiles; i += NT) ev_store_relaxed(p.ev + i, 0);
     if (tid < W_NWORDS && tid != W_STATUS && tid != W_AUX) ev_store_relaxed(p.sched + tid, 0);
   }
+}
+
+// Clears n int32 words at p: the control words and counters of a scratch buffer that
+// an earlier call may have left dirty (a fill kernel rather than a memset, so that the
+// clear can sit inside a captured graph).
+__global__ __launch_bounds__(NT) void clear_words(int* p, int n) {
+  for (int i = blockIdx.x * NT + threadIdx.x; i < n; i += gridDim.x * NT) p[i] = 0;
 }
 
 struct Layout {
@@ -250,6 +261,25 @@ inline Layout layout(int M, int N, int S) {
   L.part = c.take((size_t)L.tiles * S * TM * TN * sizeof(float));
   L.total = c.off;
   return L;
+}
+
+// Scratch of the allocation-free entry point: one array per device, held until the
+// process ends.  Host code never uses this name as an address (in host code it is a
+// stand-in); it uses the device address recorded by scratch_ptr().
+constexpr size_t SCRATCH_BYTES = (size_t)16 << 20;
+static __device__ __align__(256) char scratch[SCRATCH_BYTES];
+
+// Device address of `scratch` on device dev (current), looked up once per device.
+void* scratch_ptr(int dev) {
+  static std::mutex mu;
+  static void* ptr[host::MAX_DEVICES] = {nullptr};
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    ptr[dev] = p;
+  }
+  return ptr[dev];
 }
 
 }  // namespace splitk
@@ -282,10 +312,39 @@ ETC_API size_t etc_splitk_workspace_size(int32_t M, int32_t N, int32_t split_k) 
   return splitk::layout(M, N, split_k).total;
 }
 
+static etc_status splitk_launch(int32_t M, int32_t N, int32_t K, int32_t split_k, const void* A,
+                                const void* B, float* C, void* workspace, size_t workspace_bytes,
+                                etc_sched_mode mode, uint32_t flags, int32_t workers, void* stream,
+                                bool clear_first, int32_t* status);
+
 ETC_API etc_status etc_splitk_gemm(int32_t M, int32_t N, int32_t K, int32_t split_k,
                                    const void* A, const void* B, float* C, void* workspace,
                                    size_t workspace_bytes, etc_sched_mode mode, uint32_t flags,
                                    int32_t workers, void* stream) {
+  return splitk_launch(M, N, K, split_k, A, B, C, workspace, workspace_bytes, mode, flags, workers, stream,
+                       false, nullptr);
+}
+
+ETC_API etc_status etc_splitk_gemm_noalloc(int32_t M, int32_t N, int32_t K, int32_t split_k, const void* A,
+                                           const void* B, float* C, int32_t* status, etc_sched_mode mode,
+                                           uint32_t flags, int32_t workers, void* stream) {
+  if (M < 1 || N < 1 || K < 1 || split_k < 1) return ETC_ERR_INVALID_ARG;
+  if (!A || !B || !C) return ETC_ERR_INVALID_ARG;
+  if (status && (reinterpret_cast<uintptr_t>(status) & 3u)) return ETC_ERR_INVALID_ARG;
+  if (!splitk_shape_ok(M, N, K, split_k)) return ETC_ERR_UNSUPPORTED;
+  if (splitk::layout(M, N, split_k).total > splitk::SCRATCH_BYTES) return ETC_ERR_WORKSPACE;
+  const int dev = host::current_gfx950_device();
+  if (dev < 0) return ETC_ERR_NO_DEVICE;
+  void* ws = splitk::scratch_ptr(dev);
+  if (!ws) return ETC_ERR_HIP;
+  return splitk_launch(M, N, K, split_k, A, B, C, ws, splitk::SCRATCH_BYTES, mode, flags, workers, stream,
+                       true, status);
+}
+
+static etc_status splitk_launch(int32_t M, int32_t N, int32_t K, int32_t split_k, const void* A,
+                                const void* B, float* C, void* workspace, size_t workspace_bytes,
+                                etc_sched_mode mode, uint32_t flags, int32_t workers, void* stream,
+                                bool clear_first, int32_t* status) {
   if (M < 1 || N < 1 || K < 1 || split_k < 1) return ETC_ERR_INVALID_ARG;
   if (!A || !B || !C) return ETC_ERR_INVALID_ARG;
   if (mode != ETC_SCHED_STATIC && mode != ETC_SCHED_DYNAMIC) return ETC_ERR_INVALID_ARG;
@@ -311,9 +370,18 @@ ETC_API etc_status etc_splitk_gemm(int32_t M, int32_t N, int32_t K, int32_t spli
   p.sched = reinterpret_cast<int*>(ws + L.sched);
   p.ev = reinterpret_cast<int*>(ws + L.ev);
   p.part = reinterpret_cast<float*>(ws + L.part);
+  p.status = status;
   p.timeout_ticks = 500000000ull;  // 5 s without progress, on the 100 MHz real-time clock
 
   const int grid = host::grid_size(workers, host::device_cus(dev), splitk_occupancy(dev));
+  if (clear_first) {
+    // the shared scratch keeps the last call's contents: its control words and counters
+    // (everything before the partials, including the status word) start at zero
+    const int words = (int)(L.part / sizeof(int));
+    hipLaunchKernelGGL(splitk::clear_words, dim3(cdiv(words, NT)), dim3(NT), 0, static_cast<hipStream_t>(stream),
+                       reinterpret_cast<int*>(workspace), words);
+    if (hipGetLastError() != hipSuccess) return ETC_ERR_HIP;
+  }
   hipLaunchKernelGGL(splitk::splitk_kernel, dim3(grid), dim3(NT), 0, static_cast<hipStream_t>(stream), p);
   return hipGetLastError() == hipSuccess ? ETC_OK : ETC_ERR_HIP;
 }

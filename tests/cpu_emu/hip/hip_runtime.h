@@ -22,6 +22,7 @@
 
 #define __global__
 #define __device__
+#define __align__(n) __attribute__((aligned(n)))
 #define __host__
 #define __forceinline__ inline
 #define __launch_bounds__(...)
@@ -203,5 +204,12 @@ hipError_t hipOccupancyMaxActiveBlocksPerMultiprocessor(int* v, F, int, size_t) 
   return hipSuccess;
 }
 void emu_launch(unsigned grid, unsigned block, std::function<void()> fn);
+// a device variable's address is its host address here
+#define HIP_SYMBOL(x) (x)
+template <typename T>
+hipError_t hipGetSymbolAddress(void** p, T& sym) {
+  *p = (void*)&sym;
+  return hipSuccess;
+}
 #define hipLaunchKernelGGL(kernel, grid, block, shm, stream, ...) \
   emu_launch((grid).x, (block).x, [=]() { kernel(__VA_ARGS__); })
