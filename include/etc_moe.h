@@ -55,8 +55,12 @@ typedef enum { ETC_DTYPE_F32 = 0, ETC_DTYPE_BF16 = 1 } etc_dtype;
  * producer whose signal completes a counter enqueues the dependents, and workgroups
  * only ever take ready tasks.  (Episode summary of the podcast page: static suits
  * regular work, dynamic pays off under irregularity such as MoE routing; chapter §5.5
- * Obstacle 3: online balancing through atomics.) */
-typedef enum { ETC_SCHED_STATIC = 0, ETC_SCHED_DYNAMIC = 1 } etc_sched_mode;
+ * Obstacle 3: online balancing through atomics.)  Dedicated (etc_moe_layer only):
+ * workgroup 0 is a scheduler that watches the event counters of a window of the
+ * static order and hands ready tasks to per-worker mailboxes; workers never wait on a
+ * counter (chapter, Q&A on the Cluster Launch Control: MPK's scheduler units feeding
+ * worker queues).  Needs at least two workgroups. */
+typedef enum { ETC_SCHED_STATIC = 0, ETC_SCHED_DYNAMIC = 1, ETC_SCHED_DEDICATED = 2 } etc_sched_mode;
 
 /* Atomic: the down-projection tiles add gate * y straight into a float32 accumulator
  * (order of additions varies run to run).  Ordered: they store y and the finalize

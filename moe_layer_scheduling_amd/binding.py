@@ -18,7 +18,7 @@ ABI_VERSION = 0x00010000
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "workspace",
           4: "HIP runtime error", 5: "device wait timed out", 6: "no gfx950 device"}
 DTYPES = {torch.float32: 0, torch.bfloat16: 1}
-MODES = {"static": 0, "dynamic": 1}
+MODES = {"static": 0, "dynamic": 1, "dedicated": 2}  # dedicated: etc_moe_layer only
 COMBINES = {"atomic": 0, "ordered": 1}
 FLAG_KEEP_COUNTERS = 0x1
 FLAG_TRACE = 0x2

@@ -1201,7 +1201,7 @@ ETC_DEV void after_scan(KArgs& p, int layer, Smem& sm) {
     ev_store_relaxed(L.ev_scan, 1);  // the event tensor is complete
     if (p.n_perm == 0) ev_store_relaxed(L.ev_perm, p.n_rt);
   }
-  if (p.mode == ETC_SCHED_STATIC) return;
+  if (p.mode != ETC_SCHED_DYNAMIC) return;
   if (p.n_perm > 0) {
     push_many(p, sm, p.n_perm, [&](int i) {
       Task t;
@@ -1341,6 +1341,223 @@ ETC_DEV void run_task(KArgs& p, KLayer& L, const Task& t, Smem& sm) {
   }
 }
 
+
+// ------------------------------------------------------------------ dedicated scheduler
+//
+// Mode ETC_SCHED_DEDICATED: workgroup 0 schedules and the others work, after the runtime
+// the tutorial chapter "5 · Event Tensor et le dynamisme" describes for MPK (Q&A on the
+// Cluster Launch Control): scheduler units watch the events and hand ready tasks to
+// worker queues.  Worker w owns mailbox w (a 64-bit word in the workspace): it posts the
+// idle word when it starts and after every task, and otherwise waits on its own mailbox
+// only; a task word there is a task whose inputs are complete, which it runs and signals
+// as in static mode.  The scheduler is one wavefront.  It walks the static topological
+// order with a window of 64 tickets, one per lane: each lane decodes its ticket (once the
+// ticket's layer has published its plan) and reads the one counter the task waits on;
+// ready tickets go to idle workers in ticket order.  Every ticket before the window is
+// assigned, so the producers of the window's first ticket are all assigned and it
+// becomes ready as they finish: the scheduler keeps making progress.  Only workers that
+// have posted the idle word receive tasks, so a workgroup that is not resident yet holds
+// none.  Once every ticket is assigned and every worker is idle it writes the exit word
+// to every mailbox; a worker empties its mailbox (0) as it leaves.  Workers never wait
+// on a counter.
+
+constexpr int K_EXIT = 15;  // mailbox word: leave the task loop
+constexpr int K_IDLE = 14;  // mailbox word: the worker waits for a task
+
+struct SchedSmem {
+  int planned;                  // bit l: layer l's plan and row-tile bases are cached
+  int base[MAXL + 1];           // first ticket of each layer (-1: not known yet)
+  int plan[MAXL][PL_WORDS];
+  int rtb[MAXL][MAXE + 1];
+  int busy[MAX_WORKERS];        // 1: the worker holds a task
+  int freelist[MAX_WORKERS];
+  int word;                     // lane 0's reading, for the whole wave
+};
+static_assert(sizeof(SchedSmem) <= sizeof(SmemU), "the scheduler's state fits the task area");
+
+// The task of ticket c.  Returns 0 with the task, 1 if a plan it needs is not known yet,
+// 2 if c lies past the last ticket (every layer has planned).
+ETC_DEV int sched_decode(KArgs& p, const SchedSmem& S, int c, Task& t) {
+  t.kind = K_NONE; t.layer = 0; t.a = t.b = t.c = t.d = 0;
+  for (int l = 0; l < p.L; ++l) {
+    const int base = S.base[l];
+    if (base < 0) return 1;
+    t.layer = l;
+    if (c < base + p.n_rt) { t.kind = K_R; t.a = c - base; return 0; }
+    int off = c - base - p.n_rt;
+    if (off < p.n_perm) { t.kind = K_P; t.a = off; return 0; }
+    off -= p.n_perm;
+    if (!(S.planned >> l & 1)) return 1;
+    const int* pl = S.plan[l];
+    const int* rb = S.rtb[l];
+    const int ngu = pl[PL_NGU], nd = pl[PL_ND], nf = pl[PL_NF], nS = pl[PL_NS];
+    if (off < ngu) {
+      const int e = owner_expert_by([&](int i) ETC_INLINE { return rb[i]; }, p.E, off, p.n1);
+      const int me = rb[e + 1] - rb[e], loc = off - rb[e] * p.n1;
+      t.kind = K_GU; t.a = e; t.b = loc % me; t.c = loc / me;
+      return 0;
+    }
+    off -= ngu;
+    if (off < nd) {
+      const int e = owner_expert_by([&](int i) ETC_INLINE { return rb[i]; }, p.E, off, p.n2 * nS);
+      const int me = rb[e + 1] - rb[e], loc = off - rb[e] * p.n2 * nS;
+      t.kind = K_D; t.a = e; t.b = loc % me; t.c = (loc / me) % p.n2; t.d = loc / (me * p.n2);
+      return 0;
+    }
+    off -= nd;
+    if (off < nf) { t.kind = K_F; t.a = off; return 0; }
+  }
+  return 2;
+}
+
+// Whether the task's inputs are complete: the counter it waits on has reached its target
+// (one relaxed load; the worker that receives the task acquires through its mailbox).
+ETC_DEV bool sched_ready(KArgs& p, const SchedSmem& S, const Task& t) {
+  KLayer& L = p.layer[t.layer];
+  switch (t.kind) {
+    case K_R:
+      return t.layer == 0 || ev_load_relaxed(p.layer[t.layer - 1].ev_done + t.a) >= 1;
+    case K_P:
+      return ev_load_relaxed(L.ev_scan) >= 1;
+    case K_GU:
+      return ev_load_relaxed(L.ev_perm) >= p.n_rt;
+    case K_D: {
+      const int gpc = S.plan[t.layer][PL_GPC];
+      const int rt = S.rtb[t.layer][t.a] + t.b;
+      return ev_load_relaxed(L.ev_gu + rt * p.n1 + t.d) >= min(gpc, p.n1 - t.d * gpc);
+    }
+    case K_F:
+      return ev_load_relaxed(L.ev_comb + t.a) >=
+             tile_rows(p, t.a) * p.K * p.n2 * S.plan[t.layer][PL_NS];
+    default:
+      return false;
+  }
+}
+
+// The scheduler: every lane of wave 0 of workgroup 0.  Returns when every worker has been
+// sent the exit word, or when the call is aborted.
+ETC_DEV void run_scheduler(KArgs& p, Smem& sm) {
+  SchedSmem& S = *reinterpret_cast<SchedSmem*>(&sm.u);
+  const int lane = threadIdx.x & 63;
+  const int W = (int)gridDim.x;  // mailboxes 1 .. W-1
+  for (int w = lane; w < W; w += WAVE) S.busy[w] = 1;  // not idle until it says so
+  if (lane <= MAXL) S.base[lane] = lane == 0 ? 0 : -1;
+  if (lane == 0) S.planned = 0;
+  __builtin_amdgcn_wave_barrier();
+  int next = 0;                // lowest ticket not yet assigned
+  unsigned long long amask = 0;  // bit i: ticket next + i is assigned
+  Watchdog wd;
+  for (int it = 0;; ++it) {
+    // plans published by the layers' scans: copy each one once
+    for (int l = 0; l < p.L; ++l) {
+      if ((S.planned >> l & 1) || S.base[l] < 0) continue;
+      KLayer& L = p.layer[l];
+      // lane 0 reads the event (acquire once complete: the plan and bases written before it)
+      if (lane == 0) S.word = ev_load_relaxed(L.ev_scan) >= 1 && ev_load(L.ev_scan) >= 1;
+      __builtin_amdgcn_wave_barrier();
+      const int scanned = S.word;
+      __builtin_amdgcn_wave_barrier();
+      if (!scanned) continue;
+      if (lane < PL_WORDS) S.plan[l][lane] = gp(L.plan)[lane];
+      for (int e = lane; e <= p.E; e += WAVE) S.rtb[l][e] = gp(L.rt_base)[e];
+      __builtin_amdgcn_wave_barrier();
+      if (lane == 0) {
+        S.base[l + 1] = S.plan[l][PL_NEXTBASE];
+        S.planned |= 1 << l;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+    const int total = S.base[p.L];  // -1 until every layer has planned
+
+    // workers that have posted the idle word; the idle ones in order (the mailboxes of
+    // four groups of 64 workers are read before any is looked at)
+    int nfree = 0;
+    for (int w0 = 1; w0 < W; w0 += 4 * WAVE) {
+      long long box[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int w = w0 + j * WAVE + lane;
+        box[j] = (w < W && S.busy[w]) ? q_load_relaxed(p.queue + w) : (long long)K_IDLE;
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int w = w0 + j * WAVE + lane;
+        const bool idle = w < W && box[j] == K_IDLE;
+        if (idle) S.busy[w] = 0;
+        const unsigned long long m = __ballot(idle);
+        if (idle) S.freelist[nfree + __popcll(m & ((1ull << lane) - 1ull))] = w;
+        nfree += __popcll(m);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // the window's ready tickets go to idle workers, in ticket order
+    const int c = next + lane;
+    Task t;
+    const int st = sched_decode(p, S, c, t);
+    const bool ready = st == 0 && !((amask >> lane) & 1ull) && sched_ready(p, S, t);
+    const unsigned long long rmask = __ballot(ready);
+    const int rank = __popcll(rmask & ((1ull << lane) - 1ull));
+    const bool give = ready && rank < nfree;
+    if (give) {
+      // the task's inputs reached the point of coherence before the counter did; the
+      // worker acquires its mailbox before reading them
+      const int w = S.freelist[rank];
+      S.busy[w] = 1;
+      q_store_relaxed(p.queue + w, enc(t));
+    }
+    const unsigned long long gmask = __ballot(give);
+    if (gmask && lane == 0) ev_add_relaxed(p.sched + W_QHEAD, 1);  // progress seen by idle workers
+    amask |= gmask;
+    // slide the window past its assigned prefix
+    const int done = amask == ~0ull ? 64 : __builtin_ctzll(~amask);
+    next += done;
+    amask = done == 64 ? 0ull : (amask >> done);
+
+    const int idle_now = nfree - __popcll(gmask);
+    if (total >= 0 && next >= total && idle_now == W - 1) {
+      for (int w = 1 + lane; w < W; w += WAVE) q_store_relaxed(p.queue + w, (long long)K_EXIT);
+      return;
+    }
+    // the watchdog (lane 0) counts a new ticket assigned or a worker finishing as progress
+    const int seen = next * 4099 + idle_now;
+    if (it == 0) {
+      if (lane == 0) wd.start(p.timeout_ticks, seen);
+    } else if (it % WATCH_EVERY == 0) {
+      if (lane == 0) S.word = wd.expired(p.sched, p.timeout_ticks, seen, 40) ? 1 : 0;
+      __builtin_amdgcn_wave_barrier();
+      const int stop = S.word;
+      __builtin_amdgcn_wave_barrier();
+      if (stop) return;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+// A worker's wait for its mailbox (thread 0).  Returns false if the call was aborted.
+ETC_DEV bool claim_mailbox(KArgs& p, Task& t) {
+  long long* box = p.queue + blockIdx.x;
+  Watchdog wd;
+  for (int it = 0;; ++it) {
+    const long long w = q_load_relaxed(box);
+    if (w != K_IDLE && w != 0) {
+      const long long v = q_load(box);  // acquire: the task's inputs are complete
+      if ((v & 15) == K_EXIT) {
+        q_store_relaxed(box, 0);  // the mailbox is empty for the next call
+        t.kind = K_NONE;
+      } else {
+        t = dec(v);
+      }
+      return true;
+    }
+    if (it == 0) wd.start(p.timeout_ticks, ev_load_relaxed(p.sched + W_QHEAD));
+    else if (it % WATCH_EVERY == 0 &&
+             wd.expired(p.sched, p.timeout_ticks, ev_load_relaxed(p.sched + W_QHEAD), 41))
+      return false;
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
 template <typename TE>
 __global__ __launch_bounds__(MNT) void moe_kernel(Args pk) {
   __shared__ Smem sm;
@@ -1367,7 +1584,12 @@ __global__ __launch_bounds__(MNT) void moe_kernel(Args pk) {
     sm.next_ticket = -1;
     for (int l = 0; l <= MAXL; ++l) sm.lbase[l] = -1;
   }
-  while (true) {
+  const bool dedicated = p.mode == ETC_SCHED_DEDICATED;
+  if (dedicated && blockIdx.x != 0 && tid == 0) q_store_relaxed(p.queue + blockIdx.x, K_IDLE);
+  if (dedicated && blockIdx.x == 0) {
+    // the scheduler workgroup: wave 0 schedules, the other waves wait at the exit
+    if (tid < WAVE) run_scheduler(p, sm);
+  } else while (true) {
     // Thread 0 claims a task.  A gate/up, down or finalize task of a layer whose plan the
     // workgroup has not cached yet first has the whole workgroup copy it into LDS; then
     // (static mode) thread 0 waits for the task's inputs.
@@ -1375,8 +1597,9 @@ __global__ __launch_bounds__(MNT) void moe_kernel(Args pk) {
       if (tracing) t_claim = now_ticks();
       Task t;
       t.kind = K_NONE; t.layer = 0; t.a = t.b = t.c = t.d = 0;
-      const bool ok = (p.mode == ETC_SCHED_STATIC) ? claim_static(p, t, sm)
-                                                    : claim_dynamic(p, t);
+      const bool ok = (p.mode == ETC_SCHED_STATIC)    ? claim_static(p, t, sm)
+                      : (p.mode == ETC_SCHED_DYNAMIC) ? claim_dynamic(p, t)
+                                                      : claim_mailbox(p, t);
       if (!ok) t.kind = K_NONE;
       const bool gemm_or_f = t.kind == K_GU || t.kind == K_D || t.kind == K_F;
       sm.need_cache = (gemm_or_f && sm.lc.layer != t.layer) ? 1 : 0;
@@ -1405,12 +1628,19 @@ __global__ __launch_bounds__(MNT) void moe_kernel(Args pk) {
     KLayer& L = p.layer[t.layer];
     run_task<TE>(p, L, t, sm);
     if (tracing && tid == 0) trace_record(p, t, t_claim, t_run, now_ticks());
+    // dedicated mode: the task's signals have gone out (run_task ends at a barrier after
+    // them); the worker is idle again
+    if (dedicated && tid == 0) q_store_relaxed(p.queue + blockIdx.x, K_IDLE);
   }
 
   // the last workgroup out clears the event counters and control words
   wg_publish();
   if (tid == 0) sm.flag = (ev_add_relaxed(p.sched + W_EXIT, 1) == (int)gridDim.x - 1) ? 1 : 0;
   __syncthreads();
+  // dedicated mode: empty mailboxes for the next call (an aborted call can leave task
+  // words behind)
+  if (sm.flag && dedicated)
+    for (int i = tid; i < (int)gridDim.x; i += MNT) q_store_relaxed(p.queue + i, 0);
   if (sm.flag && !(p.flags & ETC_FLAG_KEEP_COUNTERS)) {
     for (int l = 0; l < p.L; ++l) {
       KLayer& L = p.layer[l];
@@ -1565,7 +1795,9 @@ ETC_API etc_status etc_moe_layer(int32_t T, int32_t H, int32_t E, int32_t K, int
   etc_status st = moe_shape_check(max_tokens, H, E, K, F, nl, dtype);
   if (st != ETC_OK) return st;
   if (T < 0 || T > max_tokens || !(eps >= 0.f)) return ETC_ERR_INVALID_ARG;
-  if (mode != ETC_SCHED_STATIC && mode != ETC_SCHED_DYNAMIC) return ETC_ERR_INVALID_ARG;
+  if (mode != ETC_SCHED_STATIC && mode != ETC_SCHED_DYNAMIC && mode != ETC_SCHED_DEDICATED)
+    return ETC_ERR_INVALID_ARG;
+  if (mode == ETC_SCHED_DEDICATED && workers == 1) return ETC_ERR_INVALID_ARG;  // a scheduler and a worker
   // The dynamic (ready-queue) scheduler runs only when the caller opts in: a run of it on
   // MI355X did not terminate and its cause has not been identified.
   if (mode == ETC_SCHED_DYNAMIC && !(flags & ETC_FLAG_ALLOW_DYNAMIC)) return ETC_ERR_UNSUPPORTED;
@@ -1612,6 +1844,7 @@ ETC_API etc_status etc_moe_layer(int32_t T, int32_t H, int32_t E, int32_t K, int
   p.timeout_ticks = 500000000ull;  // 5 s without progress, on the 100 MHz real-time clock
   int grid = host::grid_size(workers, host::device_cus(dev), moe_occupancy(dev, dtype));
   if (grid > moe::MAX_WORKERS) grid = moe::MAX_WORKERS;
+  if (mode == ETC_SCHED_DEDICATED && grid < 2) return ETC_ERR_INVALID_ARG;  // a scheduler and a worker
   p.workers = grid;
   p.xq = ws + Y.xq;
   p.hbuf = ws + Y.hbuf;

@@ -110,6 +110,22 @@ inline int emu_readfirstlane(int v) {
 }
 #define __builtin_amdgcn_readfirstlane(x) emu_readfirstlane(x)
 
+// bit l set when lane l's predicate holds (every lane of the wave takes part)
+inline unsigned long long emu_ballot(int pred) {
+  unsigned char* buf = static_cast<unsigned char*>(emu_wave_scratch(1));
+  const int lane = emu_lane();
+  buf[lane] = pred ? 1 : 0;
+  emu_wave_barrier();
+  unsigned long long m = 0;
+  for (int i = 0; i < 64; ++i)
+    if (buf[i]) m |= 1ull << i;
+  emu_wave_barrier();
+  return m;
+}
+#define __ballot(x) emu_ballot(x)
+#define __builtin_amdgcn_wave_barrier() emu_wave_barrier()
+inline int __popcll(unsigned long long v) { return __builtin_popcountll(v); }
+
 template <typename T>
 inline T min(T a, T b) { return b < a ? b : a; }
 template <typename T>

@@ -119,6 +119,7 @@ def test_moe_argument_errors_before_any_hip_call(lib):
     assert _call_moe(lib, ws=None) == WS
     assert _call_moe(lib, ws=256 * 1024 + 16) == WS  # not 256-byte aligned
     assert _call_moe(lib, wsb=1024) == WS
+    assert _call_moe(lib, mode=2, workers=1) == INVALID  # dedicated: a scheduler and a worker
 
 
 def test_dynamic_moe_refused_without_the_flag(lib):
@@ -145,6 +146,7 @@ def test_splitk_argument_errors_before_any_hip_call(lib):
     assert call(K=14336 + 64) == 2  # K not a multiple of 64 * split_k
     assert call(S=65) == 2
     assert call(wsb=100) == 3
+    assert f(64, 4096, 14336, 8, 1 << 20, 2 << 20, 3 << 20, 4 << 20, 1 << 30, 2, 0, 0, None) == 1  # no dedicated mode
 
 
 def test_no_cpu_fallback_without_library(tmp_path, monkeypatch):
@@ -186,5 +188,6 @@ def test_decode_attention_arguments_before_any_hip_call(lib):
     assert call(rows=0) == 1
     assert call(scale=float("nan")) == 1
     assert call(mode=3) == 1
+    assert call(mode=2) == 1  # the dedicated scheduler is the MoE layer's only
     assert call(ws=None) == 3
     assert call(wsb=ws_n - 1) == 3

@@ -18,6 +18,8 @@ from tests.cpu_emu import build_emu, driver
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 MID = synth.MoEConfig("mid", (300,), 512, 16, 6, 384, layers=2, zipf_s=0.5)
+# the MoE layer's three schedulers (split-K and attention have the first two)
+MOE_MODES = ["static", "dynamic", "dedicated"]
 
 
 @pytest.fixture(scope="module")
@@ -35,7 +37,7 @@ def _check(cfg, x, layers, g):
                              cfg.dtype, g)
 
 
-@pytest.mark.parametrize("mode", ["static", "dynamic"])
+@pytest.mark.parametrize("mode", MOE_MODES)
 @pytest.mark.parametrize("combine", ["atomic", "ordered"])
 def test_tiny(lib, mode, combine):
     cfg = synth.CONFIGS["tiny"]
@@ -43,7 +45,7 @@ def test_tiny(lib, mode, combine):
     _check(cfg, x, layers, driver.moe(lib, cfg, x, layers, mode=mode, combine=combine))
 
 
-@pytest.mark.parametrize("mode", ["static", "dynamic"])
+@pytest.mark.parametrize("mode", MOE_MODES)
 def test_mid_ragged_one_layer(lib, mode):
     cfg = MID.with_(layers=1)
     layers, x = synth.make_layers(cfg), synth.make_x(cfg, 33)
@@ -53,7 +55,7 @@ def test_mid_ragged_one_layer(lib, mode):
 SMALL = synth.MoEConfig("small", (18,), 512, 8, 2, 256, layers=2)
 
 
-@pytest.mark.parametrize("mode", ["static", "dynamic"])
+@pytest.mark.parametrize("mode", MOE_MODES)
 @pytest.mark.parametrize("T", [1, 2, 17, 18])
 def test_one_or_two_token_tiles(lib, mode, T):
     """Routing tiles of one or two tokens (the whole batch, or the last tile after a full
@@ -66,7 +68,7 @@ def test_one_or_two_token_tiles(lib, mode, T):
 EDGE = synth.MoEConfig("edge", (70,), 384, 6, 2, 320, layers=2, zipf_s=0.3)
 
 
-@pytest.mark.parametrize("mode", ["static", "dynamic"])
+@pytest.mark.parametrize("mode", MOE_MODES)
 def test_ragged_hidden_and_ffn_tiles(lib, mode):
     """H = 384 and F = 320 end inside a column tile of both GEMMs and inside a split of
     the down projection."""
@@ -78,7 +80,7 @@ def test_ragged_hidden_and_ffn_tiles(lib, mode):
 WIDE = synth.MoEConfig("wide", (1040,), 128, 256, 2, 64, layers=1, zipf_s=0.8)
 
 
-@pytest.mark.parametrize("mode", ["static", "dynamic"])
+@pytest.mark.parametrize("mode", MOE_MODES)
 def test_histogram_too_large_for_lds(lib, mode):
     """65 routing tiles x 256 experts: the scan reads the histogram in place instead of
     staging it in LDS."""
@@ -91,7 +93,7 @@ LIMITS = synth.MoEConfig("limits", (200,), 256, 256, 16, 128, layers=1, zipf_s=0
 DEEP = synth.MoEConfig("deep", (40,), 256, 8, 2, 128, layers=4)
 
 
-@pytest.mark.parametrize("mode", ["static", "dynamic"])
+@pytest.mark.parametrize("mode", MOE_MODES)
 @pytest.mark.parametrize("T", [40, 200])
 def test_most_experts_and_top_k(lib, mode, T):
     """256 experts and top-16 (the largest the library accepts), with the permutation
@@ -101,7 +103,7 @@ def test_most_experts_and_top_k(lib, mode, T):
     _check(cfg, x, layers, driver.moe(lib, cfg, x, layers, mode=mode, max_tokens=200))
 
 
-@pytest.mark.parametrize("mode", ["static", "dynamic"])
+@pytest.mark.parametrize("mode", MOE_MODES)
 @pytest.mark.parametrize("which", sorted(moe_check.DEGENERATE))
 def test_degenerate_cases(lib, mode, which):
     """One expert with top-1, top-k equal to the expert count, identical experts."""
@@ -111,7 +113,7 @@ def test_degenerate_cases(lib, mode, which):
     moe_check.check_degenerate(which, cfg, x, layers, g)
 
 
-@pytest.mark.parametrize("mode", ["static", "dynamic"])
+@pytest.mark.parametrize("mode", MOE_MODES)
 def test_four_chained_layers(lib, mode):
     """Four layers (the most one call chains) of a small shape."""
     cfg = DEEP
@@ -125,14 +127,17 @@ def test_mid_two_layers_dynamic(lib):
     _check(cfg, x, layers, driver.moe(lib, cfg, x, layers, mode="dynamic"))
 
 
-@pytest.mark.parametrize("mode", ["static", "dynamic"])
+@pytest.mark.parametrize("mode", MOE_MODES)
 def test_single_worker(lib, mode):
+    """One worker: a single workgroup (static, dynamic), or the scheduler workgroup and
+    one worker (dedicated)."""
     cfg = synth.CONFIGS["tiny"]
     layers, x = synth.make_layers(cfg), synth.make_x(cfg, 16, call=2)
-    _check(cfg, x, layers, driver.moe(lib, cfg, x, layers, mode=mode, workers=1))
+    workers = 2 if mode == "dedicated" else 1
+    _check(cfg, x, layers, driver.moe(lib, cfg, x, layers, mode=mode, workers=workers))
 
 
-@pytest.mark.parametrize("mode", ["static", "dynamic"])
+@pytest.mark.parametrize("mode", MOE_MODES)
 def test_event_tensor_final_state(lib, mode):
     cfg = MID.with_(layers=1)
     T = 64
@@ -166,7 +171,7 @@ def test_splitk(lib, mode):
     assert np.max(np.abs(C.numpy() - ref)) <= 1e-3 * np.max(np.abs(ref))
 
 
-@pytest.mark.parametrize("mode", ["static", "dynamic"])
+@pytest.mark.parametrize("mode", MOE_MODES)
 @pytest.mark.parametrize("T", [40, 100])
 def test_trace_has_one_record_per_task(lib, mode, T):
     from moe_layer_scheduling_amd import trace
@@ -196,7 +201,7 @@ def test_trace_has_one_record_per_task(lib, mode, T):
     assert s["span_us"] > 0 and 0 < s["busy_fraction"] <= 1
 
 
-@pytest.mark.parametrize("mode", ["static", "dynamic"])
+@pytest.mark.parametrize("mode", MOE_MODES)
 def test_trace_respects_every_dependency(lib, mode):
     """Read off the trace of one call: no task began before its producers signalled."""
     cfg = MID.with_(layers=2)
@@ -225,7 +230,7 @@ def test_trace_respects_every_dependency(lib, mode):
         moe_check.check_trace_causality(bad, *args)
 
 
-@pytest.mark.parametrize("mode", ["static", "dynamic"])
+@pytest.mark.parametrize("mode", MOE_MODES)
 def test_watchdog_ends_a_call_with_a_dropped_signal(lib, mode):
     """A counter that can never reach its target (planted in the workspace, on the CPU):
     the wait on it gives up after its patience (5 s without progress), the call reports
@@ -244,8 +249,10 @@ def test_watchdog_ends_a_call_with_a_dropped_signal(lib, mode):
     assert res.returncode == 0, res.stderr[-2000:]
     r = json.loads(res.stdout.strip().splitlines()[-1])
     assert r["status"] == 5, r  # ETC_ERR_TIMEOUT
-    # static: the finalize task's wait on ev_comb (site 23); dynamic: a queue-slot wait (2)
-    assert r["where"] == (23 if mode == "static" else 2), r
+    # static: the finalize task's wait on ev_comb (site 23); dynamic: a queue-slot wait (2);
+    # dedicated: the scheduler (40) or a worker waiting on its mailbox (41)
+    want = {"static": {23}, "dynamic": {2}, "dedicated": {40, 41}}[mode]
+    assert r["where"] in want, r
     assert 4.0 < r["seconds"] < 120, r
     assert r["status_after_init"] == 0
     cfg = synth.CONFIGS["tiny"]

@@ -14,12 +14,14 @@ from tests.gpu_util import layers_to_device, require_gpu, run_moe, say
 pytestmark = pytest.mark.gpu
 
 # The dynamic (ready-queue) MoE scheduler is disabled on the GPU: its first GPU run did
-# not terminate and the cause is not identified; the library refuses the mode unless
-# ETC_ENABLE_DYNAMIC_SCHED=1.  It is covered on the CPU execution harness instead
-# (tests/test_cpu_emu.py).
+# not terminate and the cause is not identified; the library refuses the mode unless the
+# caller passes ETC_FLAG_ALLOW_DYNAMIC.  It is covered on the CPU execution harness
+# instead (tests/test_cpu_emu.py).
 DYN_SKIP = pytest.mark.skip(reason="dynamic MoE scheduler disabled on the GPU pending the "
                                    "cause of a non-terminating run; covered by the CPU harness")
-STATIC_ONLY = ("static",)
+# the schedulers that run on the GPU: static tickets and the dedicated scheduler workgroup
+GPU_MODES = ("static", "dedicated")
+MODES = ["static", pytest.param("dynamic", marks=DYN_SKIP), "dedicated"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -40,7 +42,7 @@ def _compare(cfg, x, layers_np, gpu):
 MID = synth.MoEConfig("mid", (300,), 512, 16, 6, 384, layers=2, zipf_s=0.5)
 
 
-@pytest.mark.parametrize("mode", ["static", pytest.param("dynamic", marks=DYN_SKIP)])
+@pytest.mark.parametrize("mode", MODES)
 def test_tiny_fp32(mode):
     cfg = synth.CONFIGS["tiny"]
     x, layers, ld, lnp = _setup(cfg, 16)
@@ -53,7 +55,8 @@ def test_tiny_fp32(mode):
 @pytest.mark.parametrize("mode,combine", [("static", "atomic"),
                                           pytest.param("dynamic", "atomic", marks=DYN_SKIP),
                                           ("static", "ordered"),
-                                          pytest.param("dynamic", "ordered", marks=DYN_SKIP)])
+                                          pytest.param("dynamic", "ordered", marks=DYN_SKIP),
+                                          ("dedicated", "atomic"), ("dedicated", "ordered")])
 def test_mid_two_layers(mode, combine):
     """300 tokens (ragged last routing tile), 16 experts (ragged row tiles), 2 layers."""
     cfg = MID
@@ -98,7 +101,7 @@ def test_token_counts_share_one_workspace(T):
     cfg = MID.with_(layers=1)
     x, layers, ld, lnp = _setup(cfg, T, call=T)
     ws = _shared_ws(cfg)
-    for mode in STATIC_ONLY:
+    for mode in GPU_MODES:
         gpu = run_moe(x.cuda(), ld, cfg.top_k, mode=mode, workspace=ws)
         _compare(cfg, x, lnp, gpu)
 
@@ -121,16 +124,17 @@ def test_zero_tokens_is_a_noop():
     assert out.shape == (0, cfg.hidden)
 
 
-@pytest.mark.parametrize("mode", ["static", pytest.param("dynamic", marks=DYN_SKIP)])
+@pytest.mark.parametrize("mode", MODES)
 def test_single_worker(mode):
-    """One workgroup runs the whole task graph alone (no deadlock in either mode)."""
+    """One workgroup runs the whole task graph alone (no deadlock in any mode); in
+    dedicated mode one worker beside the scheduler workgroup."""
     cfg = MID.with_(layers=2)
     x, layers, ld, lnp = _setup(cfg, 40, call=7)
-    gpu = run_moe(x.cuda(), ld, cfg.top_k, mode=mode, workers=1)
+    gpu = run_moe(x.cuda(), ld, cfg.top_k, mode=mode, workers=2 if mode == "dedicated" else 1)
     _compare(cfg, x, lnp, gpu)
 
 
-@pytest.mark.parametrize("mode", ["static", pytest.param("dynamic", marks=DYN_SKIP)])
+@pytest.mark.parametrize("mode", MODES)
 def test_event_tensor_final_state(mode):
     """With the counters kept, every counter of the event tensor ends exactly at the
     value the scheduler model derives from the GPU's own routing and split."""
@@ -157,8 +161,9 @@ def _trace_check(cfg, T, ws, gpu):
                                            gpu, ws.layout, read, cfg.layers)
 
 
+@pytest.mark.parametrize("mode", GPU_MODES)
 @pytest.mark.parametrize("which", ["mid", "decode"])
-def test_trace_respects_every_dependency(which):
+def test_trace_respects_every_dependency(which, mode):
     """On the device clock (a trace of one call): every task of the scheduler model ran
     exactly once, and none began before every task whose signals it waits for had
     signalled -- the event tensor's true dependencies hold on the hardware."""
@@ -166,8 +171,8 @@ def test_trace_respects_every_dependency(which):
     x, layers, ld, lnp = _setup(cfg, T, call=13)
     ws = binding.MoEWorkspace(T, cfg.hidden, cfg.experts, cfg.top_k, cfg.ffn, cfg.layers,
                               torch.bfloat16)
-    say(f"trace {which} T={T}")
-    gpu = run_moe(x.cuda(), ld, cfg.top_k, mode="static", workspace=ws, flags=binding.FLAG_TRACE)
+    say(f"trace {which} T={T} mode={mode}")
+    gpu = run_moe(x.cuda(), ld, cfg.top_k, mode=mode, workspace=ws, flags=binding.FLAG_TRACE)
     _compare(cfg, x, lnp, gpu)
     checked = _trace_check(cfg, T, ws, gpu)
     say(f"{checked} dependencies checked")
@@ -226,10 +231,10 @@ def test_decode_sequence_one_kernel():
     seq = [64, 1, 16, 4]  # every size once, largest first
     for i, T in enumerate(seq):
         x = synth.make_x(cfg, T, call=i)
-        mode = "static"
-        say(f"decode T={T} mode={mode}")
-        gpu = run_moe(x.cuda(), ld, cfg.top_k, mode=mode, workspace=ws)
-        say(_compare(cfg, x, lnp, gpu))
+        for mode in GPU_MODES:
+            say(f"decode T={T} mode={mode}")
+            gpu = run_moe(x.cuda(), ld, cfg.top_k, mode=mode, workspace=ws)
+            say(_compare(cfg, x, lnp, gpu))
 
 
 @pytest.mark.timeout(400)
@@ -257,7 +262,7 @@ def test_decode_32_calls_drawn_token_counts():
 def test_finegrained_zipf():
     cfg = synth.CONFIGS["finegrained"]
     x, layers, ld, lnp = _setup(cfg, 256)
-    for mode in STATIC_ONLY:
+    for mode in GPU_MODES:
         say(f"finegrained mode={mode}")
         gpu = run_moe(x.cuda(), ld, cfg.top_k, mode=mode)
         say(_compare(cfg, x, lnp, gpu))
@@ -273,7 +278,7 @@ def test_prefill_two_layers():
     cfg = synth.CONFIGS["prefill"]
     say("prefill: drawing inputs")
     x, layers, ld, lnp = _setup(cfg, 4096)
-    for mode in STATIC_ONLY:
+    for mode in GPU_MODES:
         say(f"prefill mode={mode}")
         gpu = run_moe(x.cuda(), ld, cfg.top_k, mode=mode)
         say(_compare(cfg, x, lnp, gpu))
