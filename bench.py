@@ -1,7 +1,7 @@
 """Throughput of the persistent event-tensor MoE kernel on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
-                    [--mode dynamic|static] [--combine atomic|ordered]
+                    [--mode static|dedicated] [--combine atomic|ordered]
                     [--secondary | --no-secondary] [--no-cpu-baseline]
 
 A step is one call of the library on one batch of synthetic input already resident in
@@ -300,7 +300,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill", choices=sorted(synth.CONFIGS))
     ap.add_argument("--tokens", type=int, default=0, help="override T (decode: 1/4/16/64)")
-    ap.add_argument("--mode", default="static", choices=["static", "dynamic"])
+    ap.add_argument("--mode", default="static", choices=["static", "dedicated"])
     ap.add_argument("--combine", default="atomic", choices=["atomic", "ordered"])
     ap.add_argument("--secondary", dest="secondary", action="store_true", default=True)
     ap.add_argument("--no-secondary", dest="secondary", action="store_false")
@@ -368,6 +368,15 @@ def main():
                        args.combine)
         secondary["finegrained_T256"] = {k: fg[k] for k in ("tokens_per_s", "launch_ms", "gbs_alg",
                                                            "hbm_frac", "experts_touched")}
+        # the other GPU scheduler of the MoE layer on the same workloads
+        other = "dedicated" if args.mode == "static" else "static"
+        sched = {}
+        for name, c, t in (("decode_T1", dec, 1), ("decode_T64", dec, 64),
+                           ("finegrained_T256", synth.CONFIGS["finegrained"], 256),
+                           (f"{cfg.name}_T{T}", cfg, T)):
+            r = bench_moe(c, t, max(5, args.steps // 2), 2, other, args.combine)
+            sched[name] = {k: r[k] for k in ("tokens_per_s", "launch_ms")}
+        secondary[f"moe_{other}"] = sched
         for m in ("static", "dynamic"):  # split-K's dynamic mode is a last-arriver reduction
             sk = bench_splitk(max(5, args.steps // 2), 2, m)
             secondary[f"splitk_{m}"] = {k: sk[k] for k in ("launch_ms", "gbs_alg", "hbm_frac")}

@@ -57,9 +57,10 @@ typedef enum { ETC_DTYPE_F32 = 0, ETC_DTYPE_BF16 = 1 } etc_dtype;
  * regular work, dynamic pays off under irregularity such as MoE routing; chapter §5.5
  * Obstacle 3: online balancing through atomics.)  Dedicated (etc_moe_layer only):
  * workgroup 0 is a scheduler that watches the event counters of a window of the
- * static order and hands ready tasks to per-worker mailboxes; workers never wait on a
- * counter (chapter, Q&A on the Cluster Launch Control: MPK's scheduler units feeding
- * worker queues).  Needs at least two workgroups. */
+ * static order and hands ready tasks to two-slot mailboxes of the other workgroups,
+ * preferring the XCD static mode would use; workers never wait on a counter (chapter,
+ * Q&A on the Cluster Launch Control: MPK's scheduler units feeding worker queues).
+ * Needs at least two workgroups; uses at most 257 (the scheduler tracks 256 workers). */
 typedef enum { ETC_SCHED_STATIC = 0, ETC_SCHED_DYNAMIC = 1, ETC_SCHED_DEDICATED = 2 } etc_sched_mode;
 
 /* Atomic: the down-projection tiles add gate * y straight into a float32 accumulator

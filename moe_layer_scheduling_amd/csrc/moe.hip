@@ -1347,30 +1347,55 @@ ETC_DEV void run_task(KArgs& p, KLayer& L, const Task& t, Smem& sm) {
 // Mode ETC_SCHED_DEDICATED: workgroup 0 schedules and the others work, after the runtime
 // the tutorial chapter "5 · Event Tensor et le dynamisme" describes for MPK (Q&A on the
 // Cluster Launch Control): scheduler units watch the events and hand ready tasks to
-// worker queues.  Worker w owns mailbox w (a 64-bit word in the workspace): it posts the
-// idle word when it starts and after every task, and otherwise waits on its own mailbox
-// only; a task word there is a task whose inputs are complete, which it runs and signals
-// as in static mode.  The scheduler is one wavefront.  It walks the static topological
-// order with a window of 64 tickets, one per lane: each lane decodes its ticket (once the
-// ticket's layer has published its plan) and reads the one counter the task waits on;
-// ready tickets go to idle workers in ticket order.  Every ticket before the window is
+// worker queues.  Workers never wait on a counter.
+//
+// Worker w owns a two-slot mailbox (words 2w and 2w+1 of the queue region) and takes its
+// slots in turn.  It posts the idle word in slot 0 when it starts; then it waits on its
+// current slot for a task word, runs the task, signals its counters as in static mode,
+// writes the idle word back into the slot and moves to the other slot.  A slot is empty
+// when it holds 0 or the idle word.  With two slots the scheduler can queue a ready task
+// behind the one a worker is running, so the worker starts it without a round trip
+// through the scheduler.
+//
+// The scheduler is one wavefront.  It walks the static topological order with a window
+// of 64 tickets, one per lane: each lane decodes its ticket (once the ticket's layer has
+// published its plan) and reads the one counter the task waits on.  Ready tickets go
+// out in ticket order, each preferring the XCD that static mode would run it on (chunks
+// of workers/8 consecutive tickets per XCD, workgroup w on XCD w mod 8, so tasks that
+// share a weight tile meet in one L2): first to idle workers of that XCD, then behind a
+// running task there, then to idle workers elsewhere.  Every ticket before the window is
 // assigned, so the producers of the window's first ticket are all assigned and it
 // becomes ready as they finish: the scheduler keeps making progress.  Only workers that
 // have posted the idle word receive tasks, so a workgroup that is not resident yet holds
 // none.  Once every ticket is assigned and every worker is idle it writes the exit word
-// to every mailbox; a worker empties its mailbox (0) as it leaves.  Workers never wait
-// on a counter.
+// into each worker's current slot; a worker empties both slots as it leaves.  All the
+// mailbox and counter reads of one pass are issued before any is used: one memory round
+// trip per pass.
 
 constexpr int K_EXIT = 15;  // mailbox word: leave the task loop
 constexpr int K_IDLE = 14;  // mailbox word: the worker waits for a task
+constexpr int NXCD = 8;
+// The scheduler lane l tracks workers 1 + l + 64 j (j < DED_PER_LANE) in registers; all
+// of them sit on XCD (1 + l) mod 8.
+constexpr int DED_PER_LANE = 4;
+constexpr int DED_MAX_GRID = 1 + DED_PER_LANE * WAVE;
+
+// Per-XCD counts of one scheduler pass.
+struct SchedTable {
+  unsigned long long ready[NXCD];  // ready tickets preferring x (bit i: i-th ticket in order)
+  unsigned long long third[NXCD];  // of those, the ones queued behind a running task
+  int n_idle[NXCD], n_b1[NXCD];    // idle workers and workers holding one task on x
+  int take[NXCD];                  // idle workers of x that x's own tickets take
+  int pool0[NXCD];                 // first pool entry of x's left-over idle workers
+  int pool_total;
+};
 
 struct SchedSmem {
+  SchedTable tab;
   int planned;                  // bit l: layer l's plan and row-tile bases are cached
   int base[MAXL + 1];           // first ticket of each layer (-1: not known yet)
   int plan[MAXL][PL_WORDS];
   int rtb[MAXL][MAXE + 1];
-  int busy[MAX_WORKERS];        // 1: the worker holds a task
-  int freelist[MAX_WORKERS];
   int word;                     // lane 0's reading, for the whole wave
 };
 static_assert(sizeof(SchedSmem) <= sizeof(SmemU), "the scheduler's state fits the task area");
@@ -1410,117 +1435,273 @@ ETC_DEV int sched_decode(KArgs& p, const SchedSmem& S, int c, Task& t) {
   return 2;
 }
 
-// Whether the task's inputs are complete: the counter it waits on has reached its target
-// (one relaxed load; the worker that receives the task acquires through its mailbox).
-ETC_DEV bool sched_ready(KArgs& p, const SchedSmem& S, const Task& t) {
+// The counter the task waits on and its target (the same waits as static mode); null
+// when the task waits on nothing.
+ETC_DEV const int* sched_dep(KArgs& p, const SchedSmem& S, const Task& t, int& target) {
   KLayer& L = p.layer[t.layer];
   switch (t.kind) {
     case K_R:
-      return t.layer == 0 || ev_load_relaxed(p.layer[t.layer - 1].ev_done + t.a) >= 1;
+      target = 1;
+      return t.layer == 0 ? nullptr : p.layer[t.layer - 1].ev_done + t.a;
     case K_P:
-      return ev_load_relaxed(L.ev_scan) >= 1;
+      target = 1;
+      return L.ev_scan;
     case K_GU:
-      return ev_load_relaxed(L.ev_perm) >= p.n_rt;
+      target = p.n_rt;
+      return L.ev_perm;
     case K_D: {
       const int gpc = S.plan[t.layer][PL_GPC];
-      const int rt = S.rtb[t.layer][t.a] + t.b;
-      return ev_load_relaxed(L.ev_gu + rt * p.n1 + t.d) >= min(gpc, p.n1 - t.d * gpc);
+      target = min(gpc, p.n1 - t.d * gpc);
+      return L.ev_gu + (S.rtb[t.layer][t.a] + t.b) * p.n1 + t.d;
     }
     case K_F:
-      return ev_load_relaxed(L.ev_comb + t.a) >=
-             tile_rows(p, t.a) * p.K * p.n2 * S.plan[t.layer][PL_NS];
+      target = tile_rows(p, t.a) * p.K * p.n2 * S.plan[t.layer][PL_NS];
+      return L.ev_comb + t.a;
     default:
-      return false;
+      target = 0;
+      return nullptr;
   }
+}
+
+ETC_DEV bool slot_empty(long long v) { return v == 0 || v == K_IDLE; }
+ETC_DEV unsigned long long lanes_below(int lane) { return (1ull << lane) - 1ull; }
+// lanes whose workers sit on XCD x: (1 + l) mod 8 == x
+ETC_DEV unsigned long long xcd_lanes(int x) { return 0x0101010101010101ull << ((x + NXCD - 1) % NXCD); }
+ETC_DEV unsigned long long rot_right(unsigned long long m, int s) { return s ? (m >> s) | (m << (64 - s)) : m; }
+// position of the r-th set bit (r counted from 0; the mask has more than r set bits)
+ETC_DEV int nth_bit(unsigned long long m, int r) {
+  int pos = 0;
+  for (int width = 32; width >= 1; width >>= 1) {
+    const unsigned long long low = m & ((1ull << width) - 1ull);
+    const int c = __popcll(low);
+    if (r >= c) { r -= c; m >>= width; pos += width; } else { m = low; }
+  }
+  return pos;
+}
+// The r-th worker (lane-major within each group of 64, groups in order) among the
+// per-group masks restricted to the lanes of XCD x.
+ETC_DEV int nth_worker(const unsigned long long (&m)[DED_PER_LANE], unsigned long long xl, int r) {
+  int w = -1;
+#pragma unroll
+  for (int j = 0; j < DED_PER_LANE; ++j) {
+    const unsigned long long mj = m[j] & xl;
+    const int c = __popcll(mj);
+    if (w < 0 && r < c) w = 1 + nth_bit(mj, r) + WAVE * j;
+    if (w < 0) r -= c;
+  }
+  return w;
 }
 
 // The scheduler: every lane of wave 0 of workgroup 0.  Returns when every worker has been
 // sent the exit word, or when the call is aborted.
+//
+// Lane l holds the window's ticket c with c = l (mod 64), so a ticket keeps its lane
+// until it is assigned and only tickets that enter the window are decoded.  Assignment,
+// in ticket order: (1) the idle workers of the ticket's XCD; (2) idle workers of other
+// XCDs (XCD by XCD); (3) behind the task of a worker of its XCD that holds one.  Each
+// lane also owns the state of its workers (tasks held, oldest slot) and works out from
+// the same wave-wide counts whether one of them was given a task.
 ETC_DEV void run_scheduler(KArgs& p, Smem& sm) {
   SchedSmem& S = *reinterpret_cast<SchedSmem*>(&sm.u);
   const int lane = threadIdx.x & 63;
-  const int W = (int)gridDim.x;  // mailboxes 1 .. W-1
-  for (int w = lane; w < W; w += WAVE) S.busy[w] = 1;  // not idle until it says so
+  const int W = (int)gridDim.x;    // workers 1 .. W-1
+  const int G = max(1, W / NXCD);  // tickets per chunk of one XCD
+  const int my_x = (1 + lane) % NXCD;
+  const unsigned long long my_xl = xcd_lanes(my_x);
   if (lane <= MAXL) S.base[lane] = lane == 0 ? 0 : -1;
   if (lane == 0) S.planned = 0;
   __builtin_amdgcn_wave_barrier();
-  int next = 0;                // lowest ticket not yet assigned
-  unsigned long long amask = 0;  // bit i: ticket next + i is assigned
+  int o[DED_PER_LANE], h[DED_PER_LANE];  // tasks held (-1: not started), oldest slot
+#pragma unroll
+  for (int j = 0; j < DED_PER_LANE; ++j) { o[j] = -1; h[j] = 0; }
+  int next = 0;  // lowest ticket not yet assigned
+  int c = lane;  // this lane's ticket
+  bool assigned = false;
+  Task t;
+  int st = 1;  // sched_decode's result for c
+  const int* dep = nullptr;
+  int target = 0;
   Watchdog wd;
   for (int it = 0;; ++it) {
-    // plans published by the layers' scans: copy each one once
-    for (int l = 0; l < p.L; ++l) {
-      if ((S.planned >> l & 1) || S.base[l] < 0) continue;
-      KLayer& L = p.layer[l];
-      // lane 0 reads the event (acquire once complete: the plan and bases written before it)
-      if (lane == 0) S.word = ev_load_relaxed(L.ev_scan) >= 1 && ev_load(L.ev_scan) >= 1;
-      __builtin_amdgcn_wave_barrier();
-      const int scanned = S.word;
-      __builtin_amdgcn_wave_barrier();
-      if (!scanned) continue;
-      if (lane < PL_WORDS) S.plan[l][lane] = gp(L.plan)[lane];
-      for (int e = lane; e <= p.E; e += WAVE) S.rtb[l][e] = gp(L.rt_base)[e];
+    // ---- every read of the pass is issued before any is used
+    int pend = -1;  // the layer whose plan is awaited (at most one)
+    for (int l = 0; l < p.L; ++l)
+      if (pend < 0 && S.base[l] >= 0 && !(S.planned >> l & 1)) pend = l;
+    if (st == 1) {
+      st = sched_decode(p, S, c, t);
+      dep = st == 0 ? sched_dep(p, S, t, target) : nullptr;
+    }
+    // (every lane reads, without a branch, so the wait for it lands with the others)
+    const int scan_v = ev_load_relaxed(pend >= 0 ? p.layer[pend].ev_scan : p.sched + W_QHEAD);
+    const int dep_v = (st == 0 && !assigned && dep) ? ev_load_relaxed(dep) : 0;
+    // (the low word of a slot tells empty, idle and task words apart: a task word's
+    // low four bits are its kind, 1 to 6)
+    int b0[DED_PER_LANE], b1[DED_PER_LANE];
+#pragma unroll
+    for (int j = 0; j < DED_PER_LANE; ++j) {
+      const int w = 1 + lane + WAVE * j;
+      const int* slots = reinterpret_cast<const int*>(p.queue + 2 * w);
+      b0[j] = (w < W && o[j] != 0) ? ev_load_relaxed(slots + 2 * h[j]) : 0;
+      b1[j] = (w < W && o[j] == 2) ? ev_load_relaxed(slots + 2 * (h[j] ^ 1)) : 0;
+    }
+    // ---- worker states: started, finished tasks
+    unsigned long long I[DED_PER_LANE], B1[DED_PER_LANE], Hm[DED_PER_LANE];
+#pragma unroll
+    for (int j = 0; j < DED_PER_LANE; ++j) {
+      const bool valid = 1 + lane + WAVE * j < W;
+      const bool start = valid && o[j] < 0 && b0[j] == K_IDLE;
+      const bool fin1 = valid && o[j] > 0 && (b0[j] == 0 || b0[j] == K_IDLE);
+      const bool fin2 = fin1 && o[j] == 2 && (b1[j] == 0 || b1[j] == K_IDLE);
+      o[j] = start ? 0 : o[j] - (int)fin1 - (int)fin2;
+      h[j] ^= (int)fin1 ^ (int)fin2;
+      I[j] = __ballot(valid && o[j] == 0);
+      B1[j] = __ballot(valid && o[j] == 1);
+      Hm[j] = __ballot(h[j] != 0);
+    }
+    int nidle = 0, started = 0;
+#pragma unroll
+    for (int j = 0; j < DED_PER_LANE; ++j) {
+      nidle += __popcll(I[j]);
+      started += __popcll(__ballot(1 + lane + WAVE * j < W && o[j] >= 0));
+    }
+
+    // ---- the plan of the awaited layer, once its scan has completed
+    if (lane == 0) S.word = pend >= 0 && scan_v >= 1 && ev_load(p.layer[pend].ev_scan) >= 1;  // acquire
+    __builtin_amdgcn_wave_barrier();
+    if (S.word) {
+      KLayer& L = p.layer[pend];
+      if (lane < PL_WORDS) S.plan[pend][lane] = gp(L.plan)[lane];
+      for (int e = lane; e <= p.E; e += WAVE) S.rtb[pend][e] = gp(L.rt_base)[e];
       __builtin_amdgcn_wave_barrier();
       if (lane == 0) {
-        S.base[l + 1] = S.plan[l][PL_NEXTBASE];
-        S.planned |= 1 << l;
-      }
-      __builtin_amdgcn_wave_barrier();
-    }
-    const int total = S.base[p.L];  // -1 until every layer has planned
-
-    // workers that have posted the idle word; the idle ones in order (the mailboxes of
-    // four groups of 64 workers are read before any is looked at)
-    int nfree = 0;
-    for (int w0 = 1; w0 < W; w0 += 4 * WAVE) {
-      long long box[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int w = w0 + j * WAVE + lane;
-        box[j] = (w < W && S.busy[w]) ? q_load_relaxed(p.queue + w) : (long long)K_IDLE;
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int w = w0 + j * WAVE + lane;
-        const bool idle = w < W && box[j] == K_IDLE;
-        if (idle) S.busy[w] = 0;
-        const unsigned long long m = __ballot(idle);
-        if (idle) S.freelist[nfree + __popcll(m & ((1ull << lane) - 1ull))] = w;
-        nfree += __popcll(m);
+        S.base[pend + 1] = S.plan[pend][PL_NEXTBASE];
+        S.planned |= 1 << pend;
       }
     }
     __builtin_amdgcn_wave_barrier();
 
-    // the window's ready tickets go to idle workers, in ticket order
-    const int c = next + lane;
-    Task t;
-    const int st = sched_decode(p, S, c, t);
-    const bool ready = st == 0 && !((amask >> lane) & 1ull) && sched_ready(p, S, t);
-    const unsigned long long rmask = __ballot(ready);
-    const int rank = __popcll(rmask & ((1ull << lane) - 1ull));
-    const bool give = ready && rank < nfree;
-    if (give) {
-      // the task's inputs reached the point of coherence before the counter did; the
-      // worker acquires its mailbox before reading them
-      const int w = S.freelist[rank];
-      S.busy[w] = 1;
-      q_store_relaxed(p.queue + w, enc(t));
+    // ---- ready tickets to workers.  Wave-wide counts per XCD go to a small LDS table
+    // that each lane reads at its ticket's XCD and at its workers' XCD.
+    const bool ready = st == 0 && !assigned && (dep == nullptr || dep_v >= target);
+    const int xp = (c / G) % NXCD;
+    const int sh = next & 63;  // lane of the lowest ticket
+    const unsigned long long before = lanes_below((lane - sh) & 63);  // earlier tickets
+    SchedTable& X = S.tab;
+    {
+      int pool = 0;
+#pragma unroll
+      for (int x = 0; x < NXCD; ++x) {
+        const unsigned long long xl = xcd_lanes(x);
+        const unsigned long long R = rot_right(__ballot(ready && xp == x), sh);
+        int ni = 0, nb = 0;
+#pragma unroll
+        for (int j = 0; j < DED_PER_LANE; ++j) { ni += __popcll(I[j] & xl); nb += __popcll(B1[j] & xl); }
+        const int take = min(__popcll(R), ni);
+        if (lane == x) {
+          X.ready[x] = R; X.n_idle[x] = ni; X.n_b1[x] = nb; X.take[x] = take; X.pool0[x] = pool;
+        }
+        pool += ni - take;  // idle workers of x that its own tickets leave
+      }
+      if (lane == 0) X.pool_total = pool;
     }
-    const unsigned long long gmask = __ballot(give);
+    __builtin_amdgcn_wave_barrier();
+    const int rank = __popcll(X.ready[xp] & before);
+    const int t_nidle = X.n_idle[xp], t_take = X.take[xp];
+    const int pool_total = X.pool_total;
+    // (1) an idle worker of its own XCD; (2) an idle worker elsewhere: entry srank of the
+    // pool, XCD by XCD
+    const bool spill = ready && rank >= t_nidle;
+    const unsigned long long SP = rot_right(__ballot(spill), sh);
+    const int srank = __popcll(SP & before);
+    const int n2 = min(__popcll(SP), pool_total);
+    int pick_x = xp, pick_r = rank;
+    bool pick = ready && rank < t_take, pick_b1 = false;
+    if (spill && srank < pool_total) {
+      int px = 0;
+      for (int x = 1; x < NXCD; ++x)
+        if (srank >= X.pool0[x] && X.n_idle[x] > X.take[x]) px = x;
+      pick = true;
+      pick_x = px;
+      pick_r = X.take[px] + (srank - X.pool0[px]);
+    }
+    // (3) behind the one task a worker of its own XCD holds, once every worker has
+    // started (while workers are still starting, a queued task could wait behind a
+    // routing task for its whole length)
+    const bool third = spill && srank >= pool_total && started == W - 1;
+#pragma unroll
+    for (int x = 0; x < NXCD; ++x) {
+      const unsigned long long Q = rot_right(__ballot(third && xp == x), sh);
+      if (lane == x) X.third[x] = Q;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (third) {
+      const int q = __popcll(X.third[xp] & before);
+      if (q < X.n_b1[xp]) { pick = true; pick_b1 = true; pick_r = q; }
+    }
+    int w_to = -1;
+    if (pick) {
+      unsigned long long m[DED_PER_LANE];
+#pragma unroll
+      for (int j = 0; j < DED_PER_LANE; ++j) m[j] = pick_b1 ? B1[j] : I[j];
+      w_to = nth_worker(m, xcd_lanes(pick_x), pick_r);
+      // the slot after the worker's current task (idle: its current slot); the task's
+      // inputs reached the point of coherence before the counter did, and the worker
+      // acquires its slot before reading them
+      const int jw = (w_to - 1) / WAVE, lw = (w_to - 1) % WAVE;
+      unsigned long long hm = Hm[0];
+#pragma unroll
+      for (int j = 1; j < DED_PER_LANE; ++j)
+        if (jw == j) hm = Hm[j];
+      const int slot = (int)((hm >> lw) & 1ull) ^ (pick_b1 ? 1 : 0);
+      q_store_relaxed(p.queue + 2 * w_to + slot, enc(t));
+    }
+    // this lane's workers that were given a task: its rank among the idle (or one-task)
+    // workers of its XCD decides, with the counts every lane saw
+    {
+      const int o_take = X.take[my_x], o_pool0 = X.pool0[my_x];
+      const int o_n3 = min(__popcll(X.third[my_x]), X.n_b1[my_x]);
+      int ri = 0, rb = 0;
+#pragma unroll
+      for (int j = 0; j < DED_PER_LANE; ++j) {
+        const unsigned long long mi = I[j] & my_xl, mb = B1[j] & my_xl;
+        const int myri = ri + __popcll(mi & lanes_below(lane));
+        const int myrb = rb + __popcll(mb & lanes_below(lane));
+        const int w = 1 + lane + WAVE * j;
+        if (w < W && o[j] == 0) {
+          if (myri < o_take || o_pool0 + (myri - o_take) < n2) o[j] = 1;
+        } else if (w < W && o[j] == 1) {
+          if (myrb < o_n3) o[j] = 2;
+        }
+        ri += __popcll(mi);
+        rb += __popcll(mb);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+    const unsigned long long gmask = __ballot(w_to >= 0);
     if (gmask && lane == 0) ev_add_relaxed(p.sched + W_QHEAD, 1);  // progress seen by idle workers
-    amask |= gmask;
-    // slide the window past its assigned prefix
-    const int done = amask == ~0ull ? 64 : __builtin_ctzll(~amask);
+    if (w_to >= 0) assigned = true;
+    // slide the window past its assigned prefix; the lanes it passes take the tickets
+    // that enter it
+    const unsigned long long A = rot_right(__ballot(assigned), sh);
+    const int done = A == ~0ull ? 64 : __builtin_ctzll(~A);
     next += done;
-    amask = done == 64 ? 0ull : (amask >> done);
+    if (assigned && c < next) {
+      c += WAVE;
+      assigned = false;
+      st = 1;
+    }
 
-    const int idle_now = nfree - __popcll(gmask);
-    if (total >= 0 && next >= total && idle_now == W - 1) {
-      for (int w = 1 + lane; w < W; w += WAVE) q_store_relaxed(p.queue + w, (long long)K_EXIT);
+    const int total = S.base[p.L];  // -1 until every layer has planned
+    if (total >= 0 && next >= total && nidle == W - 1 && gmask == 0) {
+#pragma unroll
+      for (int j = 0; j < DED_PER_LANE; ++j) {
+        const int w = 1 + lane + WAVE * j;
+        if (w < W) q_store_relaxed(p.queue + 2 * w + h[j], (long long)K_EXIT);
+      }
       return;
     }
     // the watchdog (lane 0) counts a new ticket assigned or a worker finishing as progress
-    const int seen = next * 4099 + idle_now;
+    const int seen = next * 4099 + nidle;
     if (it == 0) {
       if (lane == 0) wd.start(p.timeout_ticks, seen);
     } else if (it % WATCH_EVERY == 0) {
@@ -1530,20 +1711,21 @@ ETC_DEV void run_scheduler(KArgs& p, Smem& sm) {
       __builtin_amdgcn_wave_barrier();
       if (stop) return;
     }
-    __builtin_amdgcn_s_sleep(1);
   }
 }
 
-// A worker's wait for its mailbox (thread 0).  Returns false if the call was aborted.
-ETC_DEV bool claim_mailbox(KArgs& p, Task& t) {
-  long long* box = p.queue + blockIdx.x;
+// A worker's wait on its current mailbox slot (thread 0).  Returns false if the call was
+// aborted.
+ETC_DEV bool claim_mailbox(KArgs& p, Task& t, int slot) {
+  long long* box = p.queue + 2 * blockIdx.x + slot;
   Watchdog wd;
   for (int it = 0;; ++it) {
-    const long long w = q_load_relaxed(box);
-    if (w != K_IDLE && w != 0) {
+    if (!slot_empty(q_load_relaxed(box))) {
       const long long v = q_load(box);  // acquire: the task's inputs are complete
       if ((v & 15) == K_EXIT) {
-        q_store_relaxed(box, 0);  // the mailbox is empty for the next call
+        // both slots empty for the next call
+        q_store_relaxed(p.queue + 2 * blockIdx.x, 0);
+        q_store_relaxed(p.queue + 2 * blockIdx.x + 1, 0);
         t.kind = K_NONE;
       } else {
         t = dec(v);
@@ -1585,7 +1767,8 @@ __global__ __launch_bounds__(MNT) void moe_kernel(Args pk) {
     for (int l = 0; l <= MAXL; ++l) sm.lbase[l] = -1;
   }
   const bool dedicated = p.mode == ETC_SCHED_DEDICATED;
-  if (dedicated && blockIdx.x != 0 && tid == 0) q_store_relaxed(p.queue + blockIdx.x, K_IDLE);
+  int mslot = 0;  // dedicated mode: the worker's current mailbox slot (thread 0)
+  if (dedicated && blockIdx.x != 0 && tid == 0) q_store_relaxed(p.queue + 2 * blockIdx.x, K_IDLE);
   if (dedicated && blockIdx.x == 0) {
     // the scheduler workgroup: wave 0 schedules, the other waves wait at the exit
     if (tid < WAVE) run_scheduler(p, sm);
@@ -1599,7 +1782,7 @@ __global__ __launch_bounds__(MNT) void moe_kernel(Args pk) {
       t.kind = K_NONE; t.layer = 0; t.a = t.b = t.c = t.d = 0;
       const bool ok = (p.mode == ETC_SCHED_STATIC)    ? claim_static(p, t, sm)
                       : (p.mode == ETC_SCHED_DYNAMIC) ? claim_dynamic(p, t)
-                                                      : claim_mailbox(p, t);
+                                                      : claim_mailbox(p, t, mslot);
       if (!ok) t.kind = K_NONE;
       const bool gemm_or_f = t.kind == K_GU || t.kind == K_D || t.kind == K_F;
       sm.need_cache = (gemm_or_f && sm.lc.layer != t.layer) ? 1 : 0;
@@ -1630,7 +1813,10 @@ __global__ __launch_bounds__(MNT) void moe_kernel(Args pk) {
     if (tracing && tid == 0) trace_record(p, t, t_claim, t_run, now_ticks());
     // dedicated mode: the task's signals have gone out (run_task ends at a barrier after
     // them); the worker is idle again
-    if (dedicated && tid == 0) q_store_relaxed(p.queue + blockIdx.x, K_IDLE);
+    if (dedicated && tid == 0) {
+      q_store_relaxed(p.queue + 2 * blockIdx.x + mslot, K_IDLE);
+      mslot ^= 1;
+    }
   }
 
   // the last workgroup out clears the event counters and control words
@@ -1640,7 +1826,7 @@ __global__ __launch_bounds__(MNT) void moe_kernel(Args pk) {
   // dedicated mode: empty mailboxes for the next call (an aborted call can leave task
   // words behind)
   if (sm.flag && dedicated)
-    for (int i = tid; i < (int)gridDim.x; i += MNT) q_store_relaxed(p.queue + i, 0);
+    for (int i = tid; i < 2 * (int)gridDim.x; i += MNT) q_store_relaxed(p.queue + i, 0);
   if (sm.flag && !(p.flags & ETC_FLAG_KEEP_COUNTERS)) {
     for (int l = 0; l < p.L; ++l) {
       KLayer& L = p.layer[l];
@@ -1693,7 +1879,7 @@ inline Layout layout(int Tm, int H, int E, int K, int F, int nl, int es, bool or
   const long per_layer = (long)Y.n_rt * 4 + (long)Y.max_rt * Y.n1 + 2L * MAX_WORKERS +
                          (long)Y.max_rt * Y.n2 + 64;
   // + room for the one extra slot each worker draws before it sees the end
-  Y.queue_len = (int)(Y.n_rt + per_layer * nl + MAX_WORKERS);
+  Y.queue_len = (int)(Y.n_rt + per_layer * nl + 2 * MAX_WORKERS);  // dedicated: two slots per worker
   Y.queue = c.take((size_t)Y.queue_len * sizeof(long long));
   Y.trace = c.take((size_t)Y.queue_len * 32);  // one record per task at most
   for (int l = 0; l < nl; ++l) {
@@ -1844,7 +2030,9 @@ ETC_API etc_status etc_moe_layer(int32_t T, int32_t H, int32_t E, int32_t K, int
   p.timeout_ticks = 500000000ull;  // 5 s without progress, on the 100 MHz real-time clock
   int grid = host::grid_size(workers, host::device_cus(dev), moe_occupancy(dev, dtype));
   if (grid > moe::MAX_WORKERS) grid = moe::MAX_WORKERS;
-  if (mode == ETC_SCHED_DEDICATED && grid < 2) return ETC_ERR_INVALID_ARG;  // a scheduler and a worker
+  // dedicated: a scheduler and at least one worker; the scheduler tracks up to 256 workers
+  if (mode == ETC_SCHED_DEDICATED && grid > moe::DED_MAX_GRID) grid = moe::DED_MAX_GRID;
+  if (mode == ETC_SCHED_DEDICATED && grid < 2) return ETC_ERR_INVALID_ARG;
   p.workers = grid;
   p.xq = ws + Y.xq;
   p.hbuf = ws + Y.hbuf;

@@ -20,6 +20,8 @@ def build(out=None, sanitize=None, opt="-O1"):
            "-o", out, "-lpthread"]
     if sanitize:
         cmd[1:1] = [f"-fsanitize={sanitize}", "-fno-omit-frame-pointer"]
+    if sanitize == "thread":  # atomics carry the ordering the GPU's completion waits give
+        cmd[1:1] = ["-DETC_EMU_SC_ATOMICS"]
     subprocess.run(cmd, check=True, capture_output=True, text=True)
     return out
 

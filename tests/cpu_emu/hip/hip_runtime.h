@@ -169,9 +169,20 @@ inline float atomicAdd(float* p, float v) {
 // host memory has one address space
 #define ETC_GLOBAL
 #define ETC_LDS
-#define __hip_atomic_load(p, order, scope) __atomic_load_n((p), (order))
-#define __hip_atomic_store(p, v, order, scope) __atomic_store_n((p), (v), (order))
-#define __hip_atomic_fetch_add(p, v, order, scope) __atomic_fetch_add((p), (v), (order))
+// ThreadSanitizer builds treat every device-scope atomic as sequentially consistent.  On
+// the GPU a signal is a relaxed atomic issued after the workgroup's shared stores have
+// completed (publish_shared), so it orders those stores before it at the point of
+// coherence; a host memory model has no such completion wait, and only ordered atomics
+// carry the edge.  What TSan checks is then that every read of another workgroup's data
+// is ordered after the writes by some chain of atomics (a signal, a mailbox word).
+#ifdef ETC_EMU_SC_ATOMICS
+#define EMU_ORDER(order) __ATOMIC_SEQ_CST
+#else
+#define EMU_ORDER(order) (order)
+#endif
+#define __hip_atomic_load(p, order, scope) __atomic_load_n((p), EMU_ORDER(order))
+#define __hip_atomic_store(p, v, order, scope) __atomic_store_n((p), (v), EMU_ORDER(order))
+#define __hip_atomic_fetch_add(p, v, order, scope) __atomic_fetch_add((p), (v), EMU_ORDER(order))
 #define __builtin_amdgcn_fence(order, scope) __atomic_thread_fence(order)
 #define __builtin_amdgcn_s_waitcnt(x) ((void)0)
 #define __builtin_amdgcn_s_sleep(x) emu_yield()
@@ -194,8 +205,8 @@ inline void emu_buffer_store16(const V& v, char* base, int off, int soff) {
   uint64_t w[2];
   memcpy(w, &v, 16);
   uint64_t* d = reinterpret_cast<uint64_t*>(base + off + soff);
-  __atomic_store_n(d, w[0], __ATOMIC_RELAXED);
-  __atomic_store_n(d + 1, w[1], __ATOMIC_RELAXED);
+  __atomic_store_n(d, w[0], EMU_ORDER(__ATOMIC_RELAXED));
+  __atomic_store_n(d + 1, w[1], EMU_ORDER(__ATOMIC_RELAXED));
 }
 #define __builtin_amdgcn_raw_buffer_store_b128(v, r, off, soff, aux) emu_buffer_store16((v), (r), (off), (soff))
 #define __builtin_amdgcn_sched_barrier(mask) ((void)0)
