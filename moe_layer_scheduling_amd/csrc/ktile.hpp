@@ -212,4 +212,120 @@ struct KTile {
   }
 };
 
+// Small-M variant: BM_ (16 or 32) x 256 output tile for row tiles with at most BM_ valid
+// rows (decode batches, cold experts).  Its A rows take 2 or 4 KiB of each stage instead
+// of 16, so four stages fit where the 128-row tile keeps three (34 or 36 KiB each, at
+// most 144 KiB): three stages of weight rows are in flight instead of two.  The same
+// LDS arena thus takes one of two layouts, chosen per task from the row count.
+//
+// Copies: tile rows 0..BM_-1 are A rows, BM_..BM_+255 B rows; thread t's copy i covers
+// tile row t/8 + 64 i (same lane-to-chunk mapping and swizzle as KTile).  Copies 0..3
+// exist in every thread; copy 4 (rows 256..) only in the first BM_/8 waves, so those
+// waves count five copies per stage and the others four.  The eight waves split the 256
+// columns, 32 each: wave w owns columns 32 w .. 32 w + 31 of every row as BM_/16 x 2
+// blocks of 16 x 16 (acc[i][j]: element r in lane l is row 16 i + 4 (l/16) + r, column
+// 32 w + 16 j + (l % 16)).  Pipeline: as KTile's, four stages deep (stage k+4 goes into
+// the slot of stage k once every wave has read it).
+template <typename TE, int BM_, int NTH = 512>
+struct KTileS {
+  static_assert(NTH == 512 && (BM_ == 16 || BM_ == 32), "8 waves, 16 or 32 rows");
+  static constexpr int BM = BM_, BN = 256;
+  static constexpr int ROWS = BM + BN;              // 272 or 288
+  static constexpr int RSTEP = NTH / 8;             // 64 tile rows per copy index
+  static constexpr int FULL = BN / RSTEP;           // copies every thread makes: 4
+  static constexpr int LOADS = FULL + 1;            // the last one in the first BM/8 waves
+  static constexpr int XWAVES = BM / 8;             // waves that make the last copy
+  static constexpr int STAGE_BYTES = ROWS * 128;
+  static constexpr int NSTAGE = 4;
+  static constexpr int LDS_BYTES = NSTAGE * STAGE_BYTES;
+  static constexpr int BK = 128 / (int)sizeof(TE);  // K per stage
+  static constexpr int MI = BM / 16;                // 16-row blocks
+  static constexpr int NJ = 2;                      // 16-column blocks per wave
+  static constexpr int WCOLS = 32;
+  static_assert(LDS_BYTES <= KTile<TE, NTH>::LDS_BYTES, "both layouts fit one arena");
+
+  ETC_DEV static int load_chunk(int tid) { return KTile<TE, NTH>::load_chunk(tid); }
+  // Tile row of copy i of thread tid (>= ROWS: the thread makes no such copy).
+  ETC_DEV static int load_row(int tid, int i) { return (tid >> 3) + RSTEP * i; }
+
+  // rowp[i]: byte pointer of tile row load_row(tid, i) at k = 0 plus load_chunk(tid) * 16
+  // (any readable address where the thread makes no copy i).  klen: a positive multiple
+  // of BK.
+  ETC_DEV static void run(char* smem, const char* const (&rowp)[LOADS], int klen,
+                          f32x4 (&acc)[MI][NJ]) {
+    static_for<MI>([&](auto i) ETC_INLINE {
+      static_for<NJ>([&](auto j) ETC_INLINE { acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f}; });
+    });
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (w < XWAVES) pipeline<LOADS>(smem, rowp, klen, acc);
+    else pipeline<FULL>(smem, rowp, klen, acc);
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0): the last copies landed
+    __syncthreads();
+  }
+
+ private:
+  struct Half {
+    u32x4 a[MI], b[NJ];
+  };
+
+  template <int NL>
+  ETC_DEV static void pipeline(char* smem, const char* const (&rowp)[LOADS], int klen,
+                               f32x4 (&acc)[MI][NJ]) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int nk = klen / BK, last = nk - 1;
+    const TE* tag = nullptr;
+    int aoff[2][MI], boff[2][NJ];
+    static_for<2>([&](auto kk) ETC_INLINE {
+      const int c = kk * 4 + (lane >> 4);
+      static_for<MI>([&](auto i) ETC_INLINE { aoff[kk][i] = swz(i * 16 + (lane & 15), c); });
+      static_for<NJ>([&](auto j) ETC_INLINE { boff[kk][j] = swz(BM + w * WCOLS + j * 16 + (lane & 15), c); });
+    });
+    auto prep = [&](int kt, const char* (&src)[NL], char*& slot) ETC_INLINE {
+      const size_t off = (size_t)min(kt, last) * 128;  // past the last stage: a re-read
+      slot = smem + (kt % NSTAGE) * STAGE_BYTES + w * 8 * 128;
+      static_for<NL>([&](auto i) ETC_INLINE { src[i] = rowp[i] + off; });
+    };
+    auto go = [&](const char* const (&src)[NL], char* slot) ETC_INLINE {
+      static_for<NL>([&](auto i) ETC_INLINE { lds_dma16(src[i], slot + i * RSTEP * 128); });
+    };
+    auto issue = [&](int kt) ETC_INLINE {
+      const char* src[NL];
+      char* slot;
+      prep(kt, src, slot);
+      go(src, slot);
+    };
+    auto read = [&](Half& f, int kt, auto kk) ETC_INLINE {
+      const char* base = smem + (kt % NSTAGE) * STAGE_BYTES;
+      static_for<NJ>([&](auto j) ETC_INLINE { f.b[j] = *reinterpret_cast<const u32x4*>(base + boff[kk][j]); });
+      static_for<MI>([&](auto i) ETC_INLINE { f.a[i] = *reinterpret_cast<const u32x4*>(base + aoff[kk][i]); });
+    };
+    auto mma = [&](const Half& f) ETC_INLINE {
+      static_for<MI>([&](auto i) ETC_INLINE {
+        static_for<NJ>([&](auto j) ETC_INLINE { mma16(acc[i][j], f.a[i], f.b[j], tag); });
+      });
+    };
+    constexpr auto K0 = std::integral_constant<int, 0>{};
+    constexpr auto K1 = std::integral_constant<int, 1>{};
+    Half h0, h1;
+    static_for<NSTAGE>([&](auto k) ETC_INLINE { issue(decltype(k)::value); });
+    vm_wait_barrier<(NSTAGE - 1) * NL>();  // stage 0 has landed
+    read(h0, 0, K0);
+    for (int kt = 0; kt < nk; ++kt) {
+      lgkm_wait_all();
+      read(h1, kt, K1);
+      mma(h0);
+      // stage kt+1 has landed everywhere and every wave has read slot kt mod 4 (its
+      // reads completed before the barrier): stage kt+4 may overwrite it
+      const char* src[NL];
+      char* slot;
+      prep(kt + NSTAGE, src, slot);
+      vm_wait_barrier<(NSTAGE - 2) * NL>();
+      go(src, slot);
+      read(h0, kt + 1, K0);  // past the last stage: unused reads of an unused slot
+      mma(h1);
+    }
+  }
+};
+
 }  // namespace etc

@@ -794,53 +794,63 @@ ETC_SMALL_TASK void perm_task(KArgs& p, KLayer& L, int tau) {
 // Static mode: the next ticket of this workgroup's XCD queue (see claim_static).
 ETC_DEV int static_ticket(KArgs& p) { return xcd_ticket(p.sched); }
 
+// Gate/up rows of a tile: A row r is the token of sorted row r (rows past the expert's
+// count read the first row); B row b is in 16-row blocks that alternate gate / up over
+// the same 16 ffn columns (columns past F read row F-1).  Their results are never stored.
 template <typename TE>
-ETC_TASK void gateup_task(KArgs& p, KLayer& L, int e, int m, int n, Smem& sm) {
-  using Tile = KTile<TE, MNT>;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int wm = w / Tile::WN, wn = w % Tile::WN;
-  const int H = p.H, F = p.F, K = p.K;
-  TileSmem& Ts = sm.u.t;
-  const int r0 = sm.lc.off[e] + m * BM;
-  const int valid = min(BM, sm.lc.cnt[e] - m * BM);
-  for (int i = tid; i < BM; i += MNT) Ts.row_tok[i] = (i < valid) ? gp(L.sorted_assign)[r0 + i] / K : -1;
-  __syncthreads();
+ETC_DEV const char* gateup_row(KArgs& p, KLayer& L, const TileSmem& Ts, int e, int n, int bm,
+                               int r, int lc) {
+  const int H = p.H, F = p.F;
+  if (r < bm) {
+    const int tok = Ts.row_tok[r];
+    const TE* xq = static_cast<const TE*>(p.xq);
+    return reinterpret_cast<const char*>(xq + (size_t)(tok >= 0 ? tok : Ts.row_tok[0]) * H) + lc;
+  }
+  const int b = r - bm, blk = b >> 4;
+  const int f = min(n * BN1 + (blk >> 1) * 16 + (b & 15), F - 1);
+  const TE* src = static_cast<const TE*>((blk & 1) ? L.w_up : L.w_gate);
+  return reinterpret_cast<const char*>(src + ((size_t)e * F + f) * H) + lc;
+}
 
-  const TE* xq = static_cast<const TE*>(p.xq);
-  const TE* wg = static_cast<const TE*>(L.w_gate);
-  const TE* wu = static_cast<const TE*>(L.w_up);
+// SwiGLU of the tile into LDS (float, row stride GU_HSTR): small row tiles.
+constexpr int GU_HSTR = BN1 + 1;
+template <typename TE, int BMS>
+ETC_DEV void gateup_small(KArgs& p, KLayer& L, int e, int n, TileSmem& Ts, float* hs) {
+  using Tile = KTileS<TE, BMS, MNT>;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const char* rowp[Tile::LOADS];
   const int lc = Tile::load_chunk(tid) * 16;
-  // rows past the expert's count read the first row, columns past F read row F-1: their
-  // results are never stored
 #pragma unroll
   for (int i = 0; i < Tile::LOADS; ++i) {
     const int r = Tile::load_row(tid, i);
-    if (i < Tile::ALOADS) {
-      const int tok = Ts.row_tok[r];
-      rowp[i] = reinterpret_cast<const char*>(xq + (size_t)(tok >= 0 ? tok : Ts.row_tok[0]) * H) + lc;
-    } else {
-      // B row b: 16-row blocks alternate gate / up over the same 16 ffn columns
-      const int b = r - BM, blk = b >> 4;
-      const int f = min(n * BN1 + (blk >> 1) * 16 + (b & 15), F - 1);
-      const TE* src = (blk & 1) ? wu : wg;
-      rowp[i] = reinterpret_cast<const char*>(src + ((size_t)e * F + f) * H) + lc;
-    }
+    rowp[i] = gateup_row<TE>(p, L, Ts, e, n, BMS, r < Tile::ROWS ? r : BMS, lc);
   }
-  f32x4 acc[4][Tile::NJ];
-  Tile::run(Ts.gemm, rowp, H, valid, acc);
-  // static mode: draw the next ticket now; its atomic round trip overlaps the epilogue
-  // (issued before the tile, it would hold up the tile's first wait for its copies)
-  const bool prefetch = p.mode == ETC_SCHED_STATIC;
-  int next = -1;
-  if (prefetch && tid == 0) next = static_ticket(p);
+  f32x4 acc[Tile::MI][Tile::NJ];
+  Tile::run(Ts.gemm, rowp, p.H, acc);
+  // wave w's blocks 0 and 1 are gate and up of ffn columns 16 w .. 16 w + 15
+#pragma unroll
+  for (int i = 0; i < Tile::MI; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float g = acc[i][0][r], u = acc[i][1][r];
+      hs[(i * 16 + (lane >> 4) * 4 + r) * GU_HSTR + w * 16 + (lane & 15)] = g / (1.0f + expf(-g)) * u;
+    }
+}
 
-  // SwiGLU into LDS (float, row stride BN1 + 1 words), then whole rows out to hbuf:
+// The SwiGLU of a 128-row tile into LDS (float, row stride GU_HSTR).
+template <typename TE>
+ETC_DEV void gateup_large(KArgs& p, KLayer& L, int e, int n, int valid, TileSmem& Ts, float* hs) {
+  using Tile = KTile<TE, MNT>;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w / Tile::WN, wn = w % Tile::WN;
+  const char* rowp[Tile::LOADS];
+  const int lc = Tile::load_chunk(tid) * 16;
+#pragma unroll
+  for (int i = 0; i < Tile::LOADS; ++i) rowp[i] = gateup_row<TE>(p, L, Ts, e, n, BM, Tile::load_row(tid, i), lc);
+  f32x4 acc[4][Tile::NJ];
+  Tile::run(Ts.gemm, rowp, p.H, valid, acc);
   // column block j of this wave is gate (j even) or up (j odd) for ffn columns
   // n*BN1 + (wn*NJ + j)/2 * 16 ..
-  constexpr int HSTR = BN1 + 1;
-  static_assert(BM * HSTR * 4 <= (int)sizeof(Ts.gemm), "staged tile fits the GEMM buffer");
-  float* hs = reinterpret_cast<float*>(Ts.gemm);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -850,18 +860,44 @@ ETC_TASK void gateup_task(KArgs& p, KLayer& L, int e, int m, int n, Smem& sm) {
         const int row = wm * 64 + i * 16 + (lane >> 4) * 4 + r;
         const int col = (wn * Tile::NJ / 2 + jj) * 16 + (lane & 15);
         const float g = acc[i][2 * jj][r], u = acc[i][2 * jj + 1][r];
-        hs[row * HSTR + col] = g / (1.0f + expf(-g)) * u;
+        hs[row * GU_HSTR + col] = g / (1.0f + expf(-g)) * u;
       }
+}
+
+// GU(e, m, n): row tile m of expert e against ffn columns n*BN1.. of gate and up.  The
+// tile's layout in the workgroup's LDS arena follows its row count: up to 16 or 32 valid
+// rows take the four-stage small-M layout, more rows the three-stage 128-row one.
+template <typename TE>
+ETC_TASK void gateup_task(KArgs& p, KLayer& L, int e, int m, int n, Smem& sm) {
+  const int tid = threadIdx.x;
+  const int F = p.F, K = p.K;
+  TileSmem& Ts = sm.u.t;
+  const int r0 = sm.lc.off[e] + m * BM;
+  const int valid = min(BM, sm.lc.cnt[e] - m * BM);
+  for (int i = tid; i < BM; i += MNT) Ts.row_tok[i] = (i < valid) ? gp(L.sorted_assign)[r0 + i] / K : -1;
   __syncthreads();
-  // 8 bytes per store: 4 bf16 or 2 float columns (F is a multiple of 64, so a store never
-  // straddles the edge)
+
+  static_assert(BM * GU_HSTR * 4 <= (int)sizeof(Ts.gemm), "staged tile fits the GEMM buffer");
+  float* hs = reinterpret_cast<float*>(Ts.gemm);
+  // (the tile functions return after a barrier: the arena is free for the staging)
+  if (valid <= 16) gateup_small<TE, 16>(p, L, e, n, Ts, hs);
+  else if (valid <= 32) gateup_small<TE, 32>(p, L, e, n, Ts, hs);
+  else gateup_large<TE>(p, L, e, n, valid, Ts, hs);
+  // static mode: draw the next ticket now; its atomic round trip overlaps the epilogue
+  // (issued before the tile, it would hold up the tile's first wait for its copies)
+  const bool prefetch = p.mode == ETC_SCHED_STATIC;
+  int next = -1;
+  if (prefetch && tid == 0) next = static_ticket(p);
+  __syncthreads();
+  // whole rows out to hbuf, 8 bytes per store: 4 bf16 or 2 float columns (F is a
+  // multiple of 64, so a store never straddles the edge)
   constexpr int CPS = 8 / (int)sizeof(TE), SPR = BN1 / CPS;  // columns per store, stores per row
   TE* hb = static_cast<TE*>(p.hbuf);
   const int f0 = n * BN1, ncols = min(BN1, F - f0);
   for (int q = tid; q < valid * SPR; q += MNT) {
     const int row = q / SPR, c = (q % SPR) * CPS;
     if (c < ncols) {
-      const float* src = hs + row * HSTR + c;
+      const float* src = hs + row * GU_HSTR + c;
       uint64_t v;
       if constexpr (sizeof(TE) == 2) {
         v = (uint64_t)pack_bf16x2(src[0], src[1]) | ((uint64_t)pack_bf16x2(src[2], src[3]) << 32);
@@ -874,12 +910,76 @@ ETC_TASK void gateup_task(KArgs& p, KLayer& L, int e, int m, int n, Smem& sm) {
   if (prefetch && tid == 0) sm.next_ticket = next;
 }
 
+// Down rows of a tile: A row r is sorted row r0 + r of hbuf from column kb (rows past the
+// expert's count read row r0); B row b is row n2i*BN2 + b of the expert's w_down
+// (columns past H read row H-1).  Their results are never stored.
 template <typename TE>
-ETC_TASK void down_task(KArgs& p, KLayer& L, int e, int m, int n2i, int s, int gpc,
-                       Smem& sm) {
+ETC_DEV const char* down_row(KArgs& p, KLayer& L, int e, int n2i, int r0, int valid, int kb,
+                             int bm, int r, int lc) {
+  const int H = p.H, F = p.F;
+  if (r < bm) {
+    const TE* hb = static_cast<const TE*>(p.hbuf);
+    return reinterpret_cast<const char*>(hb + (size_t)(r0 + (r < valid ? r : 0)) * F + kb) + lc;
+  }
+  const int h = min(n2i * BN2 + r - bm, H - 1);
+  const TE* wd = static_cast<const TE*>(L.w_down);
+  return reinterpret_cast<const char*>(wd + ((size_t)e * H + h) * F + kb) + lc;
+}
+
+constexpr int D_CSTR = BN2 + 1;  // row stride of the staged down tile (words)
+
+template <typename TE, int BMS>
+ETC_DEV void down_small(KArgs& p, KLayer& L, int e, int n2i, int r0, int valid, int kb, int klen,
+                        float* ct) {
+  using Tile = KTileS<TE, BMS, MNT>;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const char* rowp[Tile::LOADS];
+  const int lc = Tile::load_chunk(tid) * 16;
+#pragma unroll
+  for (int i = 0; i < Tile::LOADS; ++i) {
+    const int r = Tile::load_row(tid, i);
+    rowp[i] = down_row<TE>(p, L, e, n2i, r0, valid, kb, BMS, r < Tile::ROWS ? r : BMS, lc);
+  }
+  f32x4 acc[Tile::MI][Tile::NJ];
+  Tile::run(reinterpret_cast<char*>(ct), rowp, klen, acc);
+#pragma unroll
+  for (int i = 0; i < Tile::MI; ++i)
+#pragma unroll
+    for (int j = 0; j < Tile::NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        ct[(i * 16 + (lane >> 4) * 4 + r) * D_CSTR + w * Tile::WCOLS + j * 16 + (lane & 15)] = acc[i][j][r];
+}
+
+template <typename TE>
+ETC_DEV void down_large(KArgs& p, KLayer& L, int e, int n2i, int r0, int valid, int kb, int klen,
+                        float* ct) {
   using Tile = KTile<TE, MNT>;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w / Tile::WN, wn = w % Tile::WN;
+  const char* rowp[Tile::LOADS];
+  const int lc = Tile::load_chunk(tid) * 16;
+#pragma unroll
+  for (int i = 0; i < Tile::LOADS; ++i)
+    rowp[i] = down_row<TE>(p, L, e, n2i, r0, valid, kb, BM, Tile::load_row(tid, i), lc);
+  f32x4 acc[4][Tile::NJ];
+  Tile::run(reinterpret_cast<char*>(ct), rowp, klen, valid, acc);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < Tile::NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        ct[(wm * 64 + i * 16 + (lane >> 4) * 4 + r) * D_CSTR + wn * Tile::WCOLS + j * 16 + (lane & 15)] =
+            acc[i][j][r];
+}
+
+// D(e, m, n2i, s): row tile m of expert e, output columns n2i*BN2.., ffn chunk s.  The
+// tile's LDS layout follows its row count, as in gateup_task.
+template <typename TE>
+ETC_TASK void down_task(KArgs& p, KLayer& L, int e, int m, int n2i, int s, int gpc,
+                       Smem& sm) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int H = p.H, F = p.F, K = p.K;
   TileSmem& Ts = sm.u.t;
   const int r0 = sm.lc.off[e] + m * BM;
@@ -892,45 +992,20 @@ ETC_TASK void down_task(KArgs& p, KLayer& L, int e, int m, int n2i, int s, int g
 
   const int kb = s * gpc * BN1;
   const int klen = min(F, kb + gpc * BN1) - kb;
-  const TE* hb = static_cast<const TE*>(p.hbuf);
-  const TE* wd = static_cast<const TE*>(L.w_down);
-  const char* rowp[Tile::LOADS];
-  const int lc = Tile::load_chunk(tid) * 16;
-  // rows past the expert's count read the first row, columns past H read row H-1: their
-  // results are never stored
-#pragma unroll
-  for (int i = 0; i < Tile::LOADS; ++i) {
-    const int r = Tile::load_row(tid, i);
-    if (i < Tile::ALOADS) {
-      rowp[i] = reinterpret_cast<const char*>(hb + (size_t)(r0 + (r < valid ? r : 0)) * F + kb) + lc;
-    } else {
-      const int h = min(n2i * BN2 + r - BM, H - 1);
-      rowp[i] = reinterpret_cast<const char*>(wd + ((size_t)e * H + h) * F + kb) + lc;
-    }
-  }
-  f32x4 acc[4][Tile::NJ];
-  Tile::run(Ts.gemm, rowp, klen, valid, acc);
+  // The tile goes through LDS first (row stride BN2 + 1 words: both passes free of bank
+  // conflicts; the arena is free once the tile has returned), so that the results leave
+  // as whole rows: each atomic instruction adds 64 consecutive columns of one token row
+  // (two cache lines) rather than 16 columns of four different rows, and the ordered
+  // combine writes its rows with 8-byte stores.
+  static_assert(BM * D_CSTR * 4 <= (int)sizeof(Ts.gemm), "staged tile fits the GEMM buffer");
+  float* ct = reinterpret_cast<float*>(Ts.gemm);
+  if (valid <= 16) down_small<TE, 16>(p, L, e, n2i, r0, valid, kb, klen, ct);
+  else if (valid <= 32) down_small<TE, 32>(p, L, e, n2i, r0, valid, kb, klen, ct);
+  else down_large<TE>(p, L, e, n2i, r0, valid, kb, klen, ct);
   const bool prefetch = p.mode == ETC_SCHED_STATIC;  // as in gateup_task
   int next = -1;
   if (prefetch && tid == 0) next = static_ticket(p);
-  const float gate = pair >= 0 ? gp(L.topk_w)[pair] : 0.f;  // arrives during the staging
-
-  // The tile goes through LDS first (row stride BN2 + 1 words: both passes free of bank
-  // conflicts; the LDS of the GEMM is free once Tile::run has returned), so that the
-  // results leave as whole rows: each atomic instruction adds 64 consecutive columns of
-  // one token row (two cache lines) rather than 16 columns of four different rows, and
-  // the ordered combine writes its rows with 8-byte stores.
-  constexpr int CSTR = BN2 + 1;
-  static_assert(BM * CSTR * 4 <= (int)sizeof(Ts.gemm), "staged tile fits the GEMM buffer");
-  float* ct = reinterpret_cast<float*>(Ts.gemm);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < Tile::NJ; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        ct[(wm * 64 + i * 16 + (lane >> 4) * 4 + r) * CSTR + wn * Tile::WCOLS + j * 16 + (lane & 15)] =
-            acc[i][j][r];
+  const float gate = pair >= 0 ? gp(L.topk_w)[pair] : 0.f;
   if (tid < BM) {
     Ts.row_tok[tid] = pair >= 0 ? pair / K : -1;
     Ts.row_gate[tid] = gate;
@@ -943,14 +1018,14 @@ ETC_TASK void down_task(KArgs& p, KLayer& L, int e, int m, int n2i, int s, int g
       const float g = Ts.row_gate[row];
 #pragma unroll
       for (int c = lane; c < BN2; c += 64)
-        if (c < ncols) red_add(dst + c, g * ct[row * CSTR + c]);
+        if (c < ncols) red_add(dst + c, g * ct[row * D_CSTR + c]);
     }
   } else {
     // H is a multiple of 128: a pair of columns never straddles the edge
     for (int q = tid; q < valid * (BN2 / 2); q += MNT) {
       const int row = q / (BN2 / 2), c = (q % (BN2 / 2)) * 2;
       if (c < ncols) {
-        const float* src = ct + row * CSTR + c;
+        const float* src = ct + row * D_CSTR + c;
         st_shared8(p.ybuf + (size_t)(r0 + row) * H + c0 + c,
                    (uint64_t)__float_as_uint(src[0]) | ((uint64_t)__float_as_uint(src[1]) << 32));
       }

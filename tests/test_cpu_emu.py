@@ -113,6 +113,19 @@ def test_degenerate_cases(lib, mode, which):
     moe_check.check_degenerate(which, cfg, x, layers, g)
 
 
+# One expert with top-1 puts every token in one expert, so T sets the rows of the row
+# tiles: 16 / 17 and 32 / 33 straddle the small-M layouts, 64 / 65 the half-A path of
+# the 128-row layout, 129 adds a one-row tile after a full one.  bf16 and float32.
+ONE = synth.MoEConfig("one", (129,), 256, 1, 1, 128, layers=1)
+
+
+@pytest.mark.parametrize("T", [1, 16, 17, 32, 33, 64, 65, 129])
+def test_tile_layout_boundaries(lib, T):
+    for cfg in (ONE, ONE.with_(dtype="f32")):
+        layers, x = synth.make_layers(cfg), synth.make_x(cfg, T, call=T)
+        _check(cfg, x, layers, driver.moe(lib, cfg, x, layers, mode="static", max_tokens=129))
+
+
 @pytest.mark.parametrize("mode", MOE_MODES)
 def test_four_chained_layers(lib, mode):
     """Four layers (the most one call chains) of a small shape."""

@@ -208,6 +208,21 @@ def test_degenerate_cases(which):
     say(moe_check.check_degenerate(which, cfg, x, layers, gpu))
 
 
+# One expert with top-1: T sets the rows of the row tiles (see the CPU harness test of
+# the same name): the layout boundaries 16 / 17, 32 / 33, 64 / 65 and a one-row tile
+# after a full one, bf16 and float32.
+ONE = synth.MoEConfig("one", (129,), 256, 1, 1, 128, layers=1)
+
+
+@pytest.mark.parametrize("T", [1, 16, 17, 32, 33, 64, 65, 129])
+def test_tile_layout_boundaries(T):
+    for cfg in (ONE, ONE.with_(dtype="f32")):
+        x, layers, ld, lnp = _setup(cfg, T, call=T)
+        say(f"layout boundary T={T} {cfg.dtype}")
+        gpu = run_moe(x.cuda(), ld, cfg.top_k, mode="static")
+        _compare(cfg, x, lnp, gpu)
+
+
 def test_four_chained_layers():
     """Four layers (the most one call chains) of a small shape."""
     cfg = DEEP
