@@ -25,6 +25,8 @@ FLAG_TRACE = 0x2
 FLAG_ALLOW_DYNAMIC = 0x4
 LAYOUT_WORDS = 16
 W_TRACE_LAST = 10  # control word holding the last traced call's record count
+CONTROL_WORDS = 320  # int32 control words at the start of every workspace
+CONTROL_BYTES = -(-CONTROL_WORDS * 4 // 256) * 256  # the region after them starts here
 
 
 class EtcError(RuntimeError):

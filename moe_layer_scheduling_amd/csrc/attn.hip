@@ -313,9 +313,10 @@ __global__ __launch_bounds__(NT) void attn_kernel(Args p) {
   if (tid == 0) sm.next = -1;
   while (true) {
     if (tid == 0) {
-      int t = sm.next >= 0 ? sm.next : atomicAdd(p.sched + W_TICKET, 1);
+      // (no check of the abort flag here: partial tasks never wait, and a merge's wait
+      // sees the flag and gives up, so every workgroup still leaves after an abort)
+      const int t = sm.next >= 0 ? sm.next : atomicAdd(p.sched + W_TICKET, 1);
       sm.next = -1;
-      if (ev_load_relaxed(p.sched + W_ABORT)) t = total;
       sm.task = t;
     }
     __syncthreads();
@@ -355,7 +356,8 @@ __global__ __launch_bounds__(NT) void attn_kernel(Args p) {
   __syncthreads();
   if (sm.flag && !(p.flags & ETC_FLAG_KEEP_COUNTERS)) {
     for (int i = tid; i < p.B * p.HKV; i += NT) ev_store_relaxed(p.ev + i, 0);
-    if (tid < W_NWORDS && tid != W_STATUS && tid != W_AUX) ev_store_relaxed(p.sched + tid, 0);
+    for (int i = tid; i < W_NWORDS; i += NT)
+      if (i != W_STATUS && i != W_AUX) ev_store_relaxed(p.sched + i, 0);
   }
 }
 

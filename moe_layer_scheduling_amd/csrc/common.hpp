@@ -235,13 +235,18 @@ enum SchedWord {
   W_QTOTAL = 3,   // dynamic: tasks that will ever be queued (grows as layers plan)
   W_PLANNED = 4,  // dynamic: layers whose task counts are final
   W_EXIT = 5,     // workgroups that have left the task loop
-  W_ABORT = 6,    // set when a wait times out: every workgroup leaves
   W_STATUS = 7,   // 0 ok, else an etc_status; survives the end-of-call reset
   W_AUX = 8,      // debug: where the abort came from
   W_TRACE = 9,    // trace records written so far in this call
   W_TRACE_LAST = 10,  // trace records of the last traced call (survives the reset)
-  W_XTICKET = 16,     // static: next ticket of each of the (up to 8) XCD queues
-  W_NWORDS = 32
+  // Words that many workgroups touch at once sit in 128-byte lines of their own.  A read
+  // of a line that a stream of atomics is updating waits behind those atomics (a
+  // workgroup that read the abort flag before every task, in the line of the ticket
+  // counter, spent most of its time on that read).
+  W_ABORT = 32,   // set when a wait times out: every workgroup leaves
+  W_XTICKET = 64, // static: next ticket of XCD queue q at W_XTICKET + q * W_LINE
+  W_LINE = 32,    // words per 128-byte line
+  W_NWORDS = 64 + 8 * 32
 };
 constexpr int MAX_XCD_QUEUES = 8;  // MI355X: 8 XCDs of 32 CUs, each with its own L2
 
@@ -258,7 +263,8 @@ ETC_DEV int xcd_ticket(int* sched) {
   const int Q = nwg < MAX_XCD_QUEUES ? nwg : MAX_XCD_QUEUES;
   const int G = nwg / Q;
   const int q = (int)blockIdx.x % Q;
-  const int i = __hip_atomic_fetch_add(gp(sched + W_XTICKET + q), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int i = __hip_atomic_fetch_add(gp(sched + W_XTICKET + q * W_LINE), 1, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
   return ((i / G) * Q + q) * G + i % G;
 }
 

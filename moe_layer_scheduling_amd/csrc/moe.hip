@@ -1918,8 +1918,8 @@ __global__ __launch_bounds__(MNT) void moe_kernel(Args pk) {
     }
     if (tid == 0) ev_store_relaxed(p.sched + W_TRACE_LAST, ev_load_relaxed(p.sched + W_TRACE));
     __syncthreads();
-    if (tid < W_NWORDS && tid != W_STATUS && tid != W_AUX && tid != W_TRACE_LAST)
-      ev_store_relaxed(p.sched + tid, 0);
+    for (int i = tid; i < W_NWORDS; i += MNT)
+      if (i != W_STATUS && i != W_AUX && i != W_TRACE_LAST) ev_store_relaxed(p.sched + i, 0);
   }
 }
 

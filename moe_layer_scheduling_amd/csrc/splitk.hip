@@ -197,8 +197,9 @@ __global__ __launch_bounds__(NT) void splitk_kernel(Args p) {
     if (tid == 0) {
       // static: partial tickets are slice-major, so a chunk of consecutive tickets (one
       // XCD queue's share) holds the tiles of one slice, which share its A block
-      int t = (p.mode == ETC_SCHED_STATIC) ? xcd_ticket(p.sched) : atomicAdd(p.sched + W_QHEAD, 1);
-      if (ev_load_relaxed(p.sched + W_ABORT)) t = total;
+      // (no check of the abort flag here: partial tasks never wait, and a reduction's
+      // wait sees the flag and gives up, so every workgroup still leaves after an abort)
+      const int t = (p.mode == ETC_SCHED_STATIC) ? xcd_ticket(p.sched) : atomicAdd(p.sched + W_QHEAD, 1);
       sm.task = t;
     }
     __syncthreads();
@@ -236,7 +237,8 @@ __global__ __launch_bounds__(NT) void splitk_kernel(Args p) {
   if (sm.flag && tid == 0 && p.status) gp(p.status)[0] = ev_load_relaxed(p.sched + W_STATUS);
   if (sm.flag && !(p.flags & ETC_FLAG_KEEP_COUNTERS)) {
     for (int i = tid; i < p.tiles; i += NT) ev_store_relaxed(p.ev + i, 0);
-    if (tid < W_NWORDS && tid != W_STATUS && tid != W_AUX) ev_store_relaxed(p.sched + tid, 0);
+    for (int i = tid; i < W_NWORDS; i += NT)
+      if (i != W_STATUS && i != W_AUX) ev_store_relaxed(p.sched + i, 0);
   }
 }
 

@@ -84,6 +84,9 @@ def test_layout_offsets_inside_workspace(lib):
         bn1 = offs[11]
         assert offs[7] == (1408 + bn1 - 1) // bn1 and offs[8] == 4096 // offs[9]
     assert lib.etc_moe_workspace_layout(4096, 4096, 64, 6, 1408, 2, 1, 0, 2, out) == 1
+    # the control words come first; layer 0's first counter follows them
+    assert lib.etc_moe_workspace_layout(4096, 4096, 64, 6, 1408, 2, 1, 0, 0, out) == 0
+    assert out[0] == binding.CONTROL_BYTES
 
 
 def _call_moe(lib, **over):

@@ -102,6 +102,6 @@ def test_counters_reach_split_k():
     binding.splitk_gemm(A.cuda(), B.cuda(), S, mode="static", workspace=ws,
                         flags=binding.FLAG_KEEP_COUNTERS)
     torch.cuda.synchronize()
-    ev = ws.view(256, N // 128, torch.int32).cpu().numpy()  # counters follow the control words
+    ev = ws.view(binding.CONTROL_BYTES, N // 128, torch.int32).cpu().numpy()  # counters follow the control words
     assert np.all(ev == S), ev
     ws.reset()
