@@ -75,7 +75,7 @@ struct Smem {
   int start[MAXB];
   int tmp[8];
   long long ltmp[4];
-  float s[MAXG][CH];        // scores, then weights exp(s - m)
+  alignas(16) float s[MAXG][CH];  // scores, then weights exp(s - m); 16-byte views in the merge
   float ml[MAXG][2];        // per head: chunk max, weight sum
   float o[4][MAXG][HD];     // per wave partial weighted value sums
   int task;
@@ -267,31 +267,104 @@ ETC_DEV void partial_task(const Args& p, Smem& sm, int b, int g, int c, int rec)
   }
 }
 
-// Output of the G query heads of (b, g) from the n_b partial records starting at rec0.
-ETC_DEV void merge_task(const Args& p, int b, int g, int rec0, int nb) {
-  const int tid = threadIdx.x;
+// Output of the G query heads of (b, g) from the n_b partial records starting at rec0
+// (every thread of the workgroup).  Pass 1: M = max m_c per head, each thread over every
+// NT-th record, then across the workgroup.  Pass 2, CH records at a time: each thread
+// turns one record's m into the weight exp(m_c - M) per head (LDS) and adds l_c times
+// that weight to its share of L; then thread (s, h, d4) adds weight times o_c[d4..d4+3]
+// over every NS-th record of the chunk (NS = NT / (32 G) threads per output, their loads
+// unrolled so that several records are in flight).  Last, the NS shares of O and the
+// shares of L are summed and out = O / L.
+ETC_DEV void merge_task(const Args& p, Smem& sm, int b, int g, int rec0, int nb) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int G = p.G, HQ = p.HKV * G;
-  for (int e = tid; e < G * (HD / 4); e += NT) {
-    const int h = e / (HD / 4), d4 = (e % (HD / 4)) * 4;
-    const float* base = p.part + (size_t)rec0 * G * REC + h * REC;
-    float M = -INFINITY;
-    for (int c = 0; c < nb; ++c) M = fmaxf(M, gp(base)[(size_t)c * G * REC + HD]);
-    float Lsum = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int c = 0; c < nb; ++c) {
-      const float* r = base + (size_t)c * G * REC;
-      const float f = __expf(gp(r)[HD] - M);
-      Lsum = fmaf(gp(r)[HD + 1], f, Lsum);
-      const f32x4 ov = gld<f32x4>(r + d4);
-      acc.x = fmaf(ov.x, f, acc.x);
-      acc.y = fmaf(ov.y, f, acc.y);
-      acc.z = fmaf(ov.z, f, acc.z);
-      acc.w = fmaf(ov.w, f, acc.w);
+  const float* base = p.part + (size_t)rec0 * G * REC;
+  float mloc[MAXG], lloc[MAXG];
+#pragma unroll
+  for (int h = 0; h < MAXG; ++h) { mloc[h] = -INFINITY; lloc[h] = 0.f; }
+  for (int c = tid; c < nb; c += NT) {
+#pragma unroll
+    for (int h = 0; h < MAXG; ++h)
+      if (h < G) mloc[h] = fmaxf(mloc[h], gp(base)[((size_t)c * G + h) * REC + HD]);
+  }
+  // workgroup max per head: the wave's lanes, then the four waves through LDS
+#pragma unroll
+  for (int h = 0; h < MAXG; ++h) {
+    if (h < G) {
+      float m = mloc[h];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, WAVE));
+      if (lane == 0) sm.o[w][h][0] = m;
     }
-    const float inv = 1.0f / Lsum;
-    *reinterpret_cast<ETC_GLOBAL f32x4*>(gp(p.out + ((size_t)b * HQ + (size_t)g * G + h) * HD + d4)) =
+  }
+  __syncthreads();
+  if (tid < G) sm.ml[tid][0] = fmaxf(fmaxf(sm.o[0][tid][0], sm.o[1][tid][0]), fmaxf(sm.o[2][tid][0], sm.o[3][tid][0]));
+  __syncthreads();
+  const int NS = NT / (32 * G);  // threads per output chunk of 4 dims (1, 2 or 8)
+  const int item = tid % (32 * G), sidx = tid / (32 * G);
+  const int oh = item / 32, d4 = (item % 32) * 4;
+  const bool active = sidx < NS;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < nb; c0 += CH) {
+    const int c = c0 + tid;
+#pragma unroll
+    for (int h = 0; h < MAXG; ++h) {
+      if (h < G) {
+        float f = 0.f;
+        if (c < nb) {
+          const float* r = base + ((size_t)c * G + h) * REC;
+          f = __expf(gp(r)[HD] - sm.ml[h][0]);
+          lloc[h] = fmaf(gp(r)[HD + 1], f, lloc[h]);
+        }
+        sm.s[h][tid] = f;
+      }
+    }
+    __syncthreads();
+    const int n = min(CH, nb - c0);
+    if (active) {
+      const float* r0 = base + ((size_t)c0 * G + oh) * REC + d4;
+#pragma unroll 8
+      for (int k = sidx; k < n; k += NS) {
+        const f32x4 ov = gld<f32x4>(r0 + (size_t)k * G * REC);
+        const float f = sm.s[oh][k];
+        acc.x = fmaf(ov.x, f, acc.x);
+        acc.y = fmaf(ov.y, f, acc.y);
+        acc.z = fmaf(ov.z, f, acc.z);
+        acc.w = fmaf(ov.w, f, acc.w);
+      }
+    }
+    __syncthreads();  // the weights of the chunk are read before the next chunk's
+  }
+  // L per head: the wave's lanes, then the waves
+#pragma unroll
+  for (int h = 0; h < MAXG; ++h) {
+    if (h < G) {
+      float l = lloc[h];
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off, WAVE);
+      if (lane == 0) sm.o[w][h][1] = l;
+    }
+  }
+  __syncthreads();
+  if (tid < G) sm.ml[tid][1] = (sm.o[0][tid][1] + sm.o[1][tid][1]) + (sm.o[2][tid][1] + sm.o[3][tid][1]);
+  __syncthreads();
+  // the NS shares of each output chunk (staged in the weight area: NS * 32 G * 4 floats
+  // = 4 NT floats)
+  float* stage = &sm.s[0][0];
+  if (active && NS > 1) *reinterpret_cast<f32x4*>(stage + 4 * tid) = acc;
+  __syncthreads();
+  if (sidx == 0) {
+    if (NS > 1) {
+      for (int s2 = 1; s2 < NS; ++s2) {
+        const f32x4 o2 = *reinterpret_cast<const f32x4*>(stage + 4 * (s2 * 32 * G + item));
+        acc.x += o2.x; acc.y += o2.y; acc.z += o2.z; acc.w += o2.w;
+      }
+    }
+    const float inv = 1.0f / sm.ml[oh][1];
+    *reinterpret_cast<ETC_GLOBAL f32x4*>(gp(p.out + ((size_t)b * HQ + (size_t)g * G + oh) * HD + d4)) =
         f32x4{acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv};
   }
+  __syncthreads();
 }
 
 __global__ __launch_bounds__(NT) void attn_kernel(Args p) {
@@ -338,14 +411,14 @@ __global__ __launch_bounds__(NT) void attn_kernel(Args p) {
         sm.flag = (p.mode == ETC_SCHED_DYNAMIC && old == nb - 1) ? 1 : 0;
       }
       __syncthreads();
-      if (sm.flag) merge_task(p, b, g, sm.pbase[b] + g * nb, nb);
+      if (sm.flag) merge_task(p, sm, b, g, sm.pbase[b] + g * nb, nb);
       __syncthreads();
     } else {
       const int bg = t - np, b = bg / p.HKV, g = bg % p.HKV;
       const int nb = sm.nsplit[b];
       if (tid == 0) sm.flag = spin_until_geq(p.ev + bg, nb, p.sched, p.timeout_ticks, 30) ? 1 : 0;
       __syncthreads();
-      if (sm.flag) merge_task(p, b, g, sm.pbase[b] + g * nb, nb);
+      if (sm.flag) merge_task(p, sm, b, g, sm.pbase[b] + g * nb, nb);
       __syncthreads();
     }
   }
