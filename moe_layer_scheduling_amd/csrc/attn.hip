@@ -257,9 +257,14 @@ ETC_DEV void partial_task(const Args& p, Smem& sm, int b, int g, int c, int rec)
   __syncthreads();
   // the partial record of every head, read by the merge on any XCD: agent-scope stores
   float* dst = p.part + (size_t)rec * G * REC;
-  for (int e = tid; e < G * HD; e += NT) {
-    const int h = e / HD, d = e % HD;
-    st_shared(dst + h * REC + d, sm.o[0][h][d] + sm.o[1][h][d] + sm.o[2][h][d] + sm.o[3][h][d]);
+  // four dims per 16-byte store (a record is REC floats, a multiple of 4)
+  for (int e = tid; e < G * (HD / 4); e += NT) {
+    const int h = e / (HD / 4), d = (e % (HD / 4)) * 4;
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = sm.o[0][h][d + i] + sm.o[1][h][d + i] + sm.o[2][h][d + i] + sm.o[3][h][d + i];
+    st_shared16(dst, (uint32_t)((h * REC + d) * sizeof(float)),
+                u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
   }
   if (tid < G) {
     st_shared(dst + tid * REC + HD, sm.ml[tid][0]);

@@ -165,7 +165,8 @@ ETC_DEV void st_shared(float* p, float v) { st_shared(reinterpret_cast<uint32_t*
 ETC_DEV void st_shared8(void* p, uint64_t v) {
   __hip_atomic_store(gp(static_cast<uint64_t*>(p)), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-// 16 bytes at byte offset off (16-byte aligned, per lane) from the wave-uniform base, as
+// 16 bytes at byte offset off (16-byte aligned, per lane, below 2^31) from the wave-uniform
+// base, as
 // one buffer_store_dwordx4 with the same device-scope policy (sc1).  Two 8-byte stores
 // would leave every 16-byte piece half written by each instruction: byte-masked partial
 // writes of the cache lines, which cost far more than whole 64-byte pieces.

@@ -556,9 +556,11 @@ ETC_SMALL_TASK void route_task(KArgs& p, KLayer& L, int tau, Smem& sm) {
   }
   // clear this tile's accumulator rows for the atomic combine: the last global loads of
   // the task are done, so these stores drain while the rest of the task runs
+  // (16-byte stores: half the store instructions of 8-byte ones for the same bytes)
   if (p.combine == ETC_COMBINE_ATOMIC) {
-    uint64_t* acc = reinterpret_cast<uint64_t*>(p.out_acc + (size_t)t0 * H);
-    for (int i = tid; i < nt * H / 2; i += MNT) st_shared8(acc + i, 0);
+    float* acc = p.out_acc + (size_t)t0 * H;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int i = tid; i < nt * H / 4; i += MNT) st_shared16(acc, (uint32_t)(i * 16), z);
   }
   __syncthreads();
   for (int o = tid; o < nt * E; o += MNT) {
@@ -889,22 +891,20 @@ ETC_TASK void gateup_task(KArgs& p, KLayer& L, int e, int m, int n, Smem& sm) {
   int next = -1;
   if (prefetch && tid == 0) next = static_ticket(p);
   __syncthreads();
-  // whole rows out to hbuf, 8 bytes per store: 4 bf16 or 2 float columns (F is a
-  // multiple of 64, so a store never straddles the edge)
-  constexpr int CPS = 8 / (int)sizeof(TE), SPR = BN1 / CPS;  // columns per store, stores per row
-  TE* hb = static_cast<TE*>(p.hbuf);
+  // whole rows out to hbuf, 16 bytes per store: 8 bf16 or 4 float columns (F is a
+  // multiple of 64, so a store never straddles the edge).  16-byte stores: coherent
+  // 8-byte stores move less than half the bytes per cycle when every CU stores at once.
+  constexpr int CPS = 16 / (int)sizeof(TE), SPR = BN1 / CPS;  // columns per store, stores per row
   const int f0 = n * BN1, ncols = min(BN1, F - f0);
+  TE* hb = static_cast<TE*>(p.hbuf) + (size_t)r0 * F + f0;  // the tile's first element
   for (int q = tid; q < valid * SPR; q += MNT) {
     const int row = q / SPR, c = (q % SPR) * CPS;
     if (c < ncols) {
       const float* src = hs + row * GU_HSTR + c;
-      uint64_t v;
-      if constexpr (sizeof(TE) == 2) {
-        v = (uint64_t)pack_bf16x2(src[0], src[1]) | ((uint64_t)pack_bf16x2(src[2], src[3]) << 32);
-      } else {
-        v = (uint64_t)__float_as_uint(src[0]) | ((uint64_t)__float_as_uint(src[1]) << 32);
-      }
-      st_shared8(hb + (size_t)(r0 + row) * F + f0 + c, v);
+      float v[CPS];
+#pragma unroll
+      for (int i = 0; i < CPS; ++i) v[i] = src[i];
+      st_shared16(hb, (uint32_t)(((size_t)row * F + c) * sizeof(TE)), pack16<TE>(v));
     }
   }
   if (prefetch && tid == 0) sm.next_ticket = next;
@@ -1021,13 +1021,15 @@ ETC_TASK void down_task(KArgs& p, KLayer& L, int e, int m, int n2i, int s, int g
         if (c < ncols) red_add(dst + c, g * ct[row * D_CSTR + c]);
     }
   } else {
-    // H is a multiple of 128: a pair of columns never straddles the edge
-    for (int q = tid; q < valid * (BN2 / 2); q += MNT) {
-      const int row = q / (BN2 / 2), c = (q % (BN2 / 2)) * 2;
+    // H is a multiple of 128: four columns never straddle the edge (16-byte stores)
+    float* yb = p.ybuf + (size_t)r0 * H + c0;  // the tile's first element
+    for (int q = tid; q < valid * (BN2 / 4); q += MNT) {
+      const int row = q / (BN2 / 4), c = (q % (BN2 / 4)) * 4;
       if (c < ncols) {
         const float* src = ct + row * D_CSTR + c;
-        st_shared8(p.ybuf + (size_t)(r0 + row) * H + c0 + c,
-                   (uint64_t)__float_as_uint(src[0]) | ((uint64_t)__float_as_uint(src[1]) << 32));
+        st_shared16(yb, (uint32_t)(((size_t)row * H + c) * sizeof(float)),
+                    u32x4{__float_as_uint(src[0]), __float_as_uint(src[1]), __float_as_uint(src[2]),
+                          __float_as_uint(src[3])});
       }
     }
   }

@@ -148,18 +148,28 @@ ETC_DEV void partial_task(const Args& p, Smem& sm, int tile, int s) {
   __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
   __syncthreads();
 
-  // the partial is read by another workgroup: agent-scope stores (see st_shared)
-  float* dst = p.part + ((long)tile * p.S + s) * (TM * TN);
+  // The partial is read by another workgroup: agent-scope stores (see st_shared), 16
+  // bytes each, so the tile goes through LDS first (the ring is free now; row stride
+  // TN + 4 floats keeps the four row groups of a write in different banks and the rows
+  // 16-byte aligned).
+  constexpr int PSTR = TN + 4;
+  static_assert(TM * PSTR * 4 <= (int)sizeof(sm.stage), "staged partial fits the ring");
+  float* pt = reinterpret_cast<float*>(&sm.stage[0][0]);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = i * 16 + (lane >> 4) * 4 + r;
-        const int col = w * 32 + j * 16 + (lane & 15);
-        st_shared(dst + row * TN + col, acc[i][j][r]);
-      }
+      for (int r = 0; r < 4; ++r)
+        pt[(i * 16 + (lane >> 4) * 4 + r) * PSTR + w * 32 + j * 16 + (lane & 15)] = acc[i][j][r];
+  __syncthreads();
+  float* dst = p.part + ((long)tile * p.S + s) * (TM * TN);
+  for (int q = tid; q < TM * TN / 4; q += NT) {
+    const int row = q / (TN / 4), c = (q % (TN / 4)) * 4;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(pt + row * PSTR + c);
+    st_shared16(dst, (uint32_t)((row * TN + c) * sizeof(float)),
+                u32x4{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)});
+  }
 }
 
 // Rows [rc*TM/RCHUNKS, ...) of a C tile = partials summed in slice order.  Every thread
