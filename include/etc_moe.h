@@ -172,11 +172,14 @@ size_t etc_moe_workspace_size(int32_t max_tokens, int32_t hidden, int32_t expert
  *   [6] max_rt   [7] n1   [8] n_rt(max_tokens)   [9] rows per routing tile
  *   [10] rows per expert tile   [11] ffn columns per gate/up tile
  *   [12] hidden columns per down tile   [13] trace region   [14] trace records it holds
- *   [15] ev_perm (1 int32: routing tiles whose pairs are placed in the permutation).
+ *   [15] ev_perm (1 int32: routing tiles whose pairs are placed in the permutation)
+ *   [16] ev_rq ([n_rt] int32: router slices of each routing tile that have reported).
  * The plan words are: [0] row tiles RT, [1] gate/up tasks, [2] down tasks,
  * [3] finalize tasks, [4] ffn chunks of the down projection nS, [5] gate/up tiles per
- * chunk, [6] first static ticket of the next layer. */
-#define ETC_LAYOUT_WORDS 16
+ * chunk, [6] first static ticket of the next layer, [7] router slices per routing tile
+ * Q (the call cuts each tile's router along H into Q tasks when the routing tiles
+ * would leave at least half of the workgroups idle; Q = 1 otherwise). */
+#define ETC_LAYOUT_WORDS 17
 etc_status etc_moe_workspace_layout(int32_t max_tokens, int32_t hidden, int32_t experts,
                                     int32_t top_k, int32_t ffn, int32_t num_layers,
                                     etc_dtype dtype, etc_combine combine, int32_t layer,
@@ -311,7 +314,7 @@ const char* etc_status_string(etc_status status);
 int32_t etc_default_workers(int32_t kind, etc_dtype dtype);
 
 /* ABI version of this header: (major << 16) | minor. */
-#define ETC_ABI_VERSION 0x00010000
+#define ETC_ABI_VERSION 0x00010001
 int32_t etc_abi_version(void);
 
 #ifdef __cplusplus

@@ -38,6 +38,7 @@
 // and whichever signal completes a counter enqueues the tasks it releases.
 // The token count T is a kernel argument; nothing in the code depends on its value.
 #include <float.h>
+#include <algorithm>
 #include <string.h>
 
 #include "common.hpp"
@@ -60,6 +61,11 @@ constexpr int MAX_TOKENS = 262143;  // task fields are 14 bits
 // Up to this many routing tiles (T <= 64) the scan task also scatters the permutation
 // (at most 64 * k pairs): separate P tasks would only add a hand-off to a short path.
 constexpr int PERM_INLINE_RT = 4;
+// Router slices: with few routing tiles for the workers, the router of a tile is split
+// along K into Q slice tasks (Q <= RQ_MAX) whose partial logits go through the
+// workspace; the slice whose report completes its tile's counter finishes the tile
+// (sum, top-k, ranks).  At most NRQ_CAP slice records per call.
+constexpr int RQ_MAX = 8, NRQ_CAP = 256;
 
 // Task bodies are separate functions: each gets its own register allocation instead of
 // sharing one with the scheduler loop and every other task (inlined together they spill
@@ -71,7 +77,7 @@ constexpr int PERM_INLINE_RT = 4;
 #define ETC_SMALL_TASK __device__ __attribute__((always_inline))
 
 enum Kind { K_NONE = 0, K_R = 1, K_S = 2, K_GU = 3, K_D = 4, K_F = 5, K_P = 6 };
-enum PlanWord { PL_RT = 0, PL_NGU, PL_ND, PL_NF, PL_NS, PL_GPC, PL_NEXTBASE, PL_WORDS = 8 };
+enum PlanWord { PL_RT = 0, PL_NGU, PL_ND, PL_NF, PL_NS, PL_GPC, PL_NEXTBASE, PL_Q, PL_WORDS = 8 };
 
 struct Task {
   int kind, layer, a, b, c, d;
@@ -116,6 +122,7 @@ struct LayerArgs {
   int* pos;            // [T][k]
   int* plan;           // [PL_WORDS]
   int* ev_route;       // 1
+  int* ev_rq;          // [n_rt] router slices of each tile that have reported
   int* ev_scan;        // 1
   int* ev_perm;        // 1
   int* ev_gu;          // [max_rt][n1]
@@ -130,11 +137,13 @@ struct Args {
   unsigned flags;
   int n_rt, n1, n2, workers, max_rt, n_rt_cap, queue_len;
   int n_perm;  // P tasks per layer: n_rt, or 0 when S scatters the permutation itself
+  int Q, n_rq; // router slices per routing tile, R tasks per layer (n_rt * Q)
   uint64_t timeout_ticks;  // watchdog: a wait without progress for this long gives up
   void* xq;        // [T][H] normalised input in storage precision
   void* hbuf;      // [T*k][F] SwiGLU output, rows in sorted order
   float* out_acc;  // [T][H] atomic-combine accumulator
   float* ybuf;     // [T*k][H] ordered-combine rows
+  float* rpart;    // [NRQ_CAP][BT][E] partial logits of router slices
   long long* queue;
   int* sched;
   unsigned long long* trace;  // ETC_FLAG_TRACE records, 4 words each
@@ -289,7 +298,7 @@ struct RouterSplit<1> {  // float32 layers: the values themselves
 // Writes the partial logits of its K slice to R.part[ks][t][e].
 template <typename TE, int NBW>
 ETC_DEV void router_item(KArgs& p, KLayer& L, RouteSmem& R, int t0, int nt, int g, int ks,
-                         int KS) {
+                         int KS, int k_lo, int k_hi) {
   constexpr int EPC = 16 / (int)sizeof(TE);  // values per 16-byte chunk
   constexpr int KSTEP = 4 * EPC;              // K per MFMA step (four lane groups)
   constexpr int NSPLIT = sizeof(TE) == 2 ? 3 : 1;
@@ -316,8 +325,8 @@ ETC_DEV void router_item(KArgs& p, KLayer& L, RouteSmem& R, int t0, int nt, int 
 #pragma unroll
     for (int q = 0; q < NSPLIT; ++q) acc[b][q] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int kc = 0; kc < H; kc += RouteSmem::GCHUNK) {
-    const int len = min(RouteSmem::GCHUNK, H - kc);
+  for (int kc = k_lo; kc < k_hi; kc += RouteSmem::GCHUNK) {
+    const int len = min(RouteSmem::GCHUNK, k_hi - kc);
     __syncthreads();  // every wave is done with the previous chunk
     for (int i = tid * 4; i < len; i += MNT * 4)
       *reinterpret_cast<f32x4*>(&R.gam[i]) = gld<f32x4>(L.gamma + kc + i);
@@ -381,11 +390,11 @@ ETC_DEV void router_item(KArgs& p, KLayer& L, RouteSmem& R, int t0, int nt, int 
 // then every wave sums its lanes and writes R.part[w][t][e] (KS = NWAVE slices).  It also
 // writes xq = dtype(v * rs) for the tile's tokens (16 bytes per lane, rows contiguous).
 template <typename TE, int NTOK>
-ETC_DEV void router_valu(KArgs& p, KLayer& L, RouteSmem& R, int t0, int nt) {
+ETC_DEV void router_valu(KArgs& p, KLayer& L, RouteSmem& R, int t0, int nt, int k_lo, int k_hi) {
   constexpr int EPC = 16 / (int)sizeof(TE);
   constexpr int EMAX = 16;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int H = p.H, E = p.E, cpr = H / EPC;
+  const int H = p.H, E = p.E;
   const TE* x = static_cast<const TE*>(L.in) + (size_t)t0 * H;
   const TE* wr = static_cast<const TE*>(L.w_router);
   TE* xq = static_cast<TE*>(p.xq) + (size_t)t0 * H;
@@ -397,7 +406,7 @@ ETC_DEV void router_valu(KArgs& p, KLayer& L, RouteSmem& R, int t0, int nt) {
   float rs[NTOK];
 #pragma unroll
   for (int t = 0; t < NTOK; ++t) rs[t] = R.rs[min(t, nt - 1)];
-  for (int c = tid; c < cpr; c += MNT) {
+  for (int c = k_lo / EPC + tid; c < k_hi / EPC; c += MNT) {
     // rows past the tile's tokens repeat its last token, experts past E the last expert
     u32x4 xv[NTOK], wv[EMAX];
     f32x4 gv[EPC / 4];
@@ -493,12 +502,17 @@ ETC_DEV void topk_row(KArgs& p, KLayer& L, RouteSmem& R, int t0, int nt) {
   }
 }
 
+// R(a): slice q = a mod Q of routing tile tau = a / Q.  Returns true when the tile's
+// routing is complete in this workgroup: always with one slice (Q = 1), else only in the
+// slice whose report completed the tile's slice counter.  Every thread calls this and
+// gets the same answer.
 template <typename TE>
-ETC_SMALL_TASK void route_task(KArgs& p, KLayer& L, int tau, Smem& sm) {
+ETC_SMALL_TASK bool route_task(KArgs& p, KLayer& L, int a, Smem& sm) {
   constexpr int EPC = 16 / (int)sizeof(TE);
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int H = p.H, E = p.E, K = p.K;
+  const int H = p.H, E = p.E, K = p.K, Q = p.Q;
+  const int tau = a / Q, q = a - tau * Q;
   const int t0 = tau * BT, nt = tile_rows(p, tau);
   RouteSmem& R = sm.u.r;
 
@@ -539,35 +553,73 @@ ETC_SMALL_TASK void route_task(KArgs& p, KLayer& L, int tau, Smem& sm) {
   }
   __syncthreads();
 
-  // 2. partial logits: on the vector ALUs for a few tokens and experts, else per
-  //    (expert group, K slice) on the matrix cores, one item per wave
+  // 2. partial logits over this slice's K range (whole steps of the MFMA or VALU path):
+  //    on the vector ALUs for a few tokens and experts, else per (expert group, K
+  //    slice) on the matrix cores, one item per wave
+  const int kstep = 4 * EPC, nst = H / kstep;
+  const int k_lo = (q * nst / Q) * kstep, k_hi = ((q + 1) * nst / Q) * kstep;
   const int NB = cdiv(E, 16);
   const int NBW = NB <= 1 ? 1 : (NB <= 2 ? 2 : 4);
   int KS = NWAVE / cdiv(NB, NBW);
   if (E <= 16 && nt <= 2) {
     KS = NWAVE;
-    if (nt == 1) router_valu<TE, 1>(p, L, R, t0, nt);
-    else router_valu<TE, 2>(p, L, R, t0, nt);
+    if (nt == 1) router_valu<TE, 1>(p, L, R, t0, nt, k_lo, k_hi);
+    else router_valu<TE, 2>(p, L, R, t0, nt, k_lo, k_hi);
   } else {
     const int g = w / KS, ks = w % KS;
-    if (NBW == 1) router_item<TE, 1>(p, L, R, t0, nt, g, ks, KS);
-    else if (NBW == 2) router_item<TE, 2>(p, L, R, t0, nt, g, ks, KS);
-    else router_item<TE, 4>(p, L, R, t0, nt, g, ks, KS);
+    if (NBW == 1) router_item<TE, 1>(p, L, R, t0, nt, g, ks, KS, k_lo, k_hi);
+    else if (NBW == 2) router_item<TE, 2>(p, L, R, t0, nt, g, ks, KS, k_lo, k_hi);
+    else router_item<TE, 4>(p, L, R, t0, nt, g, ks, KS, k_lo, k_hi);
   }
-  // clear this tile's accumulator rows for the atomic combine: the last global loads of
-  // the task are done, so these stores drain while the rest of the task runs
-  // (16-byte stores: half the store instructions of 8-byte ones for the same bytes)
+  // clear this slice's share of the tile's accumulator rows for the atomic combine (the
+  // 16-byte chunks c_lo .. c_hi-1 of every row): the last global loads of the task are
+  // done, so these stores drain while the rest of the task runs
   if (p.combine == ETC_COMBINE_ATOMIC) {
     float* acc = p.out_acc + (size_t)t0 * H;
     const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int i = tid; i < nt * H / 4; i += MNT) st_shared16(acc, (uint32_t)(i * 16), z);
+    const int cpr = H / 4, c_lo = q * cpr / Q, ncs = (q + 1) * cpr / Q - c_lo;
+    for (int i = tid; i < nt * ncs; i += MNT) {
+      const int row = i / ncs, c = c_lo + (i - row * ncs);
+      st_shared16(acc, (uint32_t)((row * cpr + c) * 16), z);
+    }
   }
   __syncthreads();
-  for (int o = tid; o < nt * E; o += MNT) {
-    const int tt = o / E, e = o - tt * E;
-    float v = 0.f;
-    for (int k = 0; k < KS; ++k) v += R.part[(k * BT + tt) * E + e];
-    R.lg[tt][e] = R.rs[tt] * v + R.bias[e];
+  if (Q == 1) {
+    for (int o = tid; o < nt * E; o += MNT) {
+      const int tt = o / E, e = o - tt * E;
+      float v = 0.f;
+      for (int k = 0; k < KS; ++k) v += R.part[(k * BT + tt) * E + e];
+      R.lg[tt][e] = R.rs[tt] * v + R.bias[e];
+    }
+  } else {
+    // the slice's partial logits (before the 1/rms factor and the bias) go out; the
+    // slice whose report completes the tile's counter sums them in slice order
+    float* mine = p.rpart + (size_t)a * BT * E;
+    for (int o = tid; o < nt * E; o += MNT) {
+      const int tt = o / E, e = o - tt * E;
+      float v = 0.f;
+      for (int k = 0; k < KS; ++k) v += R.part[(k * BT + tt) * E + e];
+      st_shared(mine + o, v);
+    }
+    publish_shared();
+    if (tid == 0) sm.flag = (ev_add_acquire(L.ev_rq + tau, 1) == Q - 1) ? 1 : 0;  // acquire: the others' slices
+    __syncthreads();
+    const bool last = sm.flag != 0;
+    __syncthreads();
+    if (!last) return false;
+    // every slice's value of an output is loaded before any is added (one round trip),
+    // then they are summed in slice order
+    const float* all = p.rpart + (size_t)tau * Q * BT * E;
+    for (int o = tid; o < nt * E; o += MNT) {
+      const int tt = o / E, e = o - tt * E;
+      float part[RQ_MAX];
+#pragma unroll
+      for (int s2 = 0; s2 < RQ_MAX; ++s2) part[s2] = s2 < Q ? gp(all)[(size_t)s2 * BT * E + o] : 0.f;
+      float v = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < RQ_MAX; ++s2) v += part[s2];
+      R.lg[tt][e] = R.rs[tt] * v + R.bias[e];
+    }
   }
   __syncthreads();
 
@@ -590,6 +642,7 @@ ETC_SMALL_TASK void route_task(KArgs& p, KLayer& L, int tau, Smem& sm) {
     st_shared(L.lrank + t0 * K + a, __popc(R.emask[R.sel[tt][j]] & ((1u << tt) - 1u)));
   }
   for (int e = tid; e < E; e += MNT) st_shared(L.hist + tau * E + e, __popc(R.emask[e]));
+  return true;
 }
 
 // ------------------------------------------------------------------ S: scan and permutation
@@ -643,7 +696,8 @@ ETC_DEV void write_plan(KArgs& p, KLayer& L, int layer, int RT) {
   st_shared(L.plan + PL_NF, nf);
   st_shared(L.plan + PL_NS, nS);
   st_shared(L.plan + PL_GPC, gpc);
-  st_shared(L.plan + PL_NEXTBASE, base + n_rt + p.n_perm + ngu + nd + nf);
+  st_shared(L.plan + PL_NEXTBASE, base + p.n_rq + p.n_perm + ngu + nd + nf);
+  st_shared(L.plan + PL_Q, p.Q);
 }
 
 // S for a layer of a single routing tile, run by that tile's R task straight from its
@@ -1122,8 +1176,8 @@ ETC_DEV bool claim_static(KArgs& p, Task& t, Smem& sm) {
     }
     KLayer& L = p.layer[l];
     t.layer = l;
-    if (ticket < base + p.n_rt) { t.kind = K_R; t.a = ticket - base; return true; }
-    int off = ticket - base - p.n_rt;
+    if (ticket < base + p.n_rq) { t.kind = K_R; t.a = ticket - base; return true; }
+    int off = ticket - base - p.n_rq;
     if (off < p.n_perm) { t.kind = K_P; t.a = off; return true; }
     off -= p.n_perm;
     if (!(sm.scan_seen >> l & 1u)) {
@@ -1159,11 +1213,11 @@ ETC_DEV bool claim_static(KArgs& p, Task& t, Smem& sm) {
   return true;
 }
 
-// Dynamic: the next queue slot; slots below n_rt are the first layer's R tasks.  The
+// Dynamic: the next queue slot; slots below n_rq are the first layer's R tasks.  The
 // watchdog counts progress as tasks being pushed anywhere (the queue tail moving).
 ETC_DEV bool claim_dynamic(KArgs& p, Task& t) {
   const int slot = ev_add_relaxed(p.sched + W_QHEAD, 1);
-  if (slot < p.n_rt) {
+  if (slot < p.n_rq) {
     t.kind = K_R; t.layer = 0; t.a = slot;
     return true;
   }
@@ -1199,7 +1253,7 @@ ETC_DEV bool wait_deps(KArgs& p, const Task& t, Smem& sm) {
   switch (t.kind) {
     case K_R:
       if (t.layer == 0) return true;
-      return spin_until_geq(p.layer[t.layer - 1].ev_done + t.a, 1, p.sched, p.timeout_ticks, 20);
+      return spin_until_geq(p.layer[t.layer - 1].ev_done + t.a / p.Q, 1, p.sched, p.timeout_ticks, 20);
     case K_P:
       return spin_until_geq(L.ev_scan, 1, p.sched, p.timeout_ticks, 24);
     case K_GU:
@@ -1240,7 +1294,7 @@ ETC_DEV void load_layer_cache(KArgs& p, int l, Smem& sm) {
 // Enqueue n tasks (dynamic mode); every thread of the workgroup calls this.
 template <typename Gen>
 ETC_DEV void push_many(KArgs& p, Smem& sm, int n, Gen gen) {
-  if (threadIdx.x == 0) sm.ibuf[0] = p.n_rt + ev_add_relaxed(p.sched + W_QTAIL, n);
+  if (threadIdx.x == 0) sm.ibuf[0] = p.n_rq + ev_add_relaxed(p.sched + W_QTAIL, n);
   __syncthreads();
   const int base = sm.ibuf[0];
   // the results these tasks read were published (publish_shared) before the call
@@ -1250,7 +1304,7 @@ ETC_DEV void push_many(KArgs& p, Smem& sm, int n, Gen gen) {
 
 // The results the task reads were published (publish_shared) before the call.
 ETC_DEV void push_one(KArgs& p, const Task& t) {
-  const int slot = p.n_rt + ev_add_relaxed(p.sched + W_QTAIL, 1);
+  const int slot = p.n_rq + ev_add_relaxed(p.sched + W_QTAIL, 1);
   q_store_relaxed(p.queue + slot, enc(t));
 }
 
@@ -1291,7 +1345,7 @@ ETC_DEV void after_scan(KArgs& p, int layer, Smem& sm) {
   if (threadIdx.x == 0) {
     // the plan words are in global memory, written by this thread before publish_shared
     const int added = p.n_perm + gp(L.plan)[PL_NGU] + gp(L.plan)[PL_ND] + gp(L.plan)[PL_NF] +
-                      (layer + 1 < p.L ? p.n_rt : 0) + (layer == 0 ? p.n_rt : 0);
+                      (layer + 1 < p.L ? p.n_rq : 0) + (layer == 0 ? p.n_rq : 0);
     ev_add_relaxed(p.sched + W_QTOTAL, added);
     ev_add(p.sched + W_PLANNED, 1);
   }
@@ -1317,8 +1371,8 @@ ETC_DEV void run_task(KArgs& p, KLayer& L, const Task& t, Smem& sm) {
   const int tid = threadIdx.x;
   if (t.kind == K_R && p.n_rt == 1) {
     // the layer's only routing tile: S follows on the tile's LDS results, and one
-    // publish covers both
-    route_task<TE>(p, L, t.a, sm);
+    // publish covers both (in the slice that completed the tile)
+    if (!route_task<TE>(p, L, t.a, sm)) return;
     __syncthreads();
     const uint64_t t0 = now_ticks();
     scan_single_tile(p, L, t.layer, sm);
@@ -1330,7 +1384,7 @@ ETC_DEV void run_task(KArgs& p, KLayer& L, const Task& t, Smem& sm) {
       trace_record(p, st, t0, t0, now_ticks());
     }
   } else if (t.kind == K_R) {
-    route_task<TE>(p, L, t.a, sm);
+    if (!route_task<TE>(p, L, t.a, sm)) return;  // another slice completes the tile
     publish_shared();
     if (tid == 0) {
       // the last routing tile of the layer runs S, which reads every tile's results
@@ -1409,9 +1463,13 @@ ETC_DEV void run_task(KArgs& p, KLayer& L, const Task& t, Smem& sm) {
     if (tid == 0) {
       ev_store_relaxed(L.ev_done + t.a, 1);
       if (p.mode == ETC_SCHED_DYNAMIC && t.layer + 1 < p.L) {
-        Task r;
-        r.kind = K_R; r.layer = t.layer + 1; r.a = t.a; r.b = r.c = r.d = 0;
-        push_one(p, r);
+        // the next layer's router slices of these tokens
+        const int slot = p.n_rq + ev_add_relaxed(p.sched + W_QTAIL, p.Q);
+        for (int q = 0; q < p.Q; ++q) {
+          Task r;
+          r.kind = K_R; r.layer = t.layer + 1; r.a = t.a * p.Q + q; r.b = r.c = r.d = 0;
+          q_store_relaxed(p.queue + slot + q, enc(r));
+        }
       }
     }
     __syncthreads();
@@ -1485,8 +1543,8 @@ ETC_DEV int sched_decode(KArgs& p, const SchedSmem& S, int c, Task& t) {
     const int base = S.base[l];
     if (base < 0) return 1;
     t.layer = l;
-    if (c < base + p.n_rt) { t.kind = K_R; t.a = c - base; return 0; }
-    int off = c - base - p.n_rt;
+    if (c < base + p.n_rq) { t.kind = K_R; t.a = c - base; return 0; }
+    int off = c - base - p.n_rq;
     if (off < p.n_perm) { t.kind = K_P; t.a = off; return 0; }
     off -= p.n_perm;
     if (!(S.planned >> l & 1)) return 1;
@@ -1519,7 +1577,7 @@ ETC_DEV const int* sched_dep(KArgs& p, const SchedSmem& S, const Task& t, int& t
   switch (t.kind) {
     case K_R:
       target = 1;
-      return t.layer == 0 ? nullptr : p.layer[t.layer - 1].ev_done + t.a;
+      return t.layer == 0 ? nullptr : p.layer[t.layer - 1].ev_done + t.a / p.Q;
     case K_P:
       target = 1;
       return L.ev_scan;
@@ -1916,6 +1974,7 @@ __global__ __launch_bounds__(MNT) void moe_kernel(Args pk) {
       for (int i = tid; i < p.n_rt_cap; i += MNT) {
         ev_store_relaxed(L.ev_comb + i, 0);
         ev_store_relaxed(L.ev_done + i, 0);
+        ev_store_relaxed(L.ev_rq + i, 0);
       }
     }
     if (tid == 0) ev_store_relaxed(p.sched + W_TRACE_LAST, ev_load_relaxed(p.sched + W_TRACE));
@@ -1928,10 +1987,10 @@ __global__ __launch_bounds__(MNT) void moe_kernel(Args pk) {
 // ------------------------------------------------------------------ host side
 
 struct Layout {
-  size_t sched, queue, trace, xq, hbuf, out_acc, ybuf, act, total;
+  size_t sched, queue, trace, xq, hbuf, out_acc, ybuf, act, rpart, total;
   struct {
     size_t topk_idx, topk_w, lrank, hist, tile_off, counts, offsets, rt_base, sorted_assign, pos,
-        plan, ev_route, ev_scan, ev_perm, ev_gu, ev_comb, ev_done;
+        plan, ev_route, ev_scan, ev_perm, ev_gu, ev_comb, ev_done, ev_rq;
   } l[MAXL];
   int n_rt, max_rt, n1, n2, queue_len;
 };
@@ -1951,12 +2010,13 @@ inline Layout layout(int Tm, int H, int E, int K, int F, int nl, int es, bool or
     Y.l[l].ev_gu = c.take((size_t)Y.max_rt * Y.n1 * sizeof(int));
     Y.l[l].ev_comb = c.take((size_t)Y.n_rt * sizeof(int));
     Y.l[l].ev_done = c.take((size_t)Y.n_rt * sizeof(int));
+    Y.l[l].ev_rq = c.take((size_t)Y.n_rt * sizeof(int));
     Y.l[l].plan = c.take(PL_WORDS * sizeof(int));
   }
-  const long per_layer = (long)Y.n_rt * 4 + (long)Y.max_rt * Y.n1 + 2L * MAX_WORKERS +
+  const long per_layer = (long)Y.n_rt * (4 + RQ_MAX) + (long)Y.max_rt * Y.n1 + 2L * MAX_WORKERS +
                          (long)Y.max_rt * Y.n2 + 64;
   // + room for the one extra slot each worker draws before it sees the end
-  Y.queue_len = (int)(Y.n_rt + per_layer * nl + 2 * MAX_WORKERS);  // dedicated: two slots per worker
+  Y.queue_len = (int)(Y.n_rt * RQ_MAX + per_layer * nl + 2 * MAX_WORKERS);  // dedicated: two slots per worker
   Y.queue = c.take((size_t)Y.queue_len * sizeof(long long));
   Y.trace = c.take((size_t)Y.queue_len * 32);  // one record per task at most
   for (int l = 0; l < nl; ++l) {
@@ -1977,6 +2037,7 @@ inline Layout layout(int Tm, int H, int E, int K, int F, int nl, int es, bool or
   Y.out_acc = c.take((size_t)Tm * H * 4);
   Y.ybuf = ordered ? c.take((size_t)Tm * K * H * 4) : 0;
   Y.act = c.take((size_t)(nl > 1 ? nl - 1 : 0) * Tm * H * es);
+  Y.rpart = c.take((size_t)NRQ_CAP * BT * E * sizeof(float));
   Y.total = c.off;
   return Y;
 }
@@ -2045,6 +2106,7 @@ ETC_API etc_status etc_moe_workspace_layout(int32_t max_tokens, int32_t hidden, 
   out[13] = (int64_t)Y.trace;
   out[14] = Y.queue_len;
   out[15] = (int64_t)Y.l[layer].ev_perm;
+  out[16] = (int64_t)Y.l[layer].ev_rq;
   return ETC_OK;
 }
 
@@ -2111,10 +2173,20 @@ ETC_API etc_status etc_moe_layer(int32_t T, int32_t H, int32_t E, int32_t K, int
   if (mode == ETC_SCHED_DEDICATED && grid > moe::DED_MAX_GRID) grid = moe::DED_MAX_GRID;
   if (mode == ETC_SCHED_DEDICATED && grid < 2) return ETC_ERR_INVALID_ARG;
   p.workers = grid;
+  // router slices: when the routing tiles leave at least half the workers idle, each
+  // tile's router is cut into Q slices along K (at most RQ_MAX, and NRQ_CAP slice records)
+  {
+    const int wk = mode == ETC_SCHED_DEDICATED ? grid - 1 : grid;
+    int Q = 1;
+    if (p.n_rt * 2 <= wk) Q = std::min(moe::RQ_MAX, std::min(wk / p.n_rt, moe::NRQ_CAP / p.n_rt));
+    p.Q = Q < 1 ? 1 : Q;
+    p.n_rq = p.n_rt * p.Q;
+  }
   p.xq = ws + Y.xq;
   p.hbuf = ws + Y.hbuf;
   p.out_acc = reinterpret_cast<float*>(ws + Y.out_acc);
   p.ybuf = combine == ETC_COMBINE_ORDERED ? reinterpret_cast<float*>(ws + Y.ybuf) : nullptr;
+  p.rpart = reinterpret_cast<float*>(ws + Y.rpart);
   p.queue = reinterpret_cast<long long*>(ws + Y.queue);
   p.trace = reinterpret_cast<unsigned long long*>(ws + Y.trace);
   p.trace_cap = Y.queue_len;
@@ -2155,6 +2227,7 @@ ETC_API etc_status etc_moe_layer(int32_t T, int32_t H, int32_t E, int32_t K, int
     L.ev_gu = reinterpret_cast<int*>(ws + Y.l[l].ev_gu);
     L.ev_comb = reinterpret_cast<int*>(ws + Y.l[l].ev_comb);
     L.ev_done = reinterpret_cast<int*>(ws + Y.l[l].ev_done);
+    L.ev_rq = reinterpret_cast<int*>(ws + Y.l[l].ev_rq);
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -32,6 +32,12 @@ down projection split along ffn into chunks of GPC gate/up tiles:
 reading (few routing tiles): with at most Plan.PI routing tiles S also scatters the
 permutation and there are no P tasks (a hand-off less on a short critical path).
 
+reading (router slices, Plan.Q > 1): the router of a routing tile is cut along H into Q
+slice tasks R(tau*Q + q), each waiting like R(tau) and signalling rq[l][tau] += 1; the
+slice whose signal completes rq[l][tau] (target Q) finishes the tile in the same worker
+and signals route[l] += 1.  Like S, that finish is not a task of its own: it is the
+task's `finish` field, (counter, target, counter it then signals).
+
 S is not a ticket of its own: in both modes the R task whose signal completes
 route[l] (the last arriver) runs it.  Static mode runs the other tasks in one fixed
 ticket order (per layer: all R, all P, all GU, all D, all F) and each worker spins on
@@ -59,6 +65,7 @@ class Plan:
     BN2: int  # hidden columns per down tile
     GPC: int  # gate/up tiles per down chunk (ffn split of the down projection)
     PI: int = 0  # up to this many routing tiles S scatters the permutation (no P tasks)
+    Q: int = 1  # router slices per routing tile
 
 
 @dataclass
@@ -68,6 +75,8 @@ class Task:
     key: tuple
     waits: list = field(default_factory=list)  # [(counter, target)]
     signals: list = field(default_factory=list)  # [(counter, amount)]
+    finish: tuple = None  # (counter, target, next): when the task's signal completes
+    #                       counter, the same worker then signals next += 1
 
 
 def layer_shape(T, H, F, plan):
@@ -88,9 +97,15 @@ def build_layer(l, T, H, F, k, counts, plan, tokens_of_rows):
     n_rt, n1, n2, nS = layer_shape(T, H, F, plan)
     tile_rows = rows_per_routing_tile(T, plan)
     R, GU, D, Fin = [], [], [], []
+    Q = plan.Q
     for tau in range(n_rt):
         waits = [(("done", l - 1, tau), 1)] if l > 0 else []
-        R.append(Task("R", l, (tau,), waits, [(("route", l), 1)]))
+        if Q == 1:
+            R.append(Task("R", l, (tau,), waits, [(("route", l), 1)]))
+        else:
+            for q in range(Q):
+                R.append(Task("R", l, (tau * Q + q,), list(waits), [(("rq", l, tau), 1)],
+                              finish=(("rq", l, tau), Q, ("route", l))))
     if n_rt <= plan.PI:
         S = Task("S", l, (), [(("route", l), n_rt)], [(("scan", l), 1), (("perm", l), n_rt)])
         P = []
@@ -126,12 +141,18 @@ def build_graph(T, H, F, k, layer_counts, layer_tokens_of_rows, plan):
 
 
 def expected_final_counters(graph):
-    """Every counter's value once all tasks have signalled."""
+    """Every counter's value once all tasks have signalled (and every router slice
+    counter has been completed once, moving its `next` counter by one)."""
     final = {}
+    finishes = set()
     for R, S, P, GU, D, Fin in graph:
         for t in R + [S] + P + GU + D + Fin:
             for ctr, amt in t.signals:
                 final[ctr] = final.get(ctr, 0) + amt
+            if t.finish is not None:
+                finishes.add((t.finish[0], t.finish[2]))
+    for _, nxt in finishes:
+        final[nxt] = final.get(nxt, 0) + 1
     return final
 
 
@@ -144,17 +165,30 @@ def static_order(graph):
 
 
 def _scan_of(graph):
-    """S of each layer by the route counter its last R completes."""
-    return {("route", l): (g[1], len(g[0])) for l, g in enumerate(graph)}
+    """S of each layer by the route counter its last routing tile completes (its target
+    is the number of routing tiles)."""
+    return {("route", l): (g[1], g[1].waits[0][1]) for l, g in enumerate(graph)}
+
+
+def _run_finish(task, before, counters):
+    """A router slice whose signal completed its tile's slice counter finishes the tile
+    in the same worker (its `next` counter moves by one)."""
+    if task.finish is not None:
+        ctr, target, nxt = task.finish
+        if before.get(ctr, 0) < target <= counters.get(ctr, 0):
+            counters[nxt] = counters.get(nxt, 0) + 1
 
 
 def _run_inline_scan(task, before, counters, scans, executed):
-    """If ``task`` (an R) completed its layer's route counter, S runs right after it in
-    the same worker.  Returns S or None."""
-    for ctr, _ in task.signals:
+    """After ``task`` (an R, or a router slice that finished its tile) signalled: if its
+    layer's route counter is now complete, S runs right after it in the same worker.
+    Returns S or None."""
+    _run_finish(task, before, counters)
+    ctrs = [c for c, _ in task.signals] + ([task.finish[2]] if task.finish else [])
+    for ctr in ctrs:
         if ctr in scans:
             S, n_rt = scans[ctr]
-            if before.get(ctr, 0) < n_rt <= counters[ctr]:
+            if before.get(ctr, 0) < n_rt <= counters.get(ctr, 0):
                 assert _ready(S, counters)
                 _signal(S, counters)
                 executed.append(S)
@@ -265,7 +299,11 @@ def simulate_dynamic(graph, workers, rng=None):
             dd.setdefault((e, m, s), []).append(t)
         d_by_chunk.append(dd)
         f_by_tau.append({t.key[0]: t for t in Fin})
-        r_by_tau.append({t.key[0]: t for t in R})
+        rt = {}
+        for t in R:  # the routing tasks (slices) of each tile
+            tau = t.finish[0][2] if t.finish else t.key[0]
+            rt.setdefault(tau, []).append(t)
+        r_by_tau.append(rt)
     total = sum(len(R) + len(P) + len(GU) + len(D) + len(Fin) + 1 for R, S, P, GU, D, Fin in graph)
     while len(executed) < total:
         while queue and len(running) < workers:
@@ -277,13 +315,16 @@ def simulate_dynamic(graph, workers, rng=None):
             raise RuntimeError(f"task {t.kind}{t.key} was queued before it was ready")
         before = dict(counters)
         _signal(t, counters)
+        _run_finish(t, before, counters)
         executed.append(t)
         l = t.layer
         R, S, P, GU, D, Fin = graph[l]
-        for ctr, amt in t.signals:
-            old, new = before.get(ctr, 0), counters[ctr]
+        n_rt = S.waits[0][1]
+        ctrs = [c for c, _ in t.signals] + ([t.finish[2]] if t.finish else [])
+        for ctr in ctrs:
+            old, new = before.get(ctr, 0), counters.get(ctr, 0)
             kind = ctr[0]
-            if kind == "route" and new == len(R) and old < new:
+            if kind == "route" and new == n_rt and old < new:
                 # the last routing tile runs S inline; S queues the P tasks, or the GU
                 # tasks when it scattered the permutation itself
                 assert _ready(S, counters)
@@ -302,7 +343,7 @@ def simulate_dynamic(graph, workers, rng=None):
                 if old < ft.waits[0][1] <= new:
                     queue.append(ft)
             elif kind == "done" and l + 1 < layers:
-                queue.append(r_by_tau[l + 1][ctr[2]])
+                queue.extend(r_by_tau[l + 1][ctr[2]])
     return executed, counters
 
 
@@ -317,7 +358,9 @@ def check_execution(executed, graph):
         seen.add(ident)
         if not _ready(t, counters):
             raise AssertionError(f"{ident} ran before its dependencies")
+        before = dict(counters)
         _signal(t, counters)
+        _run_finish(t, before, counters)
     n = sum(len(R) + 1 + len(P) + len(GU) + len(D) + len(Fin) for R, S, P, GU, D, Fin in graph)
     if len(seen) != n:
         raise AssertionError(f"{len(seen)} of {n} tasks ran")

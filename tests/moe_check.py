@@ -147,12 +147,13 @@ def check_event_tensor(read_i32, layout, T, H, F, k, E, gpu, layers):
     for l in range(layers):
         lay = layout(l)
         max_rt, n1, n_rt_cap, BT, BM, BN1, BN2 = lay[6:13]
-        RT, ngu, nd, nf, nS, gpc = (int(v) for v in read_i32(lay[5], 8)[:6])
+        pw = [int(v) for v in read_i32(lay[5], 8)]
+        RT, ngu, nd, nf, nS, gpc, Q = pw[0], pw[1], pw[2], pw[3], pw[4], pw[5], pw[7]
         counts = gpu["counts"][l]
         sa = gpu["sa"][l]
         off = np.concatenate([[0], np.cumsum(counts)])
         tors = [list(sa[off[e]:off[e + 1]] // k) for e in range(E)]
-        plan = sm.Plan(BT=BT, BM=BM, BN1=BN1, BN2=BN2, GPC=gpc, PI=PERM_INLINE_RT)
+        plan = sm.Plan(BT=BT, BM=BM, BN1=BN1, BN2=BN2, GPC=gpc, PI=PERM_INLINE_RT, Q=Q)
         final = sm.expected_final_counters(sm.build_graph(T, H, F, k, [counts], [tors], plan))
         n_rt, n1m, n2, nSm = sm.layer_shape(T, H, F, plan)
         assert (n1m, nSm) == (n1, nS) and RT == sum(-(-int(c) // BM) for c in counts)
@@ -174,6 +175,12 @@ def check_event_tensor(read_i32, layout, T, H, F, k, E, gpu, layers):
             assert comb[tau] == final[("comb", 0, tau)], (l, tau)
             assert done[tau] == 1
         assert not comb[n_rt:].any() and not done[n_rt:].any()
+        # router slices: every tile's slice counter ends at Q (untouched with one slice)
+        rq = np.asarray(read_i32(lay[16], n_rt_cap))
+        assert 1 <= Q <= 8
+        for tau in range(n_rt):
+            assert rq[tau] == (final[("rq", 0, tau)] if Q > 1 else 0), (l, tau, rq[tau], Q)
+        assert not rq[n_rt:].any()
 
 
 TRACE_KIND = {"R": 1, "S": 2, "GU": 3, "D": 4, "F": 5, "P": 6}
@@ -213,12 +220,13 @@ def check_trace_causality(records, T, H, F, k, E, gpu, layout, read_i32, layers,
     for l in range(layers):
         lay = layout(l)
         _, _, _, BT, BM, BN1, BN2 = lay[6:13]
-        gpc = int(read_i32(lay[5], 8)[5])
+        pw = [int(v) for v in read_i32(lay[5], 8)]
+        gpc, Q = pw[5], pw[7]
         counts = gpu["counts"][l]
         sa = gpu["sa"][l]
         off = np.concatenate([[0], np.cumsum(counts)])
         tors = [list(sa[off[e]:off[e + 1]] // k) for e in range(E)]
-        plan = sm.Plan(BT=BT, BM=BM, BN1=BN1, BN2=BN2, GPC=gpc, PI=PERM_INLINE_RT)
+        plan = sm.Plan(BT=BT, BM=BM, BN1=BN1, BN2=BN2, GPC=gpc, PI=PERM_INLINE_RT, Q=Q)
         R, S, P, GU, D, Fin = sm.build_layer(l, T, H, F, k, counts, plan, tors)
         tasks += R + [S] + P + GU + D + Fin
     assert len(tasks) == len(index), (len(tasks), len(index))
@@ -226,11 +234,13 @@ def check_trace_causality(records, T, H, F, k, E, gpu, layout, read_i32, layers,
     for t in tasks:
         for ctr, _ in t.signals:
             producers.setdefault(ctr, []).append(t)
+        if t.finish is not None:  # a router slice may be the one that moves `next`
+            producers.setdefault(t.finish[2], []).append(t)
     checked = 0
     for t in tasks:
         i = rec(t)
         for ctr, _ in t.waits:
-            for p in producers[ctr]:
+            for p in {id(x): x for x in producers[ctr]}.values():
                 j = rec(p)
                 if t.kind == "S":
                     assert t_run[i] >= t_run[j], ("S before a routing task", t.layer, p.key)

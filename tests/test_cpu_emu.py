@@ -208,7 +208,8 @@ def test_trace_has_one_record_per_task(lib, mode, T):
         # the scan runs inside the last routing task and keeps a record of its own; with
         # few routing tiles it scatters the permutation too and there are no P tasks
         n_p = 0 if n_rt <= moe_check.PERM_INLINE_RT else n_rt
-        want = {1: n_rt, 2: 1, 3: int(plan[1]), 4: int(plan[2]), 5: int(plan[3]), 6: n_p}
+        # one record per router slice (plan word 7: slices per routing tile)
+        want = {1: n_rt * int(plan[7]), 2: 1, 3: int(plan[1]), 4: int(plan[2]), 5: int(plan[3]), 6: n_p}
         assert got == want, (l, got, want)
     s = trace.summarize(rec)
     assert s["span_us"] > 0 and 0 < s["busy_fraction"] <= 1

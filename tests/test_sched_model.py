@@ -40,6 +40,10 @@ CASES = [
     (1, 4096, 14336, 8, 2, 2, sm.Plan(BT=16, BM=128, BN1=128, BN2=256, GPC=7, PI=4)),
     (64, 4096, 14336, 8, 2, 1, sm.Plan(BT=16, BM=128, BN1=128, BN2=256, GPC=4, PI=4)),
     (33, 256, 192, 8, 3, 3, sm.Plan(BT=8, BM=16, BN1=32, BN2=64, GPC=2, PI=5)),
+    # router slices: each routing tile's router in Q tasks, the last one finishing it
+    (1, 4096, 14336, 8, 2, 2, sm.Plan(BT=16, BM=128, BN1=128, BN2=256, GPC=7, PI=4, Q=8)),
+    (64, 4096, 14336, 8, 2, 1, sm.Plan(BT=16, BM=128, BN1=128, BN2=256, GPC=4, PI=4, Q=3)),
+    (256, 2048, 768, 128, 8, 2, sm.Plan(BT=16, BM=64, BN1=128, BN2=256, GPC=6, PI=4, Q=8)),
 ]
 
 
@@ -173,3 +177,23 @@ def test_splitk_graph():
         for c, a in t.signals:
             counters[c] = counters.get(c, 0) + a
     assert all(counters[t.waits[0][0]] == 8 for t in K)
+
+
+def test_router_slices_finish_each_tile_once():
+    """With Q slices per routing tile, the slice counter of every tile ends at Q, the
+    route counter at the number of tiles (one finish per tile), and S runs after the
+    last finish; a slice whose signal is dropped leaves its tile unfinished and the
+    static schedule stuck."""
+    plan = sm.Plan(BT=16, BM=64, BN1=64, BN2=128, GPC=3, PI=4, Q=4)
+    rng = np.random.default_rng(5)
+    graph = _graph_from_routing(40, 256, 384, 2, 8, [_random_idx(rng, 40, 8, 2)], plan)
+    final = sm.expected_final_counters(graph)
+    R, S, P, GU, D, Fin = graph[0]
+    assert len(R) == 3 * 4 and all(final[("rq", 0, tau)] == 4 for tau in range(3))
+    assert final[("route", 0)] == 3
+    ex = sm.replay_static(graph)
+    assert ex.index(S) > max(ex.index(t) for t in R)
+    dropped = R[5]
+    dropped.signals = []
+    with pytest.raises(RuntimeError):
+        sm.simulate_static(graph, 3, random.Random(0))
