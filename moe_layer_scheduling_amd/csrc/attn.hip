@@ -47,6 +47,9 @@ constexpr int MAXG = 8;          // query heads per KV head
 constexpr int MAXB = 2048;       // requests per call
 constexpr int REC = HD + 4;      // floats per partial record and head: o[HD], m, l, pad
 constexpr int TPW = CH / 4;      // tokens per wave: 64
+// each (request, KV head) counter has a 128-byte line of its own, so that merges polling
+// one counter do not hold up the partials signalling the others
+constexpr int EV_STRIDE = W_LINE;
 
 struct Args {
   int B, HKV, G;
@@ -64,7 +67,7 @@ struct Args {
   int cap;              // partial records the workspace holds
   long long max_total;  // the workspace's capacity in tokens over all requests
   int* sched;
-  int* ev;              // [B][HKV]
+  int* ev;              // [B][HKV] counters, EV_STRIDE words apart
   uint64_t timeout_ticks;
 };
 
@@ -170,7 +173,7 @@ ETC_DEV void partial_task(const Args& p, Smem& sm, int b, int g, int c, int rec)
   // the workgroup's next ticket, drawn while this chunk's loads are in flight (a later
   // ticket than the running one, so the order stays deadlock-free: every partial ticket
   // precedes every merge ticket, and a partial never waits)
-  if (tid == 0) sm.next = atomicAdd(p.sched + W_TICKET, 1);
+  if (tid == 0) sm.next = (int)gridDim.x + ticket_inc(p.sched + W_TICKET);
 
   // scores of the wave's 64 tokens: block j holds heads 4*grp + r (rows) x tokens
   // 16j + q16 (columns)
@@ -388,12 +391,14 @@ __global__ __launch_bounds__(NT) void attn_kernel(Args p) {
   const int nmerge = p.B * p.HKV;
   const int total = !valid ? 0 : (p.mode == ETC_SCHED_STATIC ? np + nmerge : np);
 
-  if (tid == 0) sm.next = -1;
+  // the first gridDim tickets go to the workgroups by index (every workgroup of the grid
+  // is resident); the counter hands out the later ones
+  if (tid == 0) sm.next = (int)blockIdx.x;
   while (true) {
     if (tid == 0) {
       // (no check of the abort flag here: partial tasks never wait, and a merge's wait
       // sees the flag and gives up, so every workgroup still leaves after an abort)
-      const int t = sm.next >= 0 ? sm.next : atomicAdd(p.sched + W_TICKET, 1);
+      const int t = sm.next >= 0 ? sm.next : (int)gridDim.x + ticket_inc(p.sched + W_TICKET);
       sm.next = -1;
       sm.task = t;
     }
@@ -410,10 +415,15 @@ __global__ __launch_bounds__(NT) void attn_kernel(Args p) {
       partial_task(p, sm, b, g, c, t);
       publish_shared();
       if (tid == 0) {
-        // dynamic: the last arriver merges, so its signal acquires every other partial
-        const int old = (p.mode == ETC_SCHED_DYNAMIC) ? ev_add_acquire(p.ev + b * p.HKV + g, 1)
-                                                      : ev_add_relaxed(p.ev + b * p.HKV + g, 1);
-        sm.flag = (p.mode == ETC_SCHED_DYNAMIC && old == nb - 1) ? 1 : 0;
+        int* ctr = p.ev + EV_STRIDE * (b * p.HKV + g);
+        if (p.mode == ETC_SCHED_DYNAMIC) {
+          // the last arriver merges, so its signal acquires every other partial
+          sm.flag = ev_add_acquire(ctr, 1) == nb - 1 ? 1 : 0;
+        } else {
+          // nothing waits on the result: the atomic goes out without a return
+          __hip_atomic_fetch_add(gp(ctr), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          sm.flag = 0;
+        }
       }
       __syncthreads();
       if (sm.flag) merge_task(p, sm, b, g, sm.pbase[b] + g * nb, nb);
@@ -421,7 +431,7 @@ __global__ __launch_bounds__(NT) void attn_kernel(Args p) {
     } else {
       const int bg = t - np, b = bg / p.HKV, g = bg % p.HKV;
       const int nb = sm.nsplit[b];
-      if (tid == 0) sm.flag = spin_until_geq(p.ev + bg, nb, p.sched, p.timeout_ticks, 30) ? 1 : 0;
+      if (tid == 0) sm.flag = spin_until_geq(p.ev + EV_STRIDE * bg, nb, p.sched, p.timeout_ticks, 30) ? 1 : 0;
       __syncthreads();
       if (sm.flag) merge_task(p, sm, b, g, sm.pbase[b] + g * nb, nb);
       __syncthreads();
@@ -433,7 +443,7 @@ __global__ __launch_bounds__(NT) void attn_kernel(Args p) {
   if (tid == 0) sm.flag = (atomicAdd(p.sched + W_EXIT, 1) == (int)gridDim.x - 1) ? 1 : 0;
   __syncthreads();
   if (sm.flag && !(p.flags & ETC_FLAG_KEEP_COUNTERS)) {
-    for (int i = tid; i < p.B * p.HKV; i += NT) ev_store_relaxed(p.ev + i, 0);
+    for (int i = tid; i < p.B * p.HKV; i += NT) ev_store_relaxed(p.ev + EV_STRIDE * i, 0);
     for (int i = tid; i < W_NWORDS; i += NT)
       if (i != W_STATUS && i != W_AUX) ev_store_relaxed(p.sched + i, 0);
   }
@@ -452,7 +462,7 @@ inline Layout layout(int B, int HKV, int G, long max_total_tokens) {
   Y.cap = (int)((max_total_tokens / CH + B) * HKV);
   host::Carve c;
   Y.sched = c.take(W_NWORDS * sizeof(int));
-  Y.ev = c.take((size_t)B * HKV * sizeof(int));
+  Y.ev = c.take((size_t)B * HKV * EV_STRIDE * sizeof(int));
   Y.part = c.take((size_t)Y.cap * G * REC * sizeof(float));
   Y.total = c.off;
   return Y;

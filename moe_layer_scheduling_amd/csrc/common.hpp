@@ -20,6 +20,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 // 16 raw bytes as a native vector: copies are register moves, never memcpy through memory
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct bf16 {
   uint16_t bits;
@@ -251,7 +252,7 @@ enum SchedWord {
 };
 constexpr int MAX_XCD_QUEUES = 8;  // MI355X: 8 XCDs of 32 CUs, each with its own L2
 
-// Static tickets through per-XCD queues (thread 0 of a workgroup calls this).  A fixed
+// Static tickets through per-XCD queues (thread 0 of a workgroup calls these).  A fixed
 // task order is cut into chunks of G = workers / Q consecutive tasks, chunk c belonging
 // to queue c mod Q (Q = min(8, workers)); workgroup b draws the next ticket of queue
 // b mod Q.  The dispatcher places workgroup b on XCD b mod 8, so with Q = 8 each chunk
@@ -259,15 +260,46 @@ constexpr int MAX_XCD_QUEUES = 8;  // MI355X: 8 XCDs of 32 CUs, each with its ow
 // queue hands out its tickets in the global order and has at least one workgroup, so a
 // waiting task's producers, which come earlier in the order, are always claimed by
 // workgroups that can run them: the order stays deadlock-free.
-ETC_DEV int xcd_ticket(int* sched) {
+//
+// Every workgroup of the grid is resident (the grid never exceeds what the device holds
+// at once), so the first draw needs no atomic: member m = b / Q of queue q takes the
+// queue's m-th ticket, and the counter of queue q hands out the later ones, starting
+// after the queue's n_q members.  That removes one atomic round trip from the start of
+// every call.
+ETC_DEV int xcd_ticket_of(int q, int i) {  // the i-th ticket of queue q
   const int nwg = (int)gridDim.x;
   const int Q = nwg < MAX_XCD_QUEUES ? nwg : MAX_XCD_QUEUES;
   const int G = nwg / Q;
-  const int q = (int)blockIdx.x % Q;
-  const int i = __hip_atomic_fetch_add(gp(sched + W_XTICKET + q * W_LINE), 1, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
   return ((i / G) * Q + q) * G + i % G;
 }
+ETC_DEV int xcd_first_ticket() {
+  const int nwg = (int)gridDim.x;
+  const int Q = nwg < MAX_XCD_QUEUES ? nwg : MAX_XCD_QUEUES;
+  return xcd_ticket_of((int)blockIdx.x % Q, (int)blockIdx.x / Q);
+}
+// The next value of a ticket counter (relaxed, agent scope).  An increment that wraps at
+// 2^32 - 1 is a plain increment here; unlike an atomic add it is left alone by the
+// compiler's wave-level atomic aggregation, which reads the result back at once (a wait
+// for every memory operation issued before the atomic) to spread it over the lanes.
+ETC_DEV int ticket_inc(int* counter) {
+  return (int)__builtin_amdgcn_atomic_inc32((unsigned*)gp(counter), 0xffffffffu, __ATOMIC_RELAXED, "agent");
+}
+
+// A later ticket in two steps: the draw (the atomic) and its mapping, so that a caller
+// can keep the atomic in flight and map the result only where it needs the ticket.
+ETC_DEV int xcd_ticket_draw(int* sched) {
+  const int nwg = (int)gridDim.x;
+  const int Q = nwg < MAX_XCD_QUEUES ? nwg : MAX_XCD_QUEUES;
+  return ticket_inc(sched + W_XTICKET + ((int)blockIdx.x % Q) * W_LINE);
+}
+ETC_DEV int xcd_ticket_map(int drawn) {
+  const int nwg = (int)gridDim.x;
+  const int Q = nwg < MAX_XCD_QUEUES ? nwg : MAX_XCD_QUEUES;
+  const int q = (int)blockIdx.x % Q;
+  const int members = (nwg - q + Q - 1) / Q;  // workgroups b < nwg with b mod Q == q
+  return xcd_ticket_of(q, members + drawn);
+}
+ETC_DEV int xcd_ticket(int* sched) { return xcd_ticket_map(xcd_ticket_draw(sched)); }
 
 // Waits poll with relaxed loads (no cache invalidation per poll: an agent-scope acquire
 // invalidates this CU's L1 and the XCD's L2 lines, which would keep evicting the operands

@@ -23,9 +23,11 @@
 // CU streams at once.  A stage holds the
 // A block [64 rows][64 k] (rows of 128 bytes, chunks swizzled as in mfma.hpp) and the B
 // block [64 k][128 n] (rows of 256 bytes).  B is N-contiguous while the MFMA wants 8
-// consecutive k per lane, so each lane gathers its 8 values with 2-byte LDS reads; the
-// 16-byte chunk c of B row r sits at position c ^ ((r / 8) % 16), which puts the four
-// k groups of a quarter-wave in different banks.
+// consecutive k per lane, so a lane's B fragment comes from two transposed LDS reads
+// (gfx950 ds_read_b64_tr_b16, 4 k each; see lds_read_tr16).  The 16-byte chunk c of B
+// row r sits at position c ^ bsw(r) with bsw(r) = 2 * ((r % 4) + 4 * ((r / 8) % 2)): the
+// 16 rows one transposed read touches fall on 8 different chunk pairs, two rows each,
+// which is as few bank conflicts as 512 bytes per read allow.
 #include <mutex>
 
 #include "common.hpp"
@@ -36,6 +38,11 @@ namespace etc {
 namespace splitk {
 
 constexpr int TM = 64, TN = 128, BK = 64;
+// Each tile's counter has a 128-byte line of its own: the reductions waiting on one tile
+// poll its line while the partials of the other tiles signal theirs.  With all counters
+// in one line, the polls held up those signals (static split-K 37 -> 32 us when the
+// counters moved apart).
+constexpr int EV_STRIDE = W_LINE;
 constexpr int A_STAGE = TM * 128;                    // bytes (64 rows x 64 bf16)
 constexpr int B_STAGE = BK * TN * 2;                 // bytes (64 k-rows x 128 bf16)
 constexpr int STAGE = A_STAGE + B_STAGE;             // 24 KiB
@@ -56,7 +63,7 @@ struct Args {
   float* C;
   float* part;   // [tiles][S][TM][TN]
   int* sched;    // control words
-  int* ev;       // [tiles]
+  int* ev;       // [tiles] counters, EV_STRIDE words apart
   int* status;   // or null: the last workgroup out copies the status word here
   uint64_t timeout_ticks;
 };
@@ -67,9 +74,53 @@ struct Smem {
   int flag;
 };
 
-ETC_DEV int bswz(int krow, int chunk) { return krow * 256 + ((chunk ^ ((krow >> 3) & 15)) << 4); }
+ETC_DEV int bsw(int krow) { return 2 * ((krow & 3) + 4 * ((krow >> 3) & 1)); }
 
-ETC_DEV void partial_task(const Args& p, Smem& sm, int tile, int s) {
+// Eight transposed reads of 16-bit values (gfx950 ds_read_b64_tr_b16) at base + off[i].
+// In each group of 16 lanes, lane j gives the address of 4 consecutive values (8 bytes);
+// lanes 4r..4r+3 of the group thus give row r (r = 0..3) of a 4 x 16 block, and lane i
+// of the group receives column i: value r of lane i is value i % 4 at the address of
+// lane 4r + i / 4 (layout checked on the device with a probe of known values).
+// The device code issues them as one block that waits for its own results: through the
+// builtin, the compiler waits for every outstanding direct-to-LDS copy (vmcnt(0))
+// before each such read, which would drain the copy ring every stage; here the ring's
+// explicit waits already order the reads after the copies of their stage.  Results are
+// early-clobber, so no result register shares a register with an address.
+ETC_DEV void lds_read_tr16_x8(u32x2 (&o)[8], const char* base, const uint32_t (&off)[8]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t b = (uint32_t)(uintptr_t)(const ETC_LDS char*)base;
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n\t"
+      "ds_read_b64_tr_b16 %1, %9\n\t"
+      "ds_read_b64_tr_b16 %2, %10\n\t"
+      "ds_read_b64_tr_b16 %3, %11\n\t"
+      "ds_read_b64_tr_b16 %4, %12\n\t"
+      "ds_read_b64_tr_b16 %5, %13\n\t"
+      "ds_read_b64_tr_b16 %6, %14\n\t"
+      "ds_read_b64_tr_b16 %7, %15\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]),
+        "=&v"(o[6]), "=&v"(o[7])
+      : "v"(b + off[0]), "v"(b + off[1]), "v"(b + off[2]), "v"(b + off[3]), "v"(b + off[4]),
+        "v"(b + off[5]), "v"(b + off[6]), "v"(b + off[7])
+      : "memory");
+#else  // host passes: the builtin (the CPU harness supplies it)
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  for (int i = 0; i < 8; ++i) {
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((ETC_LDS s16x4*)(base + off[i]));
+    __builtin_memcpy(&o[i], &v, sizeof(v));
+  }
+#endif
+}
+
+// The partial of (tile, s).  Thread 0 draws the workgroup's next ticket with `draw`
+// right after the first copies go out, so that the atomic's round trip overlaps the
+// stream (it is older than every later copy, so the ring's counted waits stay upper
+// bounds), and maps the result with `map` only at the end: a use of the result inside
+// the stream would make the wave wait for every copy issued before the atomic.  The
+// ticket is in sm.task when the partial returns.
+template <typename Draw, typename Map>
+ETC_DEV void partial_task(const Args& p, Smem& sm, int tile, int s, Draw draw, Map map) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tm = tile / p.tiles_n, tn = tile % p.tiles_n;
@@ -79,7 +130,7 @@ ETC_DEV void partial_task(const Args& p, Smem& sm, int tile, int s) {
 
   // copy sources: A rows 8w + 32i + lane/8 at the chunk its swizzled LDS position holds
   // (rows past M repeat row M-1; their results are not stored); B k-rows 16i + 4w +
-  // lane/16 at chunk (lane % 16) ^ ((row / 8) % 16)
+  // lane/16 at chunk (lane % 16) ^ bsw(row)
   const char* asrc[A_LOADS];
   const char* bsrc[B_LOADS];
   const int lca = (lane & 7) ^ ((4 * w + (lane >> 4)) & 7);
@@ -91,7 +142,7 @@ ETC_DEV void partial_task(const Args& p, Smem& sm, int tile, int s) {
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i) {
     const int r = 16 * i + 4 * w + (lane >> 4);
-    const int c = (lane & 15) ^ ((r >> 3) & 15);
+    const int c = (lane & 15) ^ bsw(r);
     bsrc[i] = reinterpret_cast<const char*>(p.B + (size_t)(kbeg + r) * p.N + n0) + c * 16;
   }
   const size_t bstep = (size_t)BK * p.N * 2;  // bytes of B per stage
@@ -114,6 +165,8 @@ ETC_DEV void partial_task(const Args& p, Smem& sm, int tile, int s) {
 
 #pragma unroll
   for (int i = 0; i < AHEAD; ++i) issue(i);
+  int next = 0;
+  if (tid == 0) next = draw();
   for (int kt = 0; kt < nk; ++kt) {
     // this thread's copies of stage kt have landed (those of the next AHEAD-1 stages may
     // not), then every wave's have, and every wave has finished reading slot
@@ -121,22 +174,33 @@ ETC_DEV void partial_task(const Args& p, Smem& sm, int tile, int s) {
     vm_wait_barrier<(AHEAD - 1) * LOADS>();
     issue(kt + AHEAD);
     const char* base = sm.stage[kt % NSTAGE];
-    const uint16_t* bsm = reinterpret_cast<const uint16_t*>(base + A_STAGE);
+    // B fragments of the stage: lane i16 of k group g gives k-row kk*32 + 8g + 4h + i16/4,
+    // columns n .. n+3 with n = w*32 + j*16 + 4*(i16 % 4); it receives column
+    // w*32 + j*16 + i16 of k-rows kk*32 + 8g + 4h .. +3, so the reads h = 0, 1 hold its
+    // 8 consecutive k of block (kk, j)
+    const int g = lane >> 4, i16 = lane & 15;
+    uint32_t boff[8];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int n = w * 32 + j * 16 + 4 * (i16 & 3);
+          const int r = kk * 32 + 8 * g + 4 * hh + (i16 >> 2);
+          boff[kk * 4 + j * 2 + hh] = A_STAGE + r * 256 + (((n >> 3) ^ bsw(r)) << 4) + ((n & 4) << 1);
+        }
+    u32x2 bt[8];
+    lds_read_tr16_x8(bt, base, boff);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const int g = lane >> 4;
       u32x4 a[4], b[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = lds_chunk_v(base, i * 16 + (lane & 15), kk * 4 + g);
+      for (int i = 0; i < 4; ++i) a[i] = lds_chunk_v(base, i * 16 + i16, kk * 4 + g);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int n = w * 32 + j * 16 + (lane & 15);
-        const int k = kk * 32 + g * 8;
-        const uint16_t* col = bsm + (bswz(k, n >> 3) >> 1) + (n & 7);
-        uint32_t h[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) h[q] = col[q * 128];  // rows k..k+7 share the swizzle
-        b[j] = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
+        const u32x2 lo = bt[kk * 4 + j * 2], hi = bt[kk * 4 + j * 2 + 1];
+        b[j] = u32x4{lo[0], lo[1], hi[0], hi[1]};
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
@@ -170,6 +234,7 @@ ETC_DEV void partial_task(const Args& p, Smem& sm, int tile, int s) {
     st_shared16(dst, (uint32_t)((row * TN + c) * sizeof(float)),
                 u32x4{__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)});
   }
+  if (tid == 0) sm.task = map(next);
 }
 
 // Rows [rc*TM/RCHUNKS, ...) of a C tile = partials summed in slice order.  Every thread
@@ -201,43 +266,51 @@ __global__ __launch_bounds__(NT) void splitk_kernel(Args p) {
   const int tid = threadIdx.x;
   const int nparts = p.tiles * p.S;
   // static: the partials, then RCHUNKS reduction tickets per tile
-  const int total = (p.mode == ETC_SCHED_STATIC) ? nparts + p.tiles * RCHUNKS : nparts;
+  const bool stat = p.mode == ETC_SCHED_STATIC;
+  const int total = stat ? nparts + p.tiles * RCHUNKS : nparts;
+  // Static: partial tickets are slice-major, so a chunk of consecutive tickets (one XCD
+  // queue's share) holds the tiles of one slice, which share its A block.  Dynamic: one
+  // counter; the first gridDim tickets go to the workgroups by index (all are resident),
+  // the counter hands out the rest.  A workgroup draws its next ticket while its current
+  // task runs.  (No check of the abort flag here: partial tasks never wait, and a
+  // reduction's wait sees the flag and gives up, so every workgroup still leaves after
+  // an abort.)
+  auto draw = [&]() ETC_INLINE {
+    return stat ? xcd_ticket_draw(p.sched) : ticket_inc(p.sched + W_QHEAD);
+  };
+  auto map = [&](int drawn) ETC_INLINE { return stat ? xcd_ticket_map(drawn) : (int)gridDim.x + drawn; };
+  int t = stat ? xcd_first_ticket() : (int)blockIdx.x;
 
-  while (true) {
-    if (tid == 0) {
-      // static: partial tickets are slice-major, so a chunk of consecutive tickets (one
-      // XCD queue's share) holds the tiles of one slice, which share its A block
-      // (no check of the abort flag here: partial tasks never wait, and a reduction's
-      // wait sees the flag and gives up, so every workgroup still leaves after an abort)
-      const int t = (p.mode == ETC_SCHED_STATIC) ? xcd_ticket(p.sched) : atomicAdd(p.sched + W_QHEAD, 1);
-      sm.task = t;
-    }
-    __syncthreads();
-    const int t = sm.task;
-    __syncthreads();
-    if (t >= total) break;
-
+  while (t < total) {
     if (t < nparts) {
       const int tile = t % p.tiles, s = t / p.tiles;
-      partial_task(p, sm, tile, s);
+      partial_task(p, sm, tile, s, draw, map);  // leaves the next ticket in sm.task
       publish_shared();
       if (tid == 0) {
-        // dynamic: the last arriver reduces, so its signal acquires every other partial
-        const int old = (p.mode == ETC_SCHED_DYNAMIC) ? ev_add_acquire(p.ev + tile, 1)
-                                                      : ev_add_relaxed(p.ev + tile, 1);
-        sm.flag = (p.mode == ETC_SCHED_DYNAMIC && old == p.S - 1) ? 1 : 0;
+        if (stat) {
+          // nothing waits on the result: the atomic goes out without a return
+          __hip_atomic_fetch_add(gp(p.ev + EV_STRIDE * tile), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          sm.flag = 0;
+        } else {
+          // the last arriver reduces, so its signal acquires every other partial
+          sm.flag = ev_add_acquire(p.ev + EV_STRIDE * tile, 1) == p.S - 1 ? 1 : 0;
+        }
       }
       __syncthreads();
       if (sm.flag)  // last arriver
         for (int rc = 0; rc < RCHUNKS; ++rc) reduce_task(p, tile, rc);
-      __syncthreads();
     } else {
       const int tile = (t - nparts) / RCHUNKS, rc = (t - nparts) % RCHUNKS;
-      if (tid == 0) sm.flag = spin_until_geq(p.ev + tile, p.S, p.sched, p.timeout_ticks, 1) ? 1 : 0;
+      if (tid == 0) {
+        const int next = draw();  // in flight during the wait
+        sm.flag = spin_until_geq(p.ev + EV_STRIDE * tile, p.S, p.sched, p.timeout_ticks, 1) ? 1 : 0;
+        sm.task = map(next);
+      }
       __syncthreads();
       if (sm.flag) reduce_task(p, tile, rc);
-      __syncthreads();
     }
+    t = sm.task;
+    __syncthreads();  // every thread has read sm.task before the next task rewrites it
   }
 
   // the last workgroup out clears the counters for the next call
@@ -246,7 +319,7 @@ __global__ __launch_bounds__(NT) void splitk_kernel(Args p) {
   __syncthreads();
   if (sm.flag && tid == 0 && p.status) gp(p.status)[0] = ev_load_relaxed(p.sched + W_STATUS);
   if (sm.flag && !(p.flags & ETC_FLAG_KEEP_COUNTERS)) {
-    for (int i = tid; i < p.tiles; i += NT) ev_store_relaxed(p.ev + i, 0);
+    for (int i = tid; i < p.tiles; i += NT) ev_store_relaxed(p.ev + EV_STRIDE * i, 0);
     for (int i = tid; i < W_NWORDS; i += NT)
       if (i != W_STATUS && i != W_AUX) ev_store_relaxed(p.sched + i, 0);
   }
@@ -269,7 +342,7 @@ inline Layout layout(int M, int N, int S) {
   L.tiles = cdiv(M, TM) * (N / TN);
   host::Carve c;
   L.sched = c.take(W_NWORDS * sizeof(int));
-  L.ev = c.take((size_t)L.tiles * sizeof(int));
+  L.ev = c.take((size_t)L.tiles * EV_STRIDE * sizeof(int));
   L.part = c.take((size_t)L.tiles * S * TM * TN * sizeof(float));
   L.total = c.off;
   return L;

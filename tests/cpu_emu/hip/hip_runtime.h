@@ -123,6 +123,20 @@ inline unsigned long long emu_ballot(int pred) {
   return m;
 }
 #define __ballot(x) emu_ballot(x)
+
+// Transposed 16-bit LDS read (ds_read_b64_tr_b16): in each group of 16 lanes, value r of
+// lane i is value i % 4 at the address given by lane 4r + i / 4 of the group.
+typedef short emu_s16x4 __attribute__((ext_vector_type(4)));
+inline emu_s16x4 emu_read_tr16(const void* p) {
+  const int lane = emu_lane(), grp = lane & ~15, i = lane & 15;
+  emu_s16x4 out;
+  for (int r = 0; r < 4; ++r) {
+    const uintptr_t a = emu_exchange((uintptr_t)p, grp + 4 * r + i / 4);
+    out[r] = reinterpret_cast<const short*>(a)[i % 4];
+  }
+  return out;
+}
+#define __builtin_amdgcn_ds_read_tr16_b64_v4i16(p) emu_read_tr16((const void*)(p))
 #define __builtin_amdgcn_wave_barrier() emu_wave_barrier()
 inline int __popcll(unsigned long long v) { return __builtin_popcountll(v); }
 
@@ -153,6 +167,15 @@ inline int emu_update_dpp(int old, int src, int ctrl, int row_mask, int bank_mas
 #define __builtin_amdgcn_update_dpp(old, src, ctrl, rm, bm, bc) emu_update_dpp((old), (src), (ctrl), (rm), (bm), (bc))
 
 inline int atomicAdd(int* p, int v) { return __atomic_fetch_add(p, v, __ATOMIC_SEQ_CST); }
+// increment that wraps to 0 past lim (the device's atomic_inc)
+inline unsigned emu_atomic_inc32(unsigned* p, unsigned lim) {
+  unsigned old = __atomic_load_n(p, __ATOMIC_RELAXED);
+  while (!__atomic_compare_exchange_n(p, &old, old >= lim ? 0u : old + 1u, false, __ATOMIC_SEQ_CST,
+                                      __ATOMIC_RELAXED)) {
+  }
+  return old;
+}
+#define __builtin_amdgcn_atomic_inc32(p, lim, order, scope) emu_atomic_inc32((unsigned*)(p), (lim))
 inline unsigned atomicOr(unsigned* p, unsigned v) { return __atomic_fetch_or(p, v, __ATOMIC_SEQ_CST); }
 inline int __popc(unsigned v) { return __builtin_popcount(v); }
 inline float atomicAdd(float* p, float v) {

@@ -171,7 +171,10 @@ def test_event_tensor_final_state(lib, mode):
 
 
 @pytest.mark.parametrize("mode", ["static", "dynamic"])
-def test_splitk(lib, mode):
+@pytest.mark.parametrize("workers", [0, 1, 3, 12])
+def test_splitk(lib, mode, workers):
+    """Grids of 1, 3 and 12 workgroups: XCD queues with one member each, and queues of
+    two members beside queues of one (first tickets by member index)."""
     M, N, K, S = 37, 256, 1024, 4
     A, B = synth.make_splitk(M=M, N=N, K=K, seed=2)
     n = lib.etc_splitk_workspace_size(M, N, S)
@@ -179,7 +182,7 @@ def test_splitk(lib, mode):
     wptr = ws.data_ptr() + (-ws.data_ptr()) % 256
     C = torch.zeros(M, N, dtype=torch.float32)
     assert lib.etc_splitk_gemm(M, N, K, S, A.data_ptr(), B.data_ptr(), C.data_ptr(), wptr, n,
-                               binding.MODES[mode], 0, 0, None) == 0
+                               binding.MODES[mode], 0, workers, None) == 0
     ref = osk.splitk_gemm(synth.as_numpy(A), synth.as_numpy(B), S)
     assert np.max(np.abs(C.numpy() - ref)) <= 1e-3 * np.max(np.abs(ref))
 

@@ -105,10 +105,12 @@ def test_counters_reach_their_length_dependent_targets(mode):
     ws = binding.AttnWorkspace(len(lens), HKV, G, int(np.sum(lens)))
     ref = _ref(q, k, v, start, lens, G, 1 / np.sqrt(128))
     _assert_close(_run(q, k, v, lens, start, mode, ws=ws, flags=binding.FLAG_KEEP_COUNTERS), ref)
-    # the counters follow the block of control words
-    ev = ws.view(binding.CONTROL_BYTES, len(lens) * HKV, torch.int32).cpu().numpy().reshape(len(lens), HKV)
+    # the counters follow the block of control words, one per 128-byte line
+    words = ws.view(binding.CONTROL_BYTES, len(lens) * HKV * 32, torch.int32).cpu().numpy()
+    ev = words[::32].reshape(len(lens), HKV)
     want = np.array([oa.split_count(L, 256) for L in lens])
     assert np.array_equal(ev, np.repeat(want[:, None], HKV, axis=1)), ev
+    assert np.all(np.delete(words, np.arange(0, words.size, 32)) == 0)
     ws.reset()
 
 

@@ -102,6 +102,8 @@ def test_counters_reach_split_k():
     binding.splitk_gemm(A.cuda(), B.cuda(), S, mode="static", workspace=ws,
                         flags=binding.FLAG_KEEP_COUNTERS)
     torch.cuda.synchronize()
-    ev = ws.view(binding.CONTROL_BYTES, N // 128, torch.int32).cpu().numpy()  # counters follow the control words
-    assert np.all(ev == S), ev
+    # the counters follow the control words, one per 128-byte line
+    ev = ws.view(binding.CONTROL_BYTES, (N // 128) * 32, torch.int32).cpu().numpy()
+    assert np.all(ev[::32] == S), ev[::32]
+    assert np.all(np.delete(ev, np.arange(0, ev.size, 32)) == 0)
     ws.reset()
