@@ -421,7 +421,7 @@ __global__ __launch_bounds__(NT) void attn_kernel(Args p) {
           sm.flag = ev_add_acquire(ctr, 1) == nb - 1 ? 1 : 0;
         } else {
           // nothing waits on the result: the atomic goes out without a return
-          __hip_atomic_fetch_add(gp(ctr), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ev_signal(ctr, 1);
           sm.flag = 0;
         }
       }

@@ -130,6 +130,11 @@ ETC_DEV int ev_add_acquire(int* p, int v) {
 ETC_DEV int ev_add_relaxed(int* p, int v) {
   return __hip_atomic_fetch_add(gp(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// A relaxed addition whose result nobody reads: it goes out as an atomic without a
+// return, so the signalling wave does not wait for the round trip.
+ETC_DEV void ev_signal(int* p, int v) {
+  (void)__hip_atomic_fetch_add(gp(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 ETC_DEV void ev_store(int* p, int v) {
   __hip_atomic_store(gp(p), v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -1406,9 +1406,12 @@ ETC_DEV void run_task(KArgs& p, KLayer& L, const Task& t, Smem& sm) {
     perm_task(p, L, t.a);
     publish_shared();
     if (tid == 0) {
-      const int old = (p.mode == ETC_SCHED_DYNAMIC) ? ev_add_acquire(L.ev_perm, 1)
-                                                    : ev_add_relaxed(L.ev_perm, 1);
-      sm.flag = (p.mode == ETC_SCHED_DYNAMIC && old + 1 == p.n_rt) ? 1 : 0;
+      if (p.mode == ETC_SCHED_DYNAMIC) {
+        sm.flag = ev_add_acquire(L.ev_perm, 1) + 1 == p.n_rt ? 1 : 0;
+      } else {
+        ev_signal(L.ev_perm, 1);
+        sm.flag = 0;
+      }
     }
     __syncthreads();
     if (sm.flag) push_gateup(p, L, t.layer, sm);  // the permutation is complete
@@ -1420,9 +1423,12 @@ ETC_DEV void run_task(KArgs& p, KLayer& L, const Task& t, Smem& sm) {
     if (tid == 0) {
       const int rt = sm.lc.rtb[t.a] + t.b;
       const int need = min(gpc, p.n1 - s * gpc);
-      const int old = (p.mode == ETC_SCHED_DYNAMIC) ? ev_add_acquire(L.ev_gu + rt * p.n1 + s, 1)
-                                                    : ev_add_relaxed(L.ev_gu + rt * p.n1 + s, 1);
-      sm.flag = (p.mode == ETC_SCHED_DYNAMIC && old + 1 == need) ? 1 : 0;
+      if (p.mode == ETC_SCHED_DYNAMIC) {
+        sm.flag = ev_add_acquire(L.ev_gu + rt * p.n1 + s, 1) + 1 == need ? 1 : 0;
+      } else {
+        ev_signal(L.ev_gu + rt * p.n1 + s, 1);  // static: nothing reads the old value
+        sm.flag = 0;
+      }
     }
     __syncthreads();
     if (sm.flag) {
@@ -1446,13 +1452,15 @@ ETC_DEV void run_task(KArgs& p, KLayer& L, const Task& t, Smem& sm) {
       if (tid == 0 || sm.u.t.row_tok[tid - 1] / BT != tau) {
         int len = 1;
         while (tid + len < valid && sm.u.t.row_tok[tid + len] / BT == tau) ++len;
-        const int old = (p.mode == ETC_SCHED_DYNAMIC) ? ev_add_acquire(L.ev_comb + tau, len)
-                                                      : ev_add_relaxed(L.ev_comb + tau, len);
-        const int target = tile_rows(p, tau) * p.K * p.n2 * sm.lc.plan[PL_NS];
-        if (p.mode == ETC_SCHED_DYNAMIC && old + len == target) {
-          Task f;
-          f.kind = K_F; f.layer = t.layer; f.a = tau; f.b = f.c = f.d = 0;
-          push_one(p, f);
+        if (p.mode == ETC_SCHED_DYNAMIC) {
+          const int old = ev_add_acquire(L.ev_comb + tau, len);
+          if (old + len == tile_rows(p, tau) * p.K * p.n2 * sm.lc.plan[PL_NS]) {
+            Task f;
+            f.kind = K_F; f.layer = t.layer; f.a = tau; f.b = f.c = f.d = 0;
+            push_one(p, f);
+          }
+        } else {
+          ev_signal(L.ev_comb + tau, len);  // static: nothing reads the old value
         }
       }
     }

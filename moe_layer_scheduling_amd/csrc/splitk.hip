@@ -289,7 +289,7 @@ __global__ __launch_bounds__(NT) void splitk_kernel(Args p) {
       if (tid == 0) {
         if (stat) {
           // nothing waits on the result: the atomic goes out without a return
-          __hip_atomic_fetch_add(gp(p.ev + EV_STRIDE * tile), 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ev_signal(p.ev + EV_STRIDE * tile, 1);
           sm.flag = 0;
         } else {
           // the last arriver reduces, so its signal acquires every other partial
