@@ -308,8 +308,10 @@ ETC_DEV int xcd_ticket(int* sched) { return xcd_ticket_map(xcd_ticket_draw(sched
 
 // Waits poll with relaxed loads (no cache invalidation per poll: an agent-scope acquire
 // invalidates this CU's L1 and the XCD's L2 lines, which would keep evicting the operands
-// of the tiles running beside the waiter) and, once the condition holds, take one
-// acquire load of the same location, which synchronises with the producers.
+// of the tiles running beside the waiter) and, once the condition holds, take an
+// agent-scope acquire fence: the relaxed load that saw the producers' additions plus
+// the fence synchronise with them, and the fence only invalidates this reader's caches,
+// where a second (acquire) load would cost another round trip to the counter.
 //
 // Watchdog.  A wait gives up when what it watches has made no progress for `patience`
 // ticks of the 100 MHz real-time clock: the limit starts when the wait begins and starts
@@ -356,7 +358,7 @@ ETC_DEV bool spin_until_geq(const int* ctr, int target, int* sched, uint64_t pat
   for (int it = 0;; ++it) {
     const int v = ev_load_relaxed(ctr);
     if (v >= target) {
-      (void)ev_load(ctr);  // acquire: everything released before the counter reached it
+      fence_acquire_agent();  // everything released before the counter reached v
       return true;
     }
     if (it == 0) wd.start(patience, v);

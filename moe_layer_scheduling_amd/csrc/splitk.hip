@@ -261,6 +261,42 @@ ETC_DEV void reduce_task(const Args& p, int tile, int rc) {
   if (m < p.M) *reinterpret_cast<float4*>(p.C + (long)m * p.N + tn * TN + col) = sum;
 }
 
+// Rows [rc0*TM/RCHUNKS, (rc0+NC)*TM/RCHUNKS) of a C tile = partials summed in slice
+// order.  Every thread owns one float4 of each of the NC row chunks and has the loads of
+// up to 8 slices of all NC chunks in flight together.
+template <int NC>
+ETC_DEV void reduce_chunks(const Args& p, int tile, int rc0) {
+  constexpr int ROWS = TM / RCHUNKS, F4 = ROWS * TN / 4;  // 8 rows: 256 float4
+  static_assert(F4 == NT, "one float4 per thread");
+  const int tm = tile / p.tiles_n, tn = tile % p.tiles_n;
+  const int e4 = threadIdx.x, r = (e4 * 4) / TN, col = (e4 * 4) % TN;
+  const float* src = p.part + (long)tile * p.S * (TM * TN) + (rc0 * ROWS + r) * TN + col;
+  float4 sum[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) sum[c] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < p.S; s0 += 8) {
+    float4 v[NC][8];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        v[c][u] = (s0 + u < p.S)
+                      ? *reinterpret_cast<const float4*>(src + (long)(s0 + u) * TM * TN + c * ROWS * TN)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        sum[c].x += v[c][u].x; sum[c].y += v[c][u].y; sum[c].z += v[c][u].z; sum[c].w += v[c][u].w;
+      }
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int m = tm * TM + (rc0 + c) * ROWS + r;
+    if (m < p.M) *reinterpret_cast<float4*>(p.C + (long)m * p.N + tn * TN + col) = sum[c];
+  }
+}
+
 __global__ __launch_bounds__(NT) void splitk_kernel(Args p) {
   __shared__ Smem sm;
   const int tid = threadIdx.x;
@@ -297,8 +333,8 @@ __global__ __launch_bounds__(NT) void splitk_kernel(Args p) {
         }
       }
       __syncthreads();
-      if (sm.flag)  // last arriver
-        for (int rc = 0; rc < RCHUNKS; ++rc) reduce_task(p, tile, rc);
+      if (sm.flag)  // last arriver: the whole tile, a quarter of it per round trip
+        for (int rc = 0; rc < RCHUNKS; rc += RCHUNKS / 4) reduce_chunks<RCHUNKS / 4>(p, tile, rc);
     } else {
       const int tile = (t - nparts) / RCHUNKS, rc = (t - nparts) % RCHUNKS;
       if (tid == 0) {
