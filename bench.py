@@ -44,10 +44,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def time_steps(fn, steps, warmup):
+def time_steps(fn, steps, warmup, flush=None):
     """Run fn warmup times, then time exactly `steps` calls with one event pair per
-    call on the current stream.  Returns (ms per step from the outer events, mean
-    launch ms from the per-call events, list of per-call ms)."""
+    call on the current stream.  With `flush`, every timed call is preceded by an
+    untimed flush() outside its event pair.  Returns (ms per step from the outer events,
+    mean launch ms from the per-call events, list of per-call ms)."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -58,6 +59,8 @@ def time_steps(fn, steps, warmup):
     torch.cuda.synchronize()
     outer0.record(stream)
     for a, b in ev:
+        if flush is not None:
+            flush()
         a.record(stream)
         fn()
         b.record(stream)
@@ -65,6 +68,26 @@ def time_steps(fn, steps, warmup):
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) for a, b in ev]
     return outer0.elapsed_time(outer1) / steps, float(np.mean(per)), per
+
+
+_FLUSH = []
+
+
+def cache_flush():
+    """Read 1 GiB of scratch (a reduction kernel): evicts the 256 MiB Infinity Cache and
+    the L2s, so that the next call reads its operands from HBM.  A read rather than a
+    write, so that no dirty lines are left whose write-back would compete with the timed
+    call's reads."""
+    if not _FLUSH:
+        _FLUSH.append(torch.ones(1 << 28, dtype=torch.float32, device="cuda"))
+    _FLUSH[0].sum()
+
+
+def cold_times(fn, steps):
+    """Median, p10 and p90 (ms) of per-call times, each call after a cache flush."""
+    _, _, per = time_steps(fn, steps, 1, flush=cache_flush)
+    return {"launch_ms_median": float(np.median(per)), "launch_ms_p10": float(np.percentile(per, 10)),
+            "launch_ms_p90": float(np.percentile(per, 90)), "calls": steps}
 
 
 def moe_inputs(cfg, T, call=0):
@@ -119,6 +142,7 @@ def bench_moe(cfg, T, steps, warmup, mode, combine, with_cpu=False, trace_out=No
 
     log(f"[bench] {cfg.name}: timing {steps} steps")
     ms, launch_ms, per = time_steps(step, steps, warmup)
+    cold = cold_times(step, max(5, steps // 2))
     st = ws.status()
     if st != 0:
         raise RuntimeError(f"device status {st}")
@@ -142,6 +166,7 @@ def bench_moe(cfg, T, steps, warmup, mode, combine, with_cpu=False, trace_out=No
         "gbs_alg": bytes_alg / (launch_ms / 1e3) / 1e9,
         "flops_bf16": flops_bf16, "flops_router_fp32": flops_router, "bytes_alg": bytes_alg,
         "experts_touched": touched,
+        "cold": dict(cold, tokens_per_s=T / cold["launch_ms_median"] * 1e3),
     }
     if trace_summary:
         res["trace"] = trace_summary
@@ -195,12 +220,13 @@ def bench_splitk(steps, warmup, mode="static", copies=4):
         it[0] += 1
 
     ms, launch_ms, per = time_steps(step, steps, warmup)
+    cold = cold_times(step, max(5, steps // 2))
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
     nbytes = M * K * 2 + K * N * 2 + M * N * 4
     return {"ms_per_step": ms, "launch_ms": launch_ms, "gbs_alg": nbytes / (launch_ms / 1e3) / 1e9,
             "hbm_frac": nbytes / (launch_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
             "tflops_bf16": 2 * M * N * K / (launch_ms / 1e3) / 1e12, "bytes_alg": nbytes,
-            "mode": mode}
+            "mode": mode, "cold": cold}
 
 
 def bench_attention(steps, warmup, mode, lens, label):
@@ -222,6 +248,7 @@ def bench_attention(steps, warmup, mode, lens, label):
 
     log(f"[bench] attention {label}: timing {steps} steps")
     ms, launch_ms, _ = time_steps(step, steps, warmup)
+    cold = cold_times(step, max(5, steps // 2))
     st = ws.status()
     if st != 0:
         raise RuntimeError(f"device status {st}")
@@ -231,7 +258,7 @@ def bench_attention(steps, warmup, mode, lens, label):
     torch.cuda.empty_cache()
     return {"requests": B, "tokens": total, "launch_ms": launch_ms, "gbs_alg": nbytes / (launch_ms / 1e3) / 1e9,
             "hbm_frac": nbytes / (launch_ms / 1e3) / 1e9 / PEAK_HBM_GBS, "bytes_alg": nbytes,
-            "requests_per_s": B / (ms / 1e3), "mode": mode}
+            "requests_per_s": B / (ms / 1e3), "mode": mode, "cold": cold}
 
 
 def source_hash():
@@ -289,7 +316,7 @@ def attention_lines(steps):
         lines[f"attention_mixed_{m}"] = bench_attention(steps, 2, m, mixed, f"mixed {m}")
     for L in (1024, 8192, 32768):
         lines[f"attention_L{L}"] = bench_attention(steps, 2, "dynamic", [L] * cfg["batch"], f"L={L}")
-    keep = ("requests", "tokens", "launch_ms", "gbs_alg", "hbm_frac")
+    keep = ("requests", "tokens", "launch_ms", "gbs_alg", "hbm_frac", "cold")
     return {k: {f: v[f] for f in keep} for k, v in lines.items()}
 
 
@@ -363,11 +390,11 @@ def main():
         for t in (1, 64):
             r = bench_moe(dec, t, max(5, args.steps // 2), 2, args.mode, args.combine)
             secondary[f"decode_T{t}"] = {k: r[k] for k in ("tokens_per_s", "launch_ms", "gbs_alg",
-                                                          "hbm_frac", "experts_touched")}
+                                                          "hbm_frac", "experts_touched", "cold")}
         fg = bench_moe(synth.CONFIGS["finegrained"], 256, max(5, args.steps // 2), 2, args.mode,
                        args.combine)
         secondary["finegrained_T256"] = {k: fg[k] for k in ("tokens_per_s", "launch_ms", "gbs_alg",
-                                                           "hbm_frac", "experts_touched")}
+                                                           "hbm_frac", "experts_touched", "cold")}
         # the other GPU scheduler of the MoE layer on the same workloads
         other = "dedicated" if args.mode == "static" else "static"
         sched = {}
@@ -379,7 +406,7 @@ def main():
         secondary[f"moe_{other}"] = sched
         for m in ("static", "dynamic"):  # split-K's dynamic mode is a last-arriver reduction
             sk = bench_splitk(max(5, args.steps // 2), 2, m)
-            secondary[f"splitk_{m}"] = {k: sk[k] for k in ("launch_ms", "gbs_alg", "hbm_frac")}
+            secondary[f"splitk_{m}"] = {k: sk[k] for k in ("launch_ms", "gbs_alg", "hbm_frac", "cold")}
         secondary.update(attention_lines(max(5, args.steps // 2)))
 
     line = {
@@ -400,6 +427,8 @@ def main():
                    "tokens_per_step": T, "layers": cfg.layers, "mode": args.mode,
                    "combine": args.combine, "parallelism": "single GPU"},
         "roofline": roof,
+        # the same calls, each after an untimed 1 GiB cache flush (per-call events)
+        "cold_cache": head["cold"],
         "cpu_baseline": head.get("cpu"),
         "secondary": secondary,
     }
