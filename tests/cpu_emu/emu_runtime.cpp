@@ -11,6 +11,7 @@
 #include <chrono>
 #include <cstring>
 #include <thread>
+#include <deque>
 #include <vector>
 
 #include "hip/hip_runtime.h"
@@ -47,13 +48,40 @@ constexpr int LANES = 64;
 
 enum State { RUNNABLE = 0, AT_BLOCK = 1, AT_WAVE = 2, DONE = 3 };
 
+// A direct-to-LDS copy in flight (ETC_EMU_DMA_LATE): the 16 bytes were read from global
+// memory when the copy was issued and land in LDS at the lane's next wait that counts
+// it out, as late as the GPU may deliver them.
+struct Dma {
+  void* dst;
+  unsigned char data[16];
+  int size;
+};
+
 struct Fiber {
   ucontext_t ctx;
   void* tsan = nullptr;
   std::vector<char> stack;
   int state = RUNNABLE;
   unsigned tid = 0;
+  std::deque<Dma> dma;
 };
+
+std::atomic<int> g_dma_late{-1};  // -1: not set yet (ETC_EMU_DMA_LATE decides)
+bool dma_late() {
+  int v = g_dma_late.load(std::memory_order_relaxed);
+  if (v < 0) {
+    v = getenv("ETC_EMU_DMA_LATE") != nullptr ? 1 : 0;
+    g_dma_late.store(v, std::memory_order_relaxed);
+  }
+  return v != 0;
+}
+void dma_land(Fiber& f, size_t keep) {
+  while (f.dma.size() > keep) {
+    const Dma& d = f.dma.front();
+    memcpy(d.dst, d.data, d.size);
+    f.dma.pop_front();
+  }
+}
 
 struct Workgroup {
   ucontext_t sched;
@@ -99,6 +127,7 @@ void fiber_entry() {
   Workgroup& w = *g_wg;
   (*w.fn)();
   Fiber& me = w.f[w.cur];
+  dma_land(me, 0);
   me.state = DONE;
   --w.live;
   const int wave = me.tid / LANES;
@@ -170,6 +199,30 @@ EmuDim emu_block_idx() { return EmuDim{g_wg->block, 0, 0}; }
 EmuDim emu_grid_dim() { return EmuDim{g_wg->grid, 1, 1}; }
 EmuDim emu_block_dim() { return EmuDim{(unsigned)g_wg->f.size(), 1, 1}; }
 int emu_lane() { return g_wg->f[g_wg->cur].tid % LANES; }
+
+// Selects when direct-to-LDS copies land for the following launches (0: at once, 1: at
+// the lane's wait); set between launches only.
+extern "C" __attribute__((visibility("default"))) void etc_emu_set_dma_late(int late) {
+  g_dma_late.store(late ? 1 : 0, std::memory_order_relaxed);
+}
+
+// global_load_lds of one lane: lands at once, or (ETC_EMU_DMA_LATE) at the lane's wait
+void emu_dma_issue(void* dst, const void* src, int size) {
+  if (!dma_late()) {
+    memcpy(dst, src, size);
+    return;
+  }
+  Dma d;
+  d.dst = dst;
+  d.size = size;
+  memcpy(d.data, src, size);
+  g_wg->f[g_wg->cur].dma.push_back(d);
+}
+// s_waitcnt: the lane's copies beyond the vector-memory count land (oldest first)
+void emu_waitcnt(int imm) {
+  const int vm = (imm & 15) | (((imm >> 14) & 3) << 4);
+  dma_land(g_wg->f[g_wg->cur], (size_t)vm);
+}
 
 void emu_syncthreads() {
   Workgroup& w = *g_wg;

@@ -207,14 +207,20 @@ inline float atomicAdd(float* p, float v) {
 #define __hip_atomic_store(p, v, order, scope) __atomic_store_n((p), (v), EMU_ORDER(order))
 #define __hip_atomic_fetch_add(p, v, order, scope) __atomic_fetch_add((p), (v), EMU_ORDER(order))
 #define __builtin_amdgcn_fence(order, scope) __atomic_thread_fence(order)
-#define __builtin_amdgcn_s_waitcnt(x) ((void)0)
+void emu_waitcnt(int imm);
+#define __builtin_amdgcn_s_waitcnt(x) emu_waitcnt(x)
 #define __builtin_amdgcn_s_sleep(x) emu_yield()
 #define __builtin_amdgcn_s_memrealtime() emu_realtime()
 
-// global_load_lds: lane l writes 16 bytes at the wave's LDS base + 16 * l; the CPU copy
-// is synchronous, so the waits that order it on the GPU are no-ops here
+// global_load_lds: lane l writes 16 bytes at the wave's LDS base + 16 * l.  By default
+// the copy lands at once (a copy that overwrites LDS still being read then shows up as a
+// wrong result); with ETC_EMU_DMA_LATE it lands only at the lane's s_waitcnt whose
+// vector-memory count excludes it, oldest first (a read of LDS before its wait then
+// shows up).  Only these copies are counted, so a wait lands no more of them than the
+// GPU's count, which also includes the other vector-memory operations, would.
+void emu_dma_issue(void* dst, const void* src, int size);
 inline void emu_global_load_lds(const void* src, void* lds_base, int size, int off) {
-  memcpy(static_cast<char*>(lds_base) + off + emu_lane() * size, src, size);
+  emu_dma_issue(static_cast<char*>(lds_base) + off + emu_lane() * size, src, size);
 }
 #define __builtin_amdgcn_global_load_lds(src, dst, size, off, aux) \
   emu_global_load_lds((const void*)(src), (void*)(dst), (size), (off))

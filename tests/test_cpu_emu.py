@@ -170,6 +170,32 @@ def test_event_tensor_final_state(lib, mode):
     moe_check.check_event_tensor(read, layout, T, cfg.hidden, cfg.ffn, cfg.top_k, cfg.experts, g, 1)
 
 
+@pytest.mark.parametrize("mode", MOE_MODES)
+def test_copies_landing_at_their_wait(lib, mode):
+    """Direct-to-LDS copies that land only at the s_waitcnt which counts them out (the
+    latest the GPU may deliver them): a read of LDS before its wait would see stale
+    data.  The MoE layer (128-row and small-M tiles, two layers) and split-K."""
+    lib.etc_emu_set_dma_late(1)
+    try:
+        cfg = MID
+        for T in (17, 100):
+            layers, x = synth.make_layers(cfg), synth.make_x(cfg, T, call=3)
+            _check(cfg, x, layers, driver.moe(lib, cfg, x, layers, mode=mode))
+        if mode != "dedicated":
+            M, N, K, S = 37, 256, 1024, 4
+            A, B = synth.make_splitk(M=M, N=N, K=K, seed=5)
+            n = lib.etc_splitk_workspace_size(M, N, S)
+            ws = torch.zeros(n + 256, dtype=torch.uint8)
+            wptr = ws.data_ptr() + (-ws.data_ptr()) % 256
+            C = torch.zeros(M, N, dtype=torch.float32)
+            assert lib.etc_splitk_gemm(M, N, K, S, A.data_ptr(), B.data_ptr(), C.data_ptr(), wptr, n,
+                                       binding.MODES[mode], 0, 0, None) == 0
+            ref = osk.splitk_gemm(synth.as_numpy(A), synth.as_numpy(B), S)
+            assert np.max(np.abs(C.numpy() - ref)) <= 1e-3 * np.max(np.abs(ref))
+    finally:
+        lib.etc_emu_set_dma_late(0)
+
+
 @pytest.mark.parametrize("mode", ["static", "dynamic"])
 @pytest.mark.parametrize("workers", [0, 1, 3, 12])
 def test_splitk(lib, mode, workers):
