@@ -57,6 +57,10 @@ def time_steps(fn, steps, warmup, flush=None):
           for _ in range(steps)]
     outer0, outer1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    # The GPU spins (untimed) while the host queues the timed calls, so that no event
+    # pair waits for the host to submit its kernel: a call shorter than its host-side
+    # launch path (split-K's 30 us) would otherwise be timed with that path included.
+    torch.cuda._sleep(10_000_000)
     outer0.record(stream)
     for a, b in ev:
         if flush is not None:
