@@ -172,8 +172,10 @@ ETC_DEV void partial_task(const Args& p, Smem& sm, int b, int g, int c, int rec)
   });
   // the workgroup's next ticket, drawn while this chunk's loads are in flight (a later
   // ticket than the running one, so the order stays deadlock-free: every partial ticket
-  // precedes every merge ticket, and a partial never waits)
-  if (tid == 0) sm.next = (int)gridDim.x + ticket_inc(p.sched + W_TICKET);
+  // precedes every merge ticket, and a partial never waits); it is read back only at the
+  // end of the task, since a wait for it would also wait for every load issued before it
+  int drawn = 0;
+  if (tid == 0) drawn = ticket_inc(p.sched + W_TICKET);
 
   // scores of the wave's 64 tokens: block j holds heads 4*grp + r (rows) x tokens
   // 16j + q16 (columns)
@@ -273,6 +275,7 @@ ETC_DEV void partial_task(const Args& p, Smem& sm, int b, int g, int c, int rec)
     st_shared(dst + tid * REC + HD, sm.ml[tid][0]);
     st_shared(dst + tid * REC + HD + 1, sm.ml[tid][1]);
   }
+  if (tid == 0) sm.next = (int)gridDim.x + drawn;
 }
 
 // Output of the G query heads of (b, g) from the n_b partial records starting at rec0

@@ -24,7 +24,7 @@
 // A block [64 rows][64 k] (rows of 128 bytes, chunks swizzled as in mfma.hpp) and the B
 // block [64 k][128 n] (rows of 256 bytes).  B is N-contiguous while the MFMA wants 8
 // consecutive k per lane, so a lane's B fragment comes from two transposed LDS reads
-// (gfx950 ds_read_b64_tr_b16, 4 k each; see lds_read_tr16).  The 16-byte chunk c of B
+// (gfx950 ds_read_b64_tr_b16, 4 k each; see lds_read_tr16_x8).  The 16-byte chunk c of B
 // row r sits at position c ^ bsw(r) with bsw(r) = 2 * ((r % 4) + 4 * ((r / 8) % 2)): the
 // 16 rows one transposed read touches fall on 8 different chunk pairs, two rows each,
 // which is as few bank conflicts as 512 bytes per read allow.
