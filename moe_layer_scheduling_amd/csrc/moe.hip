@@ -940,10 +940,12 @@ ETC_TASK void gateup_task(KArgs& p, KLayer& L, int e, int m, int n, Smem& sm) {
   else if (valid <= 32) gateup_small<TE, 32>(p, L, e, n, Ts, hs);
   else gateup_large<TE>(p, L, e, n, valid, Ts, hs);
   // static mode: draw the next ticket now; its atomic round trip overlaps the epilogue
-  // (issued before the tile, it would hold up the tile's first wait for its copies)
+  // (issued before the tile, it would hold up the tile's first wait for its copies).  The
+  // drawn value is mapped to a ticket only after the epilogue: computing with it here
+  // would make the wave wait for the atomic, and the barrier below the whole workgroup.
   const bool prefetch = p.mode == ETC_SCHED_STATIC;
-  int next = -1;
-  if (prefetch && tid == 0) next = static_ticket(p);
+  int drawn = 0;
+  if (prefetch && tid == 0) drawn = xcd_ticket_draw(p.sched);
   __syncthreads();
   // whole rows out to hbuf, 16 bytes per store: 8 bf16 or 4 float columns (F is a
   // multiple of 64, so a store never straddles the edge).  16-byte stores: coherent
@@ -961,7 +963,7 @@ ETC_TASK void gateup_task(KArgs& p, KLayer& L, int e, int m, int n, Smem& sm) {
       st_shared16(hb, (uint32_t)(((size_t)row * F + c) * sizeof(TE)), pack16<TE>(v));
     }
   }
-  if (prefetch && tid == 0) sm.next_ticket = next;
+  if (prefetch && tid == 0) sm.next_ticket = xcd_ticket_map(drawn);
 }
 
 // Down rows of a tile: A row r is sorted row r0 + r of hbuf from column kb (rows past the
@@ -1056,14 +1058,16 @@ ETC_TASK void down_task(KArgs& p, KLayer& L, int e, int m, int n2i, int s, int g
   if (valid <= 16) down_small<TE, 16>(p, L, e, n2i, r0, valid, kb, klen, ct);
   else if (valid <= 32) down_small<TE, 32>(p, L, e, n2i, r0, valid, kb, klen, ct);
   else down_large<TE>(p, L, e, n2i, r0, valid, kb, klen, ct);
-  const bool prefetch = p.mode == ETC_SCHED_STATIC;  // as in gateup_task
-  int next = -1;
-  if (prefetch && tid == 0) next = static_ticket(p);
   const float gate = pair >= 0 ? gp(L.topk_w)[pair] : 0.f;
   if (tid < BM) {
     Ts.row_tok[tid] = pair >= 0 ? pair / K : -1;
     Ts.row_gate[tid] = gate;
   }
+  // the next ticket, as in gateup_task; drawn after the gate loads have returned, so
+  // that nothing before the epilogue waits for it
+  const bool prefetch = p.mode == ETC_SCHED_STATIC;
+  int drawn = 0;
+  if (prefetch && tid == 0) drawn = xcd_ticket_draw(p.sched);
   __syncthreads();
   const int c0 = n2i * BN2, ncols = min(BN2, H - c0);
   if (p.combine == ETC_COMBINE_ATOMIC) {
@@ -1087,7 +1091,7 @@ ETC_TASK void down_task(KArgs& p, KLayer& L, int e, int m, int n2i, int s, int g
       }
     }
   }
-  if (prefetch && tid == 0) sm.next_ticket = next;
+  if (prefetch && tid == 0) sm.next_ticket = xcd_ticket_map(drawn);
 }
 
 template <typename TE>
