@@ -39,7 +39,7 @@ extern "C" {
 typedef enum {
   ETC_OK = 0,
   ETC_ERR_INVALID_ARG = 1, /* a pointer, size or enum is out of range */
-  ETC_ERR_UNSUPPORTED = 2, /* valid shape this build does not handle (see each call) */
+  ETC_ERR_UNSUPPORTED = 2, /* valid shape the library does not handle (see each call) */
   ETC_ERR_WORKSPACE = 3,   /* workspace missing, misaligned or too small */
   ETC_ERR_HIP = 4,         /* a HIP runtime call failed (device state unknown) */
   ETC_ERR_TIMEOUT = 5,     /* device status: a wait saw no progress for 5 s (its limit
