@@ -275,7 +275,7 @@ ETC_DEV void partial_task(const Args& p, Smem& sm, int b, int g, int c, int rec)
     st_shared(dst + tid * REC + HD, sm.ml[tid][0]);
     st_shared(dst + tid * REC + HD + 1, sm.ml[tid][1]);
   }
-  if (tid == 0) sm.next = (int)gridDim.x + drawn;
+  if (tid == 0) sm.next = drawn;
 }
 
 // Output of the G query heads of (b, g) from the n_b partial records starting at rec0
@@ -394,14 +394,12 @@ __global__ __launch_bounds__(NT) void attn_kernel(Args p) {
   const int nmerge = p.B * p.HKV;
   const int total = !valid ? 0 : (p.mode == ETC_SCHED_STATIC ? np + nmerge : np);
 
-  // the first gridDim tickets go to the workgroups by index (every workgroup of the grid
-  // is resident); the counter hands out the later ones
-  if (tid == 0) sm.next = (int)blockIdx.x;
+  if (tid == 0) sm.next = -1;
   while (true) {
     if (tid == 0) {
       // (no check of the abort flag here: partial tasks never wait, and a merge's wait
       // sees the flag and gives up, so every workgroup still leaves after an abort)
-      const int t = sm.next >= 0 ? sm.next : (int)gridDim.x + ticket_inc(p.sched + W_TICKET);
+      const int t = sm.next >= 0 ? sm.next : ticket_inc(p.sched + W_TICKET);
       sm.next = -1;
       sm.task = t;
     }

@@ -266,22 +266,17 @@ constexpr int MAX_XCD_QUEUES = 8;  // MI355X: 8 XCDs of 32 CUs, each with its ow
 // waiting task's producers, which come earlier in the order, are always claimed by
 // workgroups that can run them: the order stays deadlock-free.
 //
-// Every workgroup of the grid is resident (the grid never exceeds what the device holds
-// at once), so the first draw needs no atomic: member m = b / Q of queue q takes the
-// queue's m-th ticket, and the counter of queue q hands out the later ones, starting
-// after the queue's n_q members.  That removes one atomic round trip from the start of
-// every call.
-ETC_DEV int xcd_ticket_of(int q, int i) {  // the i-th ticket of queue q
+// The i-th ticket drawn from queue q.  Every ticket, the first included, comes from the
+// queue's counter: a ticket is only ever held by a workgroup that is running, so the
+// order stays deadlock-free even when some workgroups of the grid start late (another
+// kernel holding their compute units).
+ETC_DEV int xcd_ticket_of(int q, int i) {
   const int nwg = (int)gridDim.x;
   const int Q = nwg < MAX_XCD_QUEUES ? nwg : MAX_XCD_QUEUES;
   const int G = nwg / Q;
   return ((i / G) * Q + q) * G + i % G;
 }
-ETC_DEV int xcd_first_ticket() {
-  const int nwg = (int)gridDim.x;
-  const int Q = nwg < MAX_XCD_QUEUES ? nwg : MAX_XCD_QUEUES;
-  return xcd_ticket_of((int)blockIdx.x % Q, (int)blockIdx.x / Q);
-}
+
 // The next value of a ticket counter (relaxed, agent scope).  An increment that wraps at
 // 2^32 - 1 is a plain increment here; unlike an atomic add it is left alone by the
 // compiler's wave-level atomic aggregation, which reads the result back at once (a wait
@@ -290,8 +285,8 @@ ETC_DEV int ticket_inc(int* counter) {
   return (int)__builtin_amdgcn_atomic_inc32((unsigned*)gp(counter), 0xffffffffu, __ATOMIC_RELAXED, "agent");
 }
 
-// A later ticket in two steps: the draw (the atomic) and its mapping, so that a caller
-// can keep the atomic in flight and map the result only where it needs the ticket.
+// A ticket in two steps: the draw (the atomic) and its mapping, so that a caller can
+// keep the atomic in flight and map the result only where it needs the ticket.
 ETC_DEV int xcd_ticket_draw(int* sched) {
   const int nwg = (int)gridDim.x;
   const int Q = nwg < MAX_XCD_QUEUES ? nwg : MAX_XCD_QUEUES;
@@ -300,9 +295,7 @@ ETC_DEV int xcd_ticket_draw(int* sched) {
 ETC_DEV int xcd_ticket_map(int drawn) {
   const int nwg = (int)gridDim.x;
   const int Q = nwg < MAX_XCD_QUEUES ? nwg : MAX_XCD_QUEUES;
-  const int q = (int)blockIdx.x % Q;
-  const int members = (nwg - q + Q - 1) / Q;  // workgroups b < nwg with b mod Q == q
-  return xcd_ticket_of(q, members + drawn);
+  return xcd_ticket_of((int)blockIdx.x % Q, drawn);
 }
 ETC_DEV int xcd_ticket(int* sched) { return xcd_ticket_map(xcd_ticket_draw(sched)); }
 

@@ -1910,7 +1910,7 @@ __global__ __launch_bounds__(MNT) void moe_kernel(Args pk) {
     sm.lc.layer = -1;
     sm.scan_seen = 0u;
     sm.perm_seen = 0u;
-    sm.next_ticket = p.mode == ETC_SCHED_STATIC ? xcd_first_ticket() : -1;
+    sm.next_ticket = -1;
     for (int l = 0; l <= MAXL; ++l) sm.lbase[l] = -1;
   }
   const bool dedicated = p.mode == ETC_SCHED_DEDICATED;

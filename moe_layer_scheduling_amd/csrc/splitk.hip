@@ -306,16 +306,17 @@ __global__ __launch_bounds__(NT) void splitk_kernel(Args p) {
   const int total = stat ? nparts + p.tiles * RCHUNKS : nparts;
   // Static: partial tickets are slice-major, so a chunk of consecutive tickets (one XCD
   // queue's share) holds the tiles of one slice, which share its A block.  Dynamic: one
-  // counter; the first gridDim tickets go to the workgroups by index (all are resident),
-  // the counter hands out the rest.  A workgroup draws its next ticket while its current
-  // task runs.  (No check of the abort flag here: partial tasks never wait, and a
-  // reduction's wait sees the flag and gives up, so every workgroup still leaves after
-  // an abort.)
+  // counter.  A workgroup draws its next ticket while its current task runs.  (No check
+  // of the abort flag here: partial tasks never wait, and a reduction's wait sees the
+  // flag and gives up, so every workgroup still leaves after an abort.)
   auto draw = [&]() ETC_INLINE {
     return stat ? xcd_ticket_draw(p.sched) : ticket_inc(p.sched + W_QHEAD);
   };
-  auto map = [&](int drawn) ETC_INLINE { return stat ? xcd_ticket_map(drawn) : (int)gridDim.x + drawn; };
-  int t = stat ? xcd_first_ticket() : (int)blockIdx.x;
+  auto map = [&](int drawn) ETC_INLINE { return stat ? xcd_ticket_map(drawn) : drawn; };
+  if (tid == 0) sm.task = map(draw());
+  __syncthreads();
+  int t = sm.task;
+  __syncthreads();
 
   while (t < total) {
     if (t < nparts) {

@@ -200,7 +200,7 @@ def test_copies_landing_at_their_wait(lib, mode):
 @pytest.mark.parametrize("workers", [0, 1, 3, 12])
 def test_splitk(lib, mode, workers):
     """Grids of 1, 3 and 12 workgroups: XCD queues with one member each, and queues of
-    two members beside queues of one (first tickets by member index)."""
+    two members beside queues of one."""
     M, N, K, S = 37, 256, 1024, 4
     A, B = synth.make_splitk(M=M, N=N, K=K, seed=2)
     n = lib.etc_splitk_workspace_size(M, N, S)
