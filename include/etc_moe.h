@@ -314,7 +314,7 @@ const char* etc_status_string(etc_status status);
 int32_t etc_default_workers(int32_t kind, etc_dtype dtype);
 
 /* ABI version of this header: (major << 16) | minor. */
-#define ETC_ABI_VERSION 0x00010001
+#define ETC_ABI_VERSION 0x00010002
 int32_t etc_abi_version(void);
 
 #ifdef __cplusplus

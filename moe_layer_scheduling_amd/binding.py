@@ -13,7 +13,7 @@ import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libetc_moe.so")
-ABI_VERSION = 0x00010001
+ABI_VERSION = 0x00010002
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "workspace",
           4: "HIP runtime error", 5: "device wait timed out", 6: "no gfx950 device"}
@@ -25,7 +25,7 @@ FLAG_TRACE = 0x2
 FLAG_ALLOW_DYNAMIC = 0x4
 LAYOUT_WORDS = 17
 W_TRACE_LAST = 10  # control word holding the last traced call's record count
-CONTROL_WORDS = 320  # int32 control words at the start of every workspace
+CONTROL_WORDS = 416  # int32 control words at the start of every workspace
 CONTROL_BYTES = -(-CONTROL_WORDS * 4 // 256) * 256  # the region after them starts here
 
 

@@ -237,10 +237,6 @@ ETC_DEV uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }  // 10
 // Control words shared by all workgroups of one call (in the workspace).
 enum SchedWord {
   W_TICKET = 0,   // static: next ticket
-  W_QHEAD = 1,    // dynamic: next queue slot to take
-  W_QTAIL = 2,    // dynamic: queue slots handed out to producers
-  W_QTOTAL = 3,   // dynamic: tasks that will ever be queued (grows as layers plan)
-  W_PLANNED = 4,  // dynamic: layers whose task counts are final
   W_EXIT = 5,     // workgroups that have left the task loop
   W_STATUS = 7,   // 0 ok, else an etc_status; survives the end-of-call reset
   W_AUX = 8,      // debug: where the abort came from
@@ -252,8 +248,15 @@ enum SchedWord {
   // counter, spent most of its time on that read).
   W_ABORT = 32,   // set when a wait times out: every workgroup leaves
   W_XTICKET = 64, // static: next ticket of XCD queue q at W_XTICKET + q * W_LINE
-  W_LINE = 32,    // words per 128-byte line
-  W_NWORDS = 64 + 8 * 32
+  // The dynamic queue's words: every claimer adds to the head, every producer to the
+  // tail, and idle claimers read the total and the planned-layer count, so each of the
+  // three groups has a line of its own.
+  W_QHEAD = 320,   // dynamic: next queue slot to take (dedicated: scheduler progress)
+  W_QTAIL = 352,   // dynamic: queue slots handed out to producers
+  W_QTOTAL = 384,  // dynamic: tasks that will ever be queued (grows as layers plan)
+  W_PLANNED = 385, // dynamic: layers whose task counts are final
+  W_LINE = 32,     // words per 128-byte line
+  W_NWORDS = 416
 };
 constexpr int MAX_XCD_QUEUES = 8;  // MI355X: 8 XCDs of 32 CUs, each with its own L2
 

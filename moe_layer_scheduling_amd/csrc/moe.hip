@@ -1236,17 +1236,20 @@ ETC_DEV bool claim_dynamic(KArgs& p, Task& t) {
       t = dec(v);
       return true;
     }
-    // every layer has planned (acquire: their additions to the total are visible) and
-    // this slot lies past the final total
-    if (ev_load_relaxed(p.sched + W_PLANNED) == p.L && ev_load(p.sched + W_PLANNED) == p.L &&
-        slot >= ev_load_relaxed(p.sched + W_QTOTAL)) {
-      t.kind = K_NONE;
-      return true;
+    // every WATCH_EVERY polls of the slot: every layer has planned (acquire: their
+    // additions to the total are visible) and this slot lies past the final total, or
+    // the watchdog.  (Reading those words at every poll would keep their lines busy
+    // under the producers' additions.)
+    if (it % WATCH_EVERY == 0) {
+      if (ev_load_relaxed(p.sched + W_PLANNED) == p.L && ev_load(p.sched + W_PLANNED) == p.L &&
+          slot >= ev_load_relaxed(p.sched + W_QTOTAL)) {
+        t.kind = K_NONE;
+        return true;
+      }
+      if (it == 0) wd.start(p.timeout_ticks, ev_load_relaxed(p.sched + W_QTAIL));
+      else if (wd.expired(p.sched, p.timeout_ticks, ev_load_relaxed(p.sched + W_QTAIL), 2))
+        return false;
     }
-    if (it == 0) wd.start(p.timeout_ticks, ev_load_relaxed(p.sched + W_QTAIL));
-    else if (it % WATCH_EVERY == 0 &&
-             wd.expired(p.sched, p.timeout_ticks, ev_load_relaxed(p.sched + W_QTAIL), 2))
-      return false;
     __builtin_amdgcn_s_sleep(2);
   }
 }
