@@ -14,6 +14,7 @@ import numpy as np  # noqa: E402
 import torch  # noqa: E402
 
 from moe_layer_scheduling_amd import binding, synth  # noqa: E402
+from oracle import attention as oa  # noqa: E402
 from oracle import splitk as osk  # noqa: E402
 from tests import moe_check  # noqa: E402
 from tests.cpu_emu import driver  # noqa: E402
@@ -43,6 +44,23 @@ def main(path):
                                    binding.MODES[mode], 0, 0, None) == 0
         assert np.max(np.abs(C.numpy() - ref)) <= 1e-3 * np.max(np.abs(ref))
         print(f"splitk {mode} ok", flush=True)
+    lens, HKV, G, D = [1, 257, 700], 2, 2, 128
+    q, k, v, start = synth.make_attention(lens, HKV, G, seed=5)
+    n = lib.etc_decode_attention_workspace_size(len(lens), HKV, G, D, int(np.sum(lens)))
+    lens_t = torch.as_tensor(lens, dtype=torch.int32)
+    kt = synth.as_numpy(k).transpose(1, 0, 2)
+    vt = synth.as_numpy(v).transpose(1, 0, 2)
+    ref = oa.decode_attention(synth.as_numpy(q), kt, vt, start.numpy(), np.asarray(lens), G, D ** -0.5)
+    for mode in ("static", "dynamic"):
+        ws = torch.zeros(n + 256, dtype=torch.uint8)
+        wptr = ws.data_ptr() + (-ws.data_ptr()) % 256
+        out = torch.zeros(len(lens), HKV * G, D, dtype=torch.float32)
+        assert lib.etc_decode_attention(len(lens), HKV, G, D, lens_t.data_ptr(), start.data_ptr(),
+                                        k.shape[1], D ** -0.5, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                        out.data_ptr(), wptr, n, len(lens), int(np.sum(lens)),
+                                        binding.MODES[mode], 0, 0, None) == 0
+        assert np.max(np.abs(out.numpy() - ref)) <= 1e-3 * np.max(np.abs(ref))
+        print(f"attention {mode} ok", flush=True)
 
 
 if __name__ == "__main__":

@@ -12,6 +12,7 @@ import pytest
 import torch
 
 from moe_layer_scheduling_amd import binding, synth
+from oracle import attention as oa
 from oracle import splitk as osk
 from tests import moe_check
 from tests.cpu_emu import build_emu, driver
@@ -359,3 +360,32 @@ def test_decode_attention_device_checks(lib):
     assert st == 1 and not out.any()
     out, st = driver.attention(lib, q, k, v, lens, start, scale=scale, max_total=20)
     assert st == 3 and not out.any()
+
+
+@pytest.mark.parametrize("mode", ["static", "dynamic"])
+@pytest.mark.parametrize("workers", [0, 3])
+def test_decode_attention(lib, mode, workers):
+    """Variable-context decode attention on the CPU harness: lengths of one token, one
+    chunk, one chunk and one token, several chunks with a ragged tail, against the
+    oracle; the counters read back at their targets with FLAG_KEEP_COUNTERS."""
+    lens = [1, 256, 257, 2000, 513]
+    HKV, G, D = 3, 2, 128
+    q, k, v, start = synth.make_attention(lens, HKV, G, seed=5)
+    B, rows = len(lens), k.shape[1]
+    n = lib.etc_decode_attention_workspace_size(B, HKV, G, D, int(np.sum(lens)))
+    ws = torch.zeros(n + 256, dtype=torch.uint8)
+    wptr = ws.data_ptr() + (-ws.data_ptr()) % 256
+    out = torch.zeros(B, HKV * G, D, dtype=torch.float32)
+    lens_t = torch.as_tensor(lens, dtype=torch.int32)
+    scale = 1.0 / np.sqrt(D)
+    assert lib.etc_decode_attention(B, HKV, G, D, lens_t.data_ptr(), start.data_ptr(), rows, scale,
+                                    q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), wptr, n,
+                                    B, int(np.sum(lens)), binding.MODES[mode],
+                                    binding.FLAG_KEEP_COUNTERS, workers, None) == 0
+    kt = synth.as_numpy(k).transpose(1, 0, 2)
+    vt = synth.as_numpy(v).transpose(1, 0, 2)
+    ref = oa.decode_attention(synth.as_numpy(q), kt, vt, start.numpy(), np.asarray(lens), G, scale)
+    assert np.max(np.abs(out.numpy() - ref)) <= 1e-3 * np.max(np.abs(ref))
+    words = np.frombuffer(ctypes.string_at(wptr + binding.CONTROL_BYTES, B * HKV * 32 * 4), dtype=np.int32)
+    want = np.repeat([oa.split_count(L, 256) for L in lens], HKV)
+    assert np.array_equal(words[::32], want), words[::32]

@@ -1,6 +1,7 @@
 """The kernels on the CPU execution harness built with AddressSanitizer (host code only:
-the harness compiles the HIP sources as host C++): every MoE scheduler and split-K, with
-out-of-bounds accesses to any buffer (workspace, LDS arrays, operands) reported."""
+the harness compiles the HIP sources as host C++): every MoE scheduler, split-K and decode
+attention, with out-of-bounds accesses to any buffer (workspace, LDS arrays, operands)
+reported."""
 
 import os
 import subprocess
@@ -20,4 +21,4 @@ def test_kernels_under_address_sanitizer():
     r = subprocess.run([sys.executable, os.path.join(HERE, "cpu_emu", "sanitized_run.py"), lib],
                        capture_output=True, text=True, env=env, timeout=900)
     assert r.returncode == 0, (r.stdout[-3000:], r.stderr[-6000:])
-    assert "splitk dynamic ok" in r.stdout
+    assert "attention dynamic ok" in r.stdout
