@@ -252,6 +252,82 @@ def check_trace_causality(records, T, H, F, k, E, gpu, layout, read_i32, layers,
     return checked
 
 
+def check_data_dependencies(records, T, H, k, E, gpu, layout, read_i32, layers, atomic=True,
+                            slack_ticks=200):
+    """The trace of one call against the data each task reads, derived from the routing
+    the GPU produced and the tiling alone (not from the counters or the scheduler
+    model): a task's body begins no earlier than the end of every task that writes what
+    it reads, less slack_ticks.  With a counter target set too low in both the kernel
+    and the model, the event-tensor checks would still pass; this one would not.
+
+    Reads and writes, per layer:
+      R (every slice of tile tau) writes xq rows of tau's tokens and, with the atomic
+        combine, clears their accumulator rows; layer l+1's R of tau reads F(l, tau)'s rows.
+      P(tau), or S when there are no P tasks, writes tau's entries of the permutation.
+      GU(e, m, n) reads the xq rows and permutation entries of row tile (e, m).
+      D(e, m, n2, s) reads the h rows of (e, m) that GU(e, m, n) wrote for n in chunk s,
+        and adds into the accumulator rows of its tokens.
+      F(tau) reads the accumulator rows of tau's tokens: every D whose row tile holds one.
+    Returns the number of (consumer, producer) pairs checked."""
+    from moe_layer_scheduling_amd import trace
+
+    d = trace.decode(records)
+    t_run = d["start"] + d["wait"]
+    t_end = t_run + d["run"]
+    index = {}
+    for i in range(len(d["kind"])):
+        index[(int(d["kind"][i]), int(d["layer"][i]), int(d["a"][i]), int(d["b"][i]),
+               int(d["c"][i]), int(d["d"][i]))] = i
+    K_R, K_S, K_GU, K_D, K_F, K_P = (TRACE_KIND[n] for n in ("R", "S", "GU", "D", "F", "P"))
+    checked = 0
+
+    def after(consumer, producers, what):
+        nonlocal checked
+        i = index[consumer]
+        for pk in producers:
+            j = index[pk]
+            assert t_run[i] >= t_end[j] - slack_ticks, (
+                f"task {consumer} began {int(t_end[j] - t_run[i])} ticks before {pk} "
+                f"finished ({what})")
+            checked += 1
+
+    for l in range(layers):
+        lay = layout(l)
+        _, n1, _, BT, BM, BN1, BN2 = (int(v) for v in lay[6:13])
+        pw = [int(v) for v in read_i32(lay[5], 8)]
+        nS, gpc, Q = pw[4], pw[5], pw[7]
+        n2 = -(-H // BN2)
+        n_rt = -(-T // BT)
+        counts = np.asarray(gpu["counts"][l])
+        sa = np.asarray(gpu["sa"][l])
+        off = np.concatenate([[0], np.cumsum(counts)]).astype(int)
+        perm_by_p = n_rt > PERM_INLINE_RT
+        d_of_tau = [[] for _ in range(n_rt)]
+        for e in range(E):
+            for m in range(-(-int(counts[e]) // BM)):
+                rows = sa[off[e] + m * BM:min(off[e] + (m + 1) * BM, off[e + 1])]
+                taus = sorted({int(t) // BT for t in rows // k})
+                routing = [(K_R, l, tau * Q + q, 0, 0, 0) for tau in taus for q in range(Q)]
+                perm = ([(K_P, l, tau, 0, 0, 0) for tau in taus] if perm_by_p
+                        else [(K_S, l, 0, 0, 0, 0)])
+                for n in range(n1):
+                    after((K_GU, l, e, m, n, 0), routing + perm, "xq rows and permutation")
+                for n2i in range(n2):
+                    for s_ in range(nS):
+                        gus = [(K_GU, l, e, m, n, 0) for n in range(s_ * gpc, min((s_ + 1) * gpc, n1))]
+                        after((K_D, l, e, m, n2i, s_), gus + (routing if atomic else []),
+                              "h rows of its chunk, cleared accumulator rows")
+                        for tau in taus:
+                            d_of_tau[tau].append((K_D, l, e, m, n2i, s_))
+        for tau in range(n_rt):
+            after((K_F, l, tau, 0, 0, 0), d_of_tau[tau], "accumulator rows of its tokens")
+            if l + 1 < layers:
+                Qn = int(read_i32(layout(l + 1)[5], 8)[7])
+                for q in range(Qn):
+                    after((K_R, l + 1, tau * Qn + q, 0, 0, 0), [(K_F, l, tau, 0, 0, 0)], "layer input rows")
+    return checked
+
+
 def check_identical_experts(x, layers, eps, out):
     """Every expert holds the same weights: whatever the routing, each token's output is
     the single FFN of its normalised input (the gates sum to 1), rounded to bfloat16.

@@ -265,6 +265,10 @@ def test_trace_respects_every_dependency(lib, mode):
             read, cfg.layers)
     checked = moe_check.check_trace_causality(rec, *args)
     assert checked > 1000
+    # the same trace against the data each task reads (independent of the counters)
+    pairs = moe_check.check_data_dependencies(rec, T, cfg.hidden, cfg.top_k, cfg.experts, g,
+                                              lambda l: lib_layout(lib, T, cfg, l), read, cfg.layers)
+    assert pairs > 1000
     # the check itself: a finalize task moved to begin at the call's first tick fails it
     bad = rec.copy()
     i = int(np.nonzero((bad[:, 0] & 15) == 5)[0][0])
@@ -272,6 +276,9 @@ def test_trace_respects_every_dependency(lib, mode):
     bad[i, 2] &= np.uint64(0xFFFFFFFF)  # no claim or wait ticks
     with pytest.raises(AssertionError, match="began"):
         moe_check.check_trace_causality(bad, *args)
+    with pytest.raises(AssertionError, match="began"):
+        moe_check.check_data_dependencies(bad, T, cfg.hidden, cfg.top_k, cfg.experts, g,
+                                          lambda l: lib_layout(lib, T, cfg, l), read, cfg.layers)
 
 
 @pytest.mark.parametrize("mode", MOE_MODES)

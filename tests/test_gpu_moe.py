@@ -157,8 +157,13 @@ def _trace_check(cfg, T, ws, gpu):
     def read(off, cnt):
         return ws.view(off, cnt, torch.int32).cpu().numpy()
 
-    return moe_check.check_trace_causality(rec, T, cfg.hidden, cfg.ffn, cfg.top_k, cfg.experts,
-                                           gpu, ws.layout, read, cfg.layers)
+    checked = moe_check.check_trace_causality(rec, T, cfg.hidden, cfg.ffn, cfg.top_k, cfg.experts,
+                                              gpu, ws.layout, read, cfg.layers)
+    # the same trace against the data each task reads (independent of the counters)
+    pairs = moe_check.check_data_dependencies(rec, T, cfg.hidden, cfg.top_k, cfg.experts, gpu,
+                                              ws.layout, read, cfg.layers)
+    assert pairs > 100
+    return checked
 
 
 @pytest.mark.parametrize("mode", GPU_MODES)
