@@ -311,6 +311,44 @@ def copy_calibration(nbytes=1 << 30, reps=3):
             "launch_ms": launch_ms, "gbs": 2 * nbytes / (launch_ms / 1e3) / 1e9}
 
 
+def achievable_peaks(cfg, T):
+    """Context for the nominal peaks: what the vendor library kernels reach on this GPU.
+    A streaming read (one float32 reduction over 1 GiB), a streaming copy (1 GiB read and
+    1 GiB written by one elementwise kernel), a square bf16 GEMM (8192^3,
+    hipBLASLt through torch.matmul), and the dense GEMMs that hold one call's expert
+    arithmetic: every routed row of a layer in one GEMM per projection ([T*k, H] x [H, 2F]
+    and [T*k, F] x [F, H]), for every layer, with no routing, gather or combine."""
+    reps = 5
+    cache_flush()  # allocates the 1 GiB buffer
+    buf = _FLUSH[0]
+    _, read_ms, _ = time_steps(lambda: buf.sum(), reps, 2)
+    dst = torch.empty_like(buf)
+    _, copy_ms, _ = time_steps(lambda: torch.mul(buf, 1.0, out=dst), reps, 2)
+    del dst
+    n = 8192
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    _, sq_ms, _ = time_steps(lambda: torch.matmul(a, b), reps, 2)
+    del a, b
+    rows, H, F = T * cfg.top_k, cfg.hidden, cfg.ffn
+    xg = torch.randn(rows, H, device="cuda").to(torch.bfloat16)
+    wgu = torch.randn(H, 2 * F, device="cuda").to(torch.bfloat16)
+    hd = torch.randn(rows, F, device="cuda").to(torch.bfloat16)
+    wd = torch.randn(F, H, device="cuda").to(torch.bfloat16)
+    _, gu_ms, _ = time_steps(lambda: torch.matmul(xg, wgu), reps, 2)
+    _, dn_ms, _ = time_steps(lambda: torch.matmul(hd, wd), reps, 2)
+    del xg, wgu, hd, wd
+    torch.cuda.empty_cache()
+    flops_layer = 2.0 * rows * H * 2 * F + 2.0 * rows * F * H
+    dense_ms = cfg.layers * (gu_ms + dn_ms)
+    return {"read_GBps": buf.numel() * 4 / (read_ms / 1e3) / 1e9,
+            "copy_GBps": 2 * buf.numel() * 4 / (copy_ms / 1e3) / 1e9,
+            "bf16_gemm_8192_TFLOPs": 2.0 * n ** 3 / (sq_ms / 1e3) / 1e12,
+            "dense_equivalent_ms": dense_ms,
+            "dense_equivalent_TFLOPs": cfg.layers * flops_layer / (dense_ms / 1e3) / 1e12,
+            "how": "library kernels on the same GPU, warm, per-call events (mean of 5)"}
+
+
 def attention_lines(steps):
     """Decode-attention lines: the serving batch (mixed lengths, both schedulers) and
     batches of one fixed length, all through the one compiled kernel."""
@@ -435,6 +473,8 @@ def main():
         # the same calls, each after an untimed 1 GiB cache flush (per-call events)
         "cold_cache": head["cold"],
         "cpu_baseline": head.get("cpu"),
+        # what vendor library kernels reach on this GPU (context for the nominal peaks)
+        "achievable": achievable_peaks(cfg, T) if args.secondary else None,
         "secondary": secondary,
     }
     print(json.dumps(line), flush=True)
