@@ -350,15 +350,18 @@ def achievable_peaks(cfg, T):
 
 
 def attention_lines(steps):
-    """Decode-attention lines: the serving batch (mixed lengths, both schedulers) and
-    batches of one fixed length, all through the one compiled kernel."""
+    """Decode-attention lines: the serving batch (mixed lengths) and batches of one fixed
+    length, each under both schedulers (static: the library's default; dynamic: the
+    last-arriver merge), all through the one compiled kernel."""
     cfg = synth.ATTN
     mixed = synth.draw_context_lens(cfg["batch"], cfg["min_len"], cfg["max_len"], cfg["seed"])
     lines = {}
     for m in ("static", "dynamic"):
         lines[f"attention_mixed_{m}"] = bench_attention(steps, 2, m, mixed, f"mixed {m}")
     for L in (1024, 8192, 32768):
-        lines[f"attention_L{L}"] = bench_attention(steps, 2, "dynamic", [L] * cfg["batch"], f"L={L}")
+        for m in ("static", "dynamic"):
+            key = f"attention_L{L}" + ("" if m == "static" else "_dynamic")
+            lines[key] = bench_attention(steps, 2, m, [L] * cfg["batch"], f"L={L} {m}")
     keep = ("requests", "tokens", "launch_ms", "gbs_alg", "hbm_frac", "cold")
     return {k: {f: v[f] for f in keep} for k, v in lines.items()}
 
